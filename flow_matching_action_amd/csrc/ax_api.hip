@@ -1,0 +1,174 @@
+// C ABI of libax: argument validation on the host, then launches on the caller's stream.
+// Declarations and the contract of every entry point are in include/ax.h.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/ax.h"
+#include "ax_launch.h"
+
+namespace {
+
+constexpr int kMaxDev = 64;
+int g_arch[kMaxDev];  // 0 = unknown, 1 = gfx950, -1 = other
+
+// Is the current device a gfx950? Cached per device (the query is not a stream operation).
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return AX_E_UNSUPPORTED;
+  if (g_arch[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return AX_E_UNSUPPORTED;
+    g_arch[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+  }
+  return g_arch[dev] == 1 ? AX_OK : AX_E_UNSUPPORTED;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p == nullptr) return AX_E_NULL;
+  for (const void* p : ps)
+    if (!aligned16(p)) return AX_E_ALIGN;
+  return AX_OK;
+}
+
+int check_shape(int S, int Smax) {
+  if (Smax < AX_N_TOK || Smax > AX_SMAX_LIMIT) return AX_E_SHAPE;
+  if (S < 0 || S > Smax - AX_N_TOK) return AX_E_SHAPE;
+  return AX_OK;
+}
+
+int check_eps(float eps) { return (isfinite(eps) && eps >= 0.f) ? AX_OK : AX_E_ARG; }
+
+int status(hipError_t e) { return e == hipSuccess ? AX_OK : static_cast<int>(e); }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int ax_abi_version(void) { return AX_ABI_VERSION; }
+
+const char* ax_strerror(int code) {
+  switch (code) {
+    case AX_OK: return "ok";
+    case AX_E_NULL: return "a required pointer is NULL";
+    case AX_E_SHAPE: return "invalid shape: need 64 <= Smax <= 2^20 and 0 <= S <= Smax - 64";
+    case AX_E_ALIGN: return "a device pointer is not 16-byte aligned";
+    case AX_E_WORKSPACE: return "workspace too small or misaligned";
+    case AX_E_UNSUPPORTED: return "no gfx950 device is current";
+    case AX_E_ARG: return "invalid scalar argument";
+    default: return code > 0 ? hipGetErrorString(static_cast<hipError_t>(code)) : "unknown error";
+  }
+}
+
+int ax_rope_tables(int pos0, int n_tok, int head_dim, double theta, float* cos_h, float* sin_h) {
+  if (!cos_h || !sin_h) return AX_E_NULL;
+  if (n_tok <= 0 || head_dim <= 0 || (head_dim & 1)) return AX_E_SHAPE;
+  if (!(theta > 0.0) || !isfinite(theta) || pos0 < 0) return AX_E_ARG;
+  const int half = head_dim / 2;
+  for (int j = 0; j < half; ++j) {
+    const double inv = pow(theta, -2.0 * j / head_dim);
+    for (int i = 0; i < n_tok; ++i) {
+      const double ang = (double)(pos0 + i) * inv;
+      cos_h[i * half + j] = (float)cos(ang);
+      sin_h[i * half + j] = (float)sin(ang);
+    }
+  }
+  return AX_OK;
+}
+
+int ax_qk_norm_rope(const uint16_t* q_in, const uint16_t* k_in, const uint16_t* gamma_q,
+                    const uint16_t* gamma_k, const float* rope_cos, const float* rope_sin, float eps,
+                    uint16_t* q_out, uint16_t* k_out, void* stream) {
+  int r = check_ptrs({q_in, k_in, gamma_q, gamma_k, rope_cos, rope_sin, q_out, k_out});
+  if (r == AX_OK) r = check_eps(eps);
+  if (r == AX_OK) r = check_device();
+  if (r != AX_OK) return r;
+  ax::QkLaunch p{q_in, k_in, nullptr, gamma_q, gamma_k, rope_cos, rope_sin, eps, q_out, k_out, nullptr, 0};
+  return status(ax::launch_qk_norm_rope(p, as_stream(stream)));
+}
+
+int ax_cache_tail_write(const uint16_t* k_roped, const uint16_t* v, uint16_t* Kc, uint16_t* Vc, int Smax,
+                        void* stream) {
+  int r = check_ptrs({k_roped, v, Kc, Vc});
+  if (r == AX_OK) r = check_shape(0, Smax);
+  if (r == AX_OK) r = check_device();
+  if (r != AX_OK) return r;
+  return status(ax::launch_tail_copy(k_roped, v, Kc, Vc, Smax, as_stream(stream)));
+}
+
+int ax_qk_norm_rope_tail(const uint16_t* q_in, const uint16_t* k_in, const uint16_t* v_in,
+                         const uint16_t* gamma_q, const uint16_t* gamma_k, const float* rope_cos,
+                         const float* rope_sin, float eps, uint16_t* q_out, uint16_t* Kc, uint16_t* Vc,
+                         int Smax, void* stream) {
+  int r = check_ptrs({q_in, k_in, v_in, gamma_q, gamma_k, rope_cos, rope_sin, q_out, Kc, Vc});
+  if (r == AX_OK) r = check_shape(0, Smax);
+  if (r == AX_OK) r = check_eps(eps);
+  if (r == AX_OK) r = check_device();
+  if (r != AX_OK) return r;
+  ax::QkLaunch p{q_in, k_in, v_in, gamma_q, gamma_k, rope_cos, rope_sin, eps, q_out, Kc, Vc, Smax};
+  return status(ax::launch_qk_norm_rope(p, as_stream(stream)));
+}
+
+static const size_t kQScratch = (size_t)AX_N_Q_HEADS * AX_N_TOK * AX_HEAD_DIM * 2;  // roped q, bf16
+
+size_t ax_expert_attn_workspace_bytes(int S, int Smax) {
+  if (check_shape(S, Smax) != AX_OK) return 0;
+  return kQScratch + ax::attn_partials_bytes(ax::attn_plan(S, Smax));
+}
+
+static int check_ws(const void* ws, size_t ws_bytes, int S, int Smax) {
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return AX_E_WORKSPACE;
+  return ws_bytes >= ax_expert_attn_workspace_bytes(S, Smax) ? AX_OK : AX_E_WORKSPACE;
+}
+
+int ax_expert_attn(const uint16_t* q_roped, const uint16_t* k_own, const uint16_t* v_own, uint16_t* Kc,
+                   uint16_t* Vc, int S, int Smax, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  int r = check_ptrs({q_roped, Kc, Vc, out, ws});
+  if (r == AX_OK && ((k_own == nullptr) != (v_own == nullptr))) r = AX_E_NULL;
+  if (r == AX_OK && k_own && (!aligned16(k_own) || !aligned16(v_own))) r = AX_E_ALIGN;
+  if (r == AX_OK) r = check_shape(S, Smax);
+  if (r == AX_OK) r = check_ws(ws, ws_bytes, S, Smax);
+  if (r == AX_OK) r = check_device();
+  if (r != AX_OK) return r;
+  hipStream_t st = as_stream(stream);
+  if (k_own) {
+    hipError_t e = ax::launch_tail_copy(k_own, v_own, Kc, Vc, Smax, st);
+    if (e != hipSuccess) return status(e);
+  }
+  const ax::AttnPlan plan = ax::attn_plan(S, Smax);
+  ax::AttnLaunch p{q_roped, Kc, Vc, out, static_cast<char*>(ws) + kQScratch, S, Smax};
+  return status(ax::launch_attn(plan, p, st));
+}
+
+int ax_expert_layer_attn(const uint16_t* q_in, const uint16_t* k_in, const uint16_t* v_in,
+                         const uint16_t* gamma_q, const uint16_t* gamma_k, const float* rope_cos,
+                         const float* rope_sin, float eps, uint16_t* Kc, uint16_t* Vc, int S, int Smax,
+                         uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  int r = check_ptrs({q_in, k_in, v_in, gamma_q, gamma_k, rope_cos, rope_sin, Kc, Vc, out, ws});
+  if (r == AX_OK) r = check_shape(S, Smax);
+  if (r == AX_OK) r = check_eps(eps);
+  if (r == AX_OK) r = check_ws(ws, ws_bytes, S, Smax);
+  if (r == AX_OK) r = check_device();
+  if (r != AX_OK) return r;
+  hipStream_t st = as_stream(stream);
+  uint16_t* q_roped = static_cast<uint16_t*>(ws);
+  ax::QkLaunch qk{q_in, k_in, v_in, gamma_q, gamma_k, rope_cos, rope_sin, eps, q_roped, Kc, Vc, Smax};
+  hipError_t e = ax::launch_qk_norm_rope(qk, st);
+  if (e != hipSuccess) return status(e);
+  const ax::AttnPlan plan = ax::attn_plan(S, Smax);
+  ax::AttnLaunch p{q_roped, Kc, Vc, out, static_cast<char*>(ws) + kQScratch, S, Smax};
+  return status(ax::launch_attn(plan, p, st));
+}
+
+int ax_copy_words(const void* src, void* dst, size_t n_words16, void* stream) {
+  int r = check_ptrs({src, dst});
+  if (r == AX_OK) r = check_device();
+  if (r != AX_OK) return r;
+  return status(ax::launch_copy_words(src, dst, n_words16, as_stream(stream)));
+}
+
+}  // extern "C"

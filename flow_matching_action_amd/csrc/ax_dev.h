@@ -1,0 +1,86 @@
+// Device-side helpers shared by the gfx950 kernels of libax.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <utility>
+
+namespace ax {
+
+constexpr int kHq = 16;       // query heads
+constexpr int kHkv = 8;       // kv heads
+constexpr int kT = 64;        // expert tokens
+constexpr int kD = 128;       // head dim
+constexpr int kRep = kHq / kHkv;
+constexpr int kQRows = kRep * kT;  // folded query rows per kv head
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Compile-time loop: f(std::integral_constant<int, I>{}) for I = 0 .. N-1, so that
+// register arrays indexed by I never need to live in private memory.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float32 -> bf16 bits, nearest-even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Unpack 8 bf16 held in a uint4 into floats.
+__device__ __forceinline__ void unpack8(const uint4& v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ uint4 pack8(const float* f) {
+  return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                    pack_bf16x2(f[6], f[7]));
+}
+
+// RMSNorm + rotate_half RoPE of one 128-wide row held by a group of 16 consecutive
+// lanes, 8 elements per lane (lane j16 holds columns 8*j16 .. 8*j16+7). Row partner
+// column c+-64 sits in lane j16 ^ 8. All lanes of the wave must call this together.
+// x: the 8 inputs; g: the 8 gammas; c, s: cos/sin for columns (8*j16+e) mod 64.
+__device__ __forceinline__ void norm_rope_row16(float* x, const float* g, const float* c,
+                                                const float* s, float eps, int j16) {
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+  ss += __shfl_xor(ss, 8, 16);
+  ss += __shfl_xor(ss, 4, 16);
+  ss += __shfl_xor(ss, 2, 16);
+  ss += __shfl_xor(ss, 1, 16);
+  const float inv = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = x[e] * inv * g[e];
+  const float sgn = (j16 < 8) ? -1.0f : 1.0f;  // lower half: x c - x' s; upper half: x c + x' s
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float p = __shfl_xor(y[e], 8, 16);
+    x[e] = y[e] * c[e] + sgn * p * s[e];
+  }
+}
+
+}  // namespace ax

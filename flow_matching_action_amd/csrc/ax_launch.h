@@ -1,0 +1,52 @@
+// Internal host-side launch interfaces between the C ABI (ax_api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ax {
+
+struct QkLaunch {
+  const uint16_t* q_in;
+  const uint16_t* k_in;
+  const uint16_t* v_in;
+  const uint16_t* gq;
+  const uint16_t* gk;
+  const float* cos_t;
+  const float* sin_t;
+  float eps;
+  uint16_t* q_out;
+  uint16_t* k_dst;   // k_out ([8][64][128]) or Kc
+  uint16_t* v_dst;   // null, or Vc
+  int tail_smax;     // 0: k_dst is a plain [8][64][128] tensor; >0: k_dst/v_dst are caches of this length
+};
+
+hipError_t launch_qk_norm_rope(const QkLaunch& p, hipStream_t st);
+hipError_t launch_tail_copy(const uint16_t* k, const uint16_t* v, uint16_t* Kc, uint16_t* Vc, int Smax,
+                            hipStream_t st);
+
+// Split-KV attention plan for one (S, Smax).
+struct AttnPlan {
+  int n_keys;      // S + 64 visible keys per kv head
+  int n_split;     // key splits per kv head
+  int keys_per_split;
+  int blocks;      // 32-key blocks per split (kernel variant)
+};
+
+AttnPlan attn_plan(int S, int Smax);
+size_t attn_partials_bytes(const AttnPlan& p);
+
+struct AttnLaunch {
+  const uint16_t* q;   // [8][128][128] roped (folded view of [16][64][128])
+  const uint16_t* Kc;
+  const uint16_t* Vc;
+  uint16_t* out;       // [8][128][128]
+  void* ws;            // partials
+  int S, Smax;
+};
+
+hipError_t launch_attn(const AttnPlan& plan, const AttnLaunch& p, hipStream_t st);
+
+hipError_t launch_copy_words(const void* src, void* dst, size_t n, hipStream_t st);
+
+}  // namespace ax

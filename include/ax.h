@@ -1,0 +1,168 @@
+/*
+ * ax.h - C ABI of the MI355X (gfx950) expert-attention library (libax.so).
+ *
+ * One layer of the Alpamayo2-Super flow-matching action expert's attention
+ * step, as described on page code/alpamayo_tt/expert.py (TTExpert.layer and
+ * TTExpert.attention_core) and page code/alpamayo_tt/EXPERT_NOTES.md
+ * (sections "Layouts" and "Attention over the VLM cache: masking approach"):
+ *
+ *   64 expert tokens, 16 query heads, 8 GQA kv heads, head_dim 128.
+ *   q and the expert's own k get per-head RMSNorm (eps 1e-6) and HF
+ *   rotate_half RoPE (theta 5e6, positions S + rope_delta + i); the own roped
+ *   K and the raw own V overwrite rows [Smax-64, Smax) of the layer's KV cache;
+ *   the 128 folded query rows of each kv head (2 q heads x 64 tokens) attend
+ *   non-causally to cache rows [0, S) and [Smax-64, Smax) - the rows an
+ *   additive 0/-1e9 mask leaves visible - with scale 1/sqrt(128).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Shapes are fixed by the model: Hq = 16, Hkv = 8, T = 64, D = 128.
+ * - bf16 tensors are passed as uint16_t bit patterns. All tensors are dense,
+ *   row-major, in device memory owned by the caller, 16-byte aligned:
+ *     q        [16][64][128]   (q head h, token i)
+ *     k, v     [8][64][128]    (kv head g, token i)
+ *     gamma    [128]
+ *     Kc, Vc   [8][Smax][128]  (kv head g, cache row j), 256 bytes per row
+ *     out      [16][64][128]   per-head attention output before the head concat
+ *   Folded view: row r of kv head g is q head 2g + r/64, token r % 64, so q,
+ *   out and any [8][128][128] view of them are the same bytes.
+ * - RoPE tables are float32 [64][64] in device memory: table[i][j] is
+ *   cos (or sin) of (S + rope_delta + i) * theta^(-2j/128); column j serves
+ *   both j and j + 64 (rotate_half layout). ax_rope_tables() fills them.
+ * - 0 <= S <= Smax - 64 and 64 <= Smax <= AX_SMAX_LIMIT. Rows [S, Smax-64)
+ *   are never read: any contents are allowed there.
+ * - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
+ *   work: nothing is synchronised, nothing is allocated, no host memory is
+ *   touched except where stated. Launch is asynchronous; faults surface at
+ *   the next synchronisation of the stream.
+ * - Return value: AX_OK (0) = enqueued; a negative AX_E_* code = the
+ *   arguments were rejected on the host before anything was enqueued or
+ *   written; a positive value = the hipError_t of a failed launch.
+ * - Calls on the same cache/workspace buffers must be ordered on one stream
+ *   (or synchronised); the library keeps no state between calls besides a
+ *   per-device record of whether the device is a gfx950.
+ */
+#ifndef AX_H
+#define AX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AX_ABI_VERSION 1
+
+#define AX_N_Q_HEADS 16
+#define AX_N_KV_HEADS 8
+#define AX_N_TOK 64
+#define AX_HEAD_DIM 128
+#define AX_SMAX_LIMIT (1 << 20)
+
+enum {
+  AX_OK = 0,
+  AX_E_NULL = -1,        /* a required pointer is NULL */
+  AX_E_SHAPE = -2,       /* S < 0, S > Smax - 64, Smax < 64 or Smax > AX_SMAX_LIMIT, bad n_tok/head_dim */
+  AX_E_ALIGN = -3,       /* a device pointer is not 16-byte aligned */
+  AX_E_WORKSPACE = -4,   /* workspace smaller than ax_expert_attn_workspace_bytes() */
+  AX_E_UNSUPPORTED = -5, /* current device is not a gfx950, or no device */
+  AX_E_ARG = -6          /* another invalid scalar (eps < 0 or not finite, theta <= 0, ...) */
+};
+
+/* ABI version of the loaded library (AX_ABI_VERSION). */
+int ax_abi_version(void);
+
+/* Static text for a return code of any entry point (never NULL). */
+const char* ax_strerror(int code);
+
+/*
+ * Host function: RoPE tables for the n_tok positions pos0 + i
+ * (pos0 = S + rope_delta; page code/alpamayo_tt/expert.py, TTExpert.set_context,
+ * and EXPERT_NOTES.md, table "Layouts", row "cos / sin").
+ * cos_h, sin_h: HOST float arrays [n_tok][head_dim/2], written as the float32
+ * rounding of values computed in double precision. head_dim must be even and
+ * positive, n_tok positive, theta > 0, pos0 >= 0. No device work.
+ */
+int ax_rope_tables(int pos0, int n_tok, int head_dim, double theta, float* cos_h, float* sin_h);
+
+/*
+ * q/k RMSNorm + RoPE (the q_norm, k_norm, rope q and rope k ops of
+ * TTExpert.layer, page code/alpamayo_tt/expert.py).
+ * q_out[h][i][:] = bf16(rope(gamma_q * q_in / sqrt(mean(q_in^2) + eps)))
+ * k_out likewise with gamma_k; arithmetic in float32, one rounding at the
+ * store (nearest-even). q_out may equal q_in and k_out may equal k_in
+ * (exact aliasing only). Shapes: q [16][64][128], k [8][64][128].
+ */
+int ax_qk_norm_rope(const uint16_t* q_in, const uint16_t* k_in, const uint16_t* gamma_q,
+                    const uint16_t* gamma_k, const float* rope_cos, const float* rope_sin, float eps,
+                    uint16_t* q_out, uint16_t* k_out, void* stream);
+
+/*
+ * Tail write (the two fill_cache calls of TTExpert.layer at row Smax - 64,
+ * page code/alpamayo_tt/expert.py; EXPERT_NOTES.md, "masking approach").
+ * Kc[g][Smax-64+i][:] = k_roped[g][i][:], Vc[g][Smax-64+i][:] = v[g][i][:],
+ * bit-exact copies; every other cache row is left untouched.
+ */
+int ax_cache_tail_write(const uint16_t* k_roped, const uint16_t* v, uint16_t* Kc, uint16_t* Vc,
+                        int Smax, void* stream);
+
+/*
+ * Fused RMSNorm + RoPE + tail write in one launch: q_out as ax_qk_norm_rope,
+ * the roped k goes straight into Kc rows [Smax-64, Smax) and v into Vc rows
+ * [Smax-64, Smax) (bit-identical to ax_qk_norm_rope followed by
+ * ax_cache_tail_write).
+ */
+int ax_qk_norm_rope_tail(const uint16_t* q_in, const uint16_t* k_in, const uint16_t* v_in,
+                         const uint16_t* gamma_q, const uint16_t* gamma_k, const float* rope_cos,
+                         const float* rope_sin, float eps, uint16_t* q_out, uint16_t* Kc,
+                         uint16_t* Vc, int Smax, void* stream);
+
+/*
+ * Bytes of caller-owned device workspace that ax_expert_attn and
+ * ax_expert_layer_attn need for (S, Smax): split partials (float32) plus the
+ * roped q of the composite call. 0 if (S, Smax) is invalid.
+ */
+size_t ax_expert_attn_workspace_bytes(int S, int Smax);
+
+/*
+ * Attention of the 128 folded rows of each kv head over cache rows [0, S)
+ * and [Smax-64, Smax) (TTExpert.attention_core in decode mode, page
+ * code/alpamayo_tt/expert.py; the mask of TTExpert.build_mask is implied by S
+ * and Smax: the hidden rows are skipped, not read).
+ * q_roped: [16][64][128] bf16, already normed and roped.
+ * If k_own and v_own are both non-NULL, the tail write (k_own is the ROPED
+ * own k) is done first; if both are NULL the tail is taken as already
+ * written; exactly one NULL is AX_E_NULL.
+ * out: [16][64][128] bf16 (nearest-even rounding of the float32 result).
+ * Arithmetic: bf16 products on the matrix cores, float32 accumulation,
+ * float32 softmax and split combine. ws: workspace of at least
+ * ax_expert_attn_workspace_bytes(S, Smax) bytes, 256-byte aligned; its
+ * contents on entry do not matter and on return are unspecified.
+ */
+int ax_expert_attn(const uint16_t* q_roped, const uint16_t* k_own, const uint16_t* v_own,
+                   uint16_t* Kc, uint16_t* Vc, int S, int Smax, uint16_t* out, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/*
+ * The whole attention step of one layer: ax_qk_norm_rope_tail followed by
+ * ax_expert_attn on its roped q (k_own = v_own = NULL). Updates the cache
+ * tail of Kc/Vc and writes out [16][64][128]. Inputs as above.
+ */
+int ax_expert_layer_attn(const uint16_t* q_in, const uint16_t* k_in, const uint16_t* v_in,
+                         const uint16_t* gamma_q, const uint16_t* gamma_k, const float* rope_cos,
+                         const float* rope_sin, float eps, uint16_t* Kc, uint16_t* Vc, int S,
+                         int Smax, uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Measurement helper: dst[i] = src[i] for n 16-byte words, one plain
+ * streaming copy kernel. Used to calibrate hardware byte counters against a
+ * transfer of known size. Pointers 16-byte aligned.
+ */
+int ax_copy_words(const void* src, void* dst, size_t n_words16, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AX_H */

@@ -1,0 +1,113 @@
+"""C-ABI checks that need no GPU: exports, error codes of the host-side validation, host RoPE tables.
+
+Validation happens on the host before any device call, so the rejected calls
+below never touch a device (the pointers are fake, 16-byte aligned integers).
+"""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from flow_matching_action_amd import ax
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ax.h")
+FAKE = 0x10000   # aligned, never dereferenced
+MIS = 0x10008    # 8-byte aligned only
+
+
+def declared_symbols():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ax_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_and_library_agree():
+    names = declared_symbols()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(ax.lib, n), f"libax.so does not export {n}"
+    assert sorted(ax.EXPORTS) == names
+
+
+def test_abi_version_and_strerror():
+    assert ax.abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert ax.strerror(code)
+    assert "unknown" in ax.strerror(-99)
+
+
+def test_rope_tables_match_oracle():
+    for pos0 in (0, 1, 4700, 8128, 65472):
+        cos, sin = ax.rope_tables(pos0)
+        ref_c, ref_s = oracle.rope_tables(pos0)
+        assert np.array_equal(ref_c[:, :64], ref_c[:, 64:])
+        ulp = np.spacing(np.abs(ref_c[:, :64]).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(cos - ref_c[:, :64]) <= ulp)
+        ulp = np.spacing(np.abs(ref_s[:, :64]).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(sin - ref_s[:, :64]) <= ulp)
+    c, s = ax.rope_tables(0)
+    assert np.all(c[0] == 1.0) and np.all(s[0] == 0.0)   # row 0 is position 0
+
+
+def test_rope_tables_rejects_bad_arguments():
+    buf = np.empty(64 * 64, np.float32)
+    p = buf.ctypes.data_as(ctypes.c_void_p)
+    assert ax.lib.ax_rope_tables(0, 64, 128, 5e6, None, p) == ax.AX_E_NULL
+    assert ax.lib.ax_rope_tables(0, 64, 127, 5e6, p, p) == ax.AX_E_SHAPE
+    assert ax.lib.ax_rope_tables(0, 0, 128, 5e6, p, p) == ax.AX_E_SHAPE
+    assert ax.lib.ax_rope_tables(0, 64, 128, 0.0, p, p) == ax.AX_E_ARG
+    assert ax.lib.ax_rope_tables(-1, 64, 128, 5e6, p, p) == ax.AX_E_ARG
+
+
+def test_workspace_bytes():
+    assert ax.expert_attn_workspace_bytes(128, 256) > 0
+    assert ax.expert_attn_workspace_bytes(4700, 8192) >= ax.expert_attn_workspace_bytes(128, 256)
+    assert ax.expert_attn_workspace_bytes(0, 64) > 0
+    assert ax.expert_attn_workspace_bytes(193, 256) == 0      # S > Smax - 64
+    assert ax.expert_attn_workspace_bytes(-1, 256) == 0
+    assert ax.expert_attn_workspace_bytes(0, 63) == 0
+    assert ax.expert_attn_workspace_bytes(0, (1 << 20) + 64) == 0
+
+
+def _layer(q=FAKE, k=FAKE, v=FAKE, gq=FAKE, gk=FAKE, c=FAKE, s=FAKE, eps=1e-6, Kc=FAKE, Vc=FAKE, S=128,
+           Smax=256, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    return ax.lib.ax_expert_layer_attn(q, k, v, gq, gk, c, s, eps, Kc, Vc, S, Smax, out, ws, ws_bytes, None)
+
+
+def test_layer_validation_codes():
+    assert _layer(q=None) == ax.AX_E_NULL
+    assert _layer(out=None) == ax.AX_E_NULL
+    assert _layer(Kc=MIS) == ax.AX_E_ALIGN
+    assert _layer(S=193) == ax.AX_E_SHAPE
+    assert _layer(S=-1) == ax.AX_E_SHAPE
+    assert _layer(Smax=32, S=0) == ax.AX_E_SHAPE
+    assert _layer(eps=float("nan")) == ax.AX_E_ARG
+    assert _layer(eps=-1.0) == ax.AX_E_ARG
+    assert _layer(ws_bytes=16) == ax.AX_E_WORKSPACE
+    assert _layer(ws=FAKE + 16) == ax.AX_E_WORKSPACE      # not 256-byte aligned
+
+
+def test_attn_validation_codes():
+    f = ax.lib.ax_expert_attn
+    assert f(FAKE, FAKE, None, FAKE, FAKE, 128, 256, FAKE, FAKE, 1 << 30, None) == ax.AX_E_NULL
+    assert f(FAKE, MIS, MIS, FAKE, FAKE, 128, 256, FAKE, FAKE, 1 << 30, None) == ax.AX_E_ALIGN
+    assert f(FAKE, None, None, FAKE, FAKE, 300, 256, FAKE, FAKE, 1 << 30, None) == ax.AX_E_SHAPE
+    assert f(FAKE, None, None, FAKE, FAKE, 128, 256, FAKE, FAKE, 100, None) == ax.AX_E_WORKSPACE
+    g = ax.lib.ax_qk_norm_rope
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1e-6, FAKE, FAKE, None) == ax.AX_E_NULL
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, float("inf"), FAKE, FAKE, None) == ax.AX_E_ARG
+    t = ax.lib.ax_cache_tail_write
+    assert t(FAKE, FAKE, FAKE, None, 256, None) == ax.AX_E_NULL
+    assert t(FAKE, FAKE, FAKE, FAKE, 63, None) == ax.AX_E_SHAPE
+    assert ax.lib.ax_copy_words(None, FAKE, 1, None) == ax.AX_E_NULL
+
+
+def test_no_device_is_reported_not_launched():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: the valid call would launch")
+    assert _layer() == ax.AX_E_UNSUPPORTED
