@@ -1,0 +1,229 @@
+"""Throughput of the expert-attention step on one MI355X: us/layer and achieved HBM GB/s.
+
+One step = one layer's whole attention step (q/k RMSNorm, RoPE, own K/V tail write,
+split-KV attention over the visible cache rows, split combine) at Smax = 8192,
+S = 4700, bf16. Steps rotate over 64 distinct layer caches (2.1 GB, far beyond the
+256 MB Infinity Cache) with fresh q / own k / own v per (Euler step, layer), the
+64-layer x 10-step sequence of the flow-matching sampler, in stream order. The K
+timed steps are one hipGraph replay, bracketed by device synchronisation and
+timed with HIP events on the stream the graph runs on.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+SMAX, S, ROPE_DELTA, EPS = 8192, 4700, 0, 1e-6
+N_LAYERS, N_EULER = 64, 10
+HBM_PEAK_GBS = 8000.0
+METRIC = "expert-attention us/layer + achieved HBM GB/s, Smax=8192 S=4700 bf16"
+
+
+def algorithmic_bytes(S: int, Smax: int) -> int:
+    """Bytes one step must move at minimum: visible cache rows (K and V), q, own k and v, the tail write
+    of K and V, and the output. Hidden rows and split partials are not counted."""
+    row = 128 * 2
+    visible = 2 * 8 * (S + 64) * row
+    q_in = 16 * 64 * row
+    kv_in = 2 * 8 * 64 * row
+    tail = 2 * 8 * 64 * row
+    out = 16 * 64 * row
+    return visible + q_in + kv_in + tail + out
+
+
+def algorithmic_flops(S: int) -> int:
+    return 2 * 2 * 8 * 128 * (S + 64) * 128   # QK^T and PV, 128 folded rows per kv head
+
+
+class RotatingWorkload:
+    """Device buffers of the 64-layer x 10-step sequence (seeded; see flow_matching_action_amd.synth)."""
+
+    def __init__(self, ax, torch, n_layers: int = N_LAYERS, n_sets: int = N_LAYERS * N_EULER, Smax: int = SMAX,
+                 S: int = S):
+        from flow_matching_action_amd import synth
+        dev = "cuda:0"
+        self.ax, self.torch = ax, torch
+        self.Smax, self.S, self.n_layers, self.n_sets = Smax, S, n_layers, n_sets
+        self.K, self.V, self.gq, self.gk = [], [], [], []
+        for l in range(n_layers):
+            k, v = synth.device_cache(Smax, S, l, dev)
+            self.K.append(k.contiguous())
+            self.V.append(v.contiguous())
+            gq, gk = synth.device_gammas(l, dev)
+            self.gq.append(gq.contiguous())
+            self.gk.append(gk.contiguous())
+        self.q, self.k, self.v = [], [], []
+        for i in range(n_sets):
+            s, l = divmod(i, n_layers)
+            q, k, v = synth.device_qkv(s, l, dev)
+            self.q.append(q.contiguous())
+            self.k.append(k.contiguous())
+            self.v.append(v.contiguous())
+        cos, sin = ax.rope_tables(S + ROPE_DELTA)
+        self.cos = torch.from_numpy(cos).to(dev)
+        self.sin = torch.from_numpy(sin).to(dev)
+        self.out = [torch.empty((16, 64, 128), dtype=torch.bfloat16, device=dev) for _ in range(n_layers)]
+        self.ws = torch.empty(ax.expert_attn_workspace_bytes(S, Smax), dtype=torch.uint8, device=dev)
+        for t in self.K + self.V:
+            assert t.shape == (8, Smax, 128) and t.is_contiguous()
+        torch.cuda.synchronize()
+
+    def step(self, i: int, stream=None):
+        """Enqueue step i: layer i % n_layers, q/k/v set i % n_sets."""
+        l = i % self.n_layers
+        j = i % self.n_sets
+        self.ax.expert_layer_attn(self.q[j], self.k[j], self.v[j], self.gq[l], self.gk[l], self.cos, self.sin, EPS,
+                                  self.K[l], self.V[l], self.S, self.Smax, self.out[l], self.ws, stream=stream)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "flow_matching_action_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(per_launch_alg: float):
+    """HBM bytes per step from the committed counter summary, if it was taken on the current kernels."""
+    path = os.path.join(ROOT, "profiles", "traffic_expert_layer_attn_smax8192_s4700.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_step"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(n_layers: int = 6) -> dict:
+    """The fp64 oracle on the host cores, on a bounded sample of the same workload shape."""
+    import numpy as np
+    import oracle
+    from flow_matching_action_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    times = []
+    for i in range(n_layers):
+        inp = synth.layer_inputs(SMAX, S, seed=7000 + i)
+        t0 = time.perf_counter()
+        oracle.expert_attn_layer(inp["q"], inp["k"], inp["v"], inp["gq"], inp["gk"], inp["Kc"], inp["Vc"],
+                                 S, SMAX, ROPE_DELTA)
+        times.append(time.perf_counter() - t0)
+    us = statistics.median(times) * 1e6
+    return {"value": round(us, 1), "unit": "us/layer", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_layers} layers of the Smax=8192 S=4700 workload (seeds 7000..{7000 + n_layers - 1}), "
+                      f"median per layer; numpy float64 on the host"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=N_LAYERS * N_EULER)
+    ap.add_argument("--warmup", type=int, default=N_LAYERS * N_EULER)
+    ap.add_argument("--replays", type=int, default=5, help="timed replays of the K-step graph (median reported)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the expert-attention step is measured on a single MI355X); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+    if args.steps <= 0:
+        print("--steps must be positive", file=sys.stderr)
+        return 2
+
+    import torch
+    from flow_matching_action_amd import ax
+
+    torch.cuda.set_device(0)
+    wl = RotatingWorkload(ax, torch)
+    K, W = args.steps, args.warmup
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    # warmup: eager steps on the bench stream
+    with torch.cuda.stream(stream):
+        for i in range(W):
+            wl.step(i, stream)
+    torch.cuda.synchronize()
+
+    # capture the K timed steps as one graph
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(K):
+                wl.step(W + i, stream)
+    torch.cuda.synchronize()
+
+    times_ms = []
+    for _ in range(max(1, args.replays)):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        times_ms.append(e0.elapsed_time(e1))
+    ms_total = statistics.median(times_ms)
+    us_layer = ms_total * 1e3 / K
+    out_ok = all(bool(torch.isfinite(o.float()).all()) for o in wl.out)
+
+    b_alg = algorithmic_bytes(S, SMAX)
+    gbs = b_alg / (us_layer * 1e-6) / 1e9
+    traffic = load_traffic(b_alg)
+    result = {
+        "metric": METRIC,
+        "value": round(us_layer, 3),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_total / K, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) caches, q, own k/v; hidden rows 7.0)",
+        "config": {"workload": "expert attention layer step, Smax=8192 S=4700 bf16, 64 rotating layer caches "
+                               "(2.1 GB, cold), fresh q/k/v per (Euler step, layer), hipGraph of K steps",
+                   "Smax": SMAX, "S": S, "layers_rotated": N_LAYERS, "rope_delta": ROPE_DELTA},
+        "achieved_hbm_gbs": round(gbs, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "expert_layer_attn step (all kernels of one step)",
+                     "algorithmic_bytes_per_step": b_alg,
+                     "algorithmic_flops_per_step": algorithmic_flops(S)},
+        "replays_ms": [round(t, 4) for t in times_ms],
+        "outputs_finite": out_ok,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+    return 0 if out_ok else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

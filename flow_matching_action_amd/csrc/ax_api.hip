@@ -113,11 +113,9 @@ int ax_qk_norm_rope_tail(const uint16_t* q_in, const uint16_t* k_in, const uint1
   return status(ax::launch_qk_norm_rope(p, as_stream(stream)));
 }
 
-static const size_t kQScratch = (size_t)AX_N_Q_HEADS * AX_N_TOK * AX_HEAD_DIM * 2;  // roped q, bf16
-
 size_t ax_expert_attn_workspace_bytes(int S, int Smax) {
   if (check_shape(S, Smax) != AX_OK) return 0;
-  return kQScratch + ax::attn_partials_bytes(ax::attn_plan(S, Smax));
+  return ax::attn_partials_bytes(ax::attn_plan(S, Smax));
 }
 
 static int check_ws(const void* ws, size_t ws_bytes, int S, int Smax) {
@@ -134,14 +132,10 @@ int ax_expert_attn(const uint16_t* q_roped, const uint16_t* k_own, const uint16_
   if (r == AX_OK) r = check_ws(ws, ws_bytes, S, Smax);
   if (r == AX_OK) r = check_device();
   if (r != AX_OK) return r;
-  hipStream_t st = as_stream(stream);
-  if (k_own) {
-    hipError_t e = ax::launch_tail_copy(k_own, v_own, Kc, Vc, Smax, st);
-    if (e != hipSuccess) return status(e);
-  }
   const ax::AttnPlan plan = ax::attn_plan(S, Smax);
-  ax::AttnLaunch p{q_roped, Kc, Vc, out, static_cast<char*>(ws) + kQScratch, S, Smax};
-  return status(ax::launch_attn(plan, p, st));
+  ax::AttnLaunch p{q_roped, nullptr, nullptr, nullptr, nullptr, 0.f, k_own, v_own, Kc, Vc, out, ws, S, Smax,
+                   /*q_norm=*/0, /*tail_norm=*/0};
+  return status(ax::launch_attn(plan, p, as_stream(stream)));
 }
 
 int ax_expert_layer_attn(const uint16_t* q_in, const uint16_t* k_in, const uint16_t* v_in,
@@ -154,14 +148,10 @@ int ax_expert_layer_attn(const uint16_t* q_in, const uint16_t* k_in, const uint1
   if (r == AX_OK) r = check_ws(ws, ws_bytes, S, Smax);
   if (r == AX_OK) r = check_device();
   if (r != AX_OK) return r;
-  hipStream_t st = as_stream(stream);
-  uint16_t* q_roped = static_cast<uint16_t*>(ws);
-  ax::QkLaunch qk{q_in, k_in, v_in, gamma_q, gamma_k, rope_cos, rope_sin, eps, q_roped, Kc, Vc, Smax};
-  hipError_t e = ax::launch_qk_norm_rope(qk, st);
-  if (e != hipSuccess) return status(e);
   const ax::AttnPlan plan = ax::attn_plan(S, Smax);
-  ax::AttnLaunch p{q_roped, Kc, Vc, out, static_cast<char*>(ws) + kQScratch, S, Smax};
-  return status(ax::launch_attn(plan, p, st));
+  ax::AttnLaunch p{q_in, gamma_q, gamma_k, rope_cos, rope_sin, eps, k_in, v_in, Kc, Vc, out, ws, S, Smax,
+                   /*q_norm=*/1, /*tail_norm=*/1};
+  return status(ax::launch_attn(plan, p, as_stream(stream)));
 }
 
 int ax_copy_words(const void* src, void* dst, size_t n_words16, void* stream) {

@@ -39,8 +39,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair (low = lo), nearest-even: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Unpack 8 bf16 held in a uint4 into floats.
@@ -58,27 +62,36 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
                     pack_bf16x2(f[6], f[7]));
 }
 
+// Value of lane (i + N) mod 16 within each row of 16 lanes (DPP row_ror, a plain VALU
+// move; no LDS round trip).
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {
+  static_assert(N > 0 && N < 16, "row_ror");
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x120 + N, 0xf, 0xf, false));
+}
+
 // RMSNorm + rotate_half RoPE of one 128-wide row held by a group of 16 consecutive
-// lanes, 8 elements per lane (lane j16 holds columns 8*j16 .. 8*j16+7). Row partner
-// column c+-64 sits in lane j16 ^ 8. All lanes of the wave must call this together.
-// x: the 8 inputs; g: the 8 gammas; c, s: cos/sin for columns (8*j16+e) mod 64.
+// lanes, 8 elements per lane (lane j16 holds columns 8*j16 .. 8*j16+7). The row partner
+// of column c +- 64 sits 8 lanes away. All lanes of the wave must call this together.
+// The sum of squares is a rotate-by-8/4/2/1 butterfly, which leaves the same bits in all
+// 16 lanes. x: the 8 inputs; g: the 8 gammas; c, s: cos/sin for columns (8*j16+e) mod 64.
 __device__ __forceinline__ void norm_rope_row16(float* x, const float* g, const float* c,
                                                 const float* s, float eps, int j16) {
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
-  ss += __shfl_xor(ss, 8, 16);
-  ss += __shfl_xor(ss, 4, 16);
-  ss += __shfl_xor(ss, 2, 16);
-  ss += __shfl_xor(ss, 1, 16);
-  const float inv = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
+  ss += row_ror<8>(ss);
+  ss += row_ror<4>(ss);
+  ss += row_ror<2>(ss);
+  ss += row_ror<1>(ss);
+  const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / kD) + eps);  // v_rsq_f32
   float y[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) y[e] = x[e] * inv * g[e];
   const float sgn = (j16 < 8) ? -1.0f : 1.0f;  // lower half: x c - x' s; upper half: x c + x' s
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float p = __shfl_xor(y[e], 8, 16);
+    const float p = row_ror<8>(y[e]);
     x[e] = y[e] * c[e] + sgn * p * s[e];
   }
 }

@@ -37,12 +37,20 @@ AttnPlan attn_plan(int S, int Smax);
 size_t attn_partials_bytes(const AttnPlan& p);
 
 struct AttnLaunch {
-  const uint16_t* q;   // [8][128][128] roped (folded view of [16][64][128])
-  const uint16_t* Kc;
-  const uint16_t* Vc;
-  uint16_t* out;       // [8][128][128]
-  void* ws;            // partials
+  const uint16_t* q;       // [16][64][128] (== folded [8][128][128]): raw if q_norm, else roped
+  const uint16_t* gq;      // RMSNorm gammas (used when q_norm / tail_norm)
+  const uint16_t* gk;
+  const float* cos_t;      // RoPE tables [64][64]
+  const float* sin_t;
+  float eps;
+  const uint16_t* k_tail;  // own k [8][64][128] (raw if tail_norm, else roped), or null: tail already in Kc
+  const uint16_t* v_tail;  // own v, or null
+  uint16_t* Kc;
+  uint16_t* Vc;
+  uint16_t* out;           // [8][128][128]
+  void* ws;                // partials
   int S, Smax;
+  int q_norm, tail_norm;
 };
 
 hipError_t launch_attn(const AttnPlan& plan, const AttnLaunch& p, hipStream_t st);
