@@ -43,7 +43,9 @@ constexpr int kMaxNB = 7;                     // blocks per split, upper bound (
 constexpr int kTileBytes = 2 * kBlk * kD * 2; // K 8 KB + V 8 KB
 constexpr int kQBytes = kQRows * kD * 2;      // 32 KB
 constexpr int kThreads = 512;
+constexpr int kDmaDepth = 3;                  // blocks of a split in flight per loader wave
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescale = 8.0f;              // lazy-rescale threshold (log2 units)
 
 struct FusedArgs {
   const uint16_t* q;       // [16][64][128]: raw q (q_norm) or already roped q
@@ -181,7 +183,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
     const uint16_t* vc = a.Vc + head_off;
     const uint16_t* kt = a.kt_base + g * a.tail_stride;
     const uint16_t* vt = a.vt_base + g * a.tail_stride;
-    static_for<NB>([&](auto bc) {
+    // DMA of block b: this wave's K row groups w, w+4 and V row groups w, w+4.
+    auto issue_block = [&](auto bc) {
       constexpr int b = decltype(bc)::value;
       uint8_t* tile = pick<b>(t0, t1, t2, t3, t4, t5, t6);
       static_for<2>([&](auto hc) {
@@ -198,12 +201,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
         __builtin_amdgcn_global_load_lds(ks, (lds_void*)(tile + grp * 1024), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(vs, (lds_void*)(tile + kTileBytes / 2 + grp * 1024), 16, 0, 0);
       });
-    });
+    };
+    // The CU's memory queue throttles issue, so only kDmaDepth blocks are kept in flight:
+    // block b + kDmaDepth is issued right after block b is handed over, and the barriers
+    // never wait for the issue of loads that are not needed yet.
+    static_for<(NB < kDmaDepth ? NB : kDmaDepth)>([&](auto bc) { issue_block(bc); });
     lds_barrier();  // queries and own-token K rows written by the compute waves
     static_for<NB>([&](auto bc) {
       constexpr int b = decltype(bc)::value;
-      wait_vmcnt<4 * (NB - 1 - b)>();  // issued in block order: at most this many of the
-      lds_barrier();                   // later loads may still be pending
+      constexpr int later = (b + kDmaDepth - 1 < NB - 1 ? b + kDmaDepth - 1 : NB - 1) - b;
+      wait_vmcnt<4 * later>();  // loads are issued in block order: block b has landed
+      lds_barrier();
+      if constexpr (b + kDmaDepth < NB) issue_block(std::integral_constant<int, b + kDmaDepth>{});
     });
     return;
   }
@@ -298,34 +307,40 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const float sscale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
+  float m_run = -INFINITY, l_run = 0.f;  // running max in log2 units of the scaled score, row sum
+  const float sc = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
   const int krow = perm_key(n);
 
-  // Blocks past the split end (only in a short last split) are fully masked: they add
-  // nothing, and block 0 always holds at least one key, so m_run is finite from then on.
-  static_for<NB>([&](auto bc) {
+  // S^T = K Q^T of block b: K fragments from LDS (own-token rows from kown), then 8 MFMAs.
+  auto issue_qk = [&](auto bc) -> f32x16 {
     constexpr int b = decltype(bc)::value;
     const int kb = k_begin + b * kBlk;
-    uint8_t* tk = pick<b>(t0, t1, t2, t3, t4, t5, t6);
-    uint8_t* tv = tk + kTileBytes / 2;
-    lds_barrier();  // block b is in LDS, own-token rows fixed up
-
-    // S^T = K Q^T: K fragments first, then the MFMA chain; the V^T reads are issued behind
-    // the chain so their latency hides under it and the softmax.
+    const uint8_t* tk = pick<b>(t0, t1, t2, t3, t4, t5, t6);
     const int kvk = kb + krow;
     const uint8_t* krow_base = (own_tail && kvk >= a.S) ? kown + (kvk - a.S) * 256 : tk + krow * 256;
     bf16x8 kf[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
       kf[kk] = *reinterpret_cast<const bf16x8*>(krow_base + 16 * ((dcol(kk, h) >> 3) ^ kswz(krow)));
-    __builtin_amdgcn_sched_barrier(0);
     f32x16 s;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
-    // V^T operands: lane group G = lane >> 4, i = lane & 15 points at row
+    return s;
+  };
+
+  // Software pipeline over the blocks: while the matrix cores run block b+1's S^T, the wave
+  // does block b's softmax; then block b's PV. Blocks past the split end (only in a short
+  // last split) are fully masked: they add nothing, and block 0 always holds at least one
+  // key, so m_run is finite from block 0 on.
+  lds_barrier();  // block 0 is in LDS
+  f32x16 s_cur = issue_qk(std::integral_constant<int, 0>{});
+  static_for<NB>([&](auto bc) {
+    constexpr int b = decltype(bc)::value;
+    const int kb = k_begin + b * kBlk;
+    const uint8_t* tv = pick<b>(t0, t1, t2, t3, t4, t5, t6) + kTileBytes / 2;
+    // V^T operands of block b: lane group G = lane >> 4, i = lane & 15 points at row
     // 16c + 8(G>>1) + 4*half + i/4, columns 32t + 16(G&1) + 4(i&3) .. +3; the transpose
     // read hands lane i of the group column 32t + 16(G&1) + i of 4 consecutive rows.
     v4i16 vt[2][4][2];
@@ -343,35 +358,49 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
                 (lds_v4i16*)(tv + row * 256 + 16 * (chunk ^ vswz(row)) + 8 * (i & 1)));
           }
     }
+    f32x16 s_next;
+    if constexpr (b + 1 < NB) {
+      lds_barrier();  // block b+1 is in LDS
+      s_next = issue_qk(std::integral_constant<int, b + 1>{});
+    }
     __builtin_amdgcn_sched_barrier(0);
-    // accumulator element i of lane half h is key perm_key(8(i>>2) + 4h + (i&3)) = 8h + kofs(i)
-    const int lim = k_end - kb - 8 * h;
-    float bmax = -INFINITY;
+
+    f32x16 s = s_cur;
+    if (__builtin_expect(kb + kBlk > k_end, 0)) {  // only a split's last block can be partial
+      // accumulator element i of lane half h is key perm_key(8(i>>2) + 4h + (i&3)) = 8h + kofs(i)
+      const int lim = k_end - kb - 8 * h;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kofs = 16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3);
-      s[i] = (kofs < lim) ? s[i] * sscale : -INFINITY;
-      bmax = fmaxf(bmax, s[i]);
+      for (int i = 0; i < 16; ++i) {
+        const int kofs = 16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3);
+        s[i] = (kofs < lim) ? s[i] : -INFINITY;
+      }
     }
+    float bmax = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) bmax = fmaxf(bmax, s[i]);
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-    const float m_new = fmaxf(m_run, bmax);
-    // v_exp_f32 directly: arguments are <= 0 or -inf (masked), results in [0, 1]
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    const bool grew = __any(m_new > m_run);
-    m_run = m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s[i] = __builtin_amdgcn_exp2f(s[i] - m_new);
-      psum += s[i];
-    }
-    l_run = l_run * alpha + psum;
-    if (grew) {  // rescale only when some row's running max moved (alpha == 1 otherwise)
+    // The exponent reference m_run only moves when some row's max exceeds it by more than
+    // kRescale (log2 units): p stays below 2^kRescale, exact for the final normalisation,
+    // and the O rescale (64 multiplies) runs only on such jumps (always on block 0).
+    const float m_blk = bmax * sc;
+    if (__any(m_blk > m_run + kRescale)) {
+      const float m_new = fmaxf(m_run, m_blk);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on block 0
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
     }
+    // v_exp_f32 directly: arguments are <= kRescale or -inf (masked)
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sc, -m_run));
+      psum += s[i];
+    }
+    l_run += psum;
     bf16x8 pb[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -386,6 +415,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
         __builtin_memcpy(&vf, both, 16);
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[c], o[t], 0, 0, 0);
       }
+    if constexpr (b + 1 < NB) s_cur = s_next;
   });
 
   const int qrow = 32 * wave + n;
