@@ -39,13 +39,20 @@
 namespace ax {
 
 constexpr int kBlk = 32;                      // keys per block
-constexpr int kMaxNB = 7;                     // blocks per split, upper bound (LDS: 7 x 16 KB + 32 KB)
+constexpr int kMaxNB = 6;                     // blocks per split, upper bound (LDS: 6 x 16 KB + 48 KB)
 constexpr int kTileBytes = 2 * kBlk * kD * 2; // K 8 KB + V 8 KB
 constexpr int kQBytes = kQRows * kD * 2;      // 32 KB
-constexpr int kThreads = 512;
+constexpr int kComputeWaves = 8;
+constexpr int kLoaderWaves = 4;
+constexpr int kThreads = 64 * (kComputeWaves + kLoaderWaves);
 constexpr int kDmaDepth = 3;                  // blocks of a split in flight per loader wave
+// LDS hand-off counters: queries normed, query fragments read, block b landed, block b
+// consumed, merge data of query group q ready
+constexpr int kCntQNormed = 0, kCntQRead = 1, kCntBlock = 2;
+constexpr int kCntDone = kCntBlock + kMaxNB, kCntMerge = kCntDone + kMaxNB, kNCnt = kCntMerge + 4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescale = 8.0f;              // lazy-rescale threshold (log2 units)
+constexpr int kNonTemporal = 2;               // cache-policy operand of a load: nt
 
 struct FusedArgs {
   const uint16_t* q;       // [16][64][128]: raw q (q_norm) or already roped q
@@ -62,7 +69,7 @@ struct FusedArgs {
   int own_tail;            // own rows come from k/v tensors: norm (if NORM) and write them to the cache tail
   uint16_t* Kc;
   uint16_t* Vc;
-  float* po;               // [8][n_split][128 d][128 q]
+  float* po;               // [8][n_split][4 query groups][16 slots][64 lanes]: 4 floats of O each
   float* pm;               // [8][n_split][128]
   float* pl;
   int S, Smax, n_split, kps;
@@ -107,15 +114,55 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-__device__ __forceinline__ void load_cos_sin(const float* cos_t, const float* sin_t, int tok, int j16, float* c,
-                                             float* s) {
-  const int f0 = 8 * (j16 & 7);
-  const f32x4* cp = reinterpret_cast<const f32x4*>(cos_t + tok * 64 + f0);
-  const f32x4* sp = reinterpret_cast<const f32x4*>(sin_t + tok * 64 + f0);
-  const f32x4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+// In-workgroup hand-off counters in LDS. A producer wave bumps a counter once its data is
+// in LDS; consumers poll it. Unlike s_barrier this never makes a producer wait for its
+// consumers, so the cache stream runs ahead of the arithmetic as far as the LDS tiles
+// allow (tiles are never reused within a launch, so there is nothing to wait for).
+// The increment is written as inline asm: the compiler cannot tell an LDS atomic from the
+// direct-to-LDS loads still in flight and would drain them all (vmcnt(0)) before it.
+typedef __attribute__((address_space(3))) int lds_int;
+__device__ __forceinline__ void arrive(int* cnt, int lane) {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's own LDS writes come first
+  if (lane == 0) {
+    const unsigned off = (unsigned)(uintptr_t)(lds_int*)cnt;
+    asm volatile("ds_add_u32 %0, %1" ::"v"(off), "v"(1) : "memory");
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The wait is bounded (about 30 ms at 2.4 GHz, thousands of times any real wait) so that a
+// wave always exits even if a count were wrong; the results would then be wrong, not hung.
+constexpr int kSpinLimit = 1 << 20;
+__device__ __forceinline__ void await(int* cnt, int n) {
+  __builtin_amdgcn_sched_barrier(0);
+  for (int spin = 0; spin < kSpinLimit; ++spin) {
+    if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >= n)
+      break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// RoPE table values of token tok for the 8 frequencies 8 (j16 & 7) .. +7: lanes j16 < 8 load
+// the cosines, lanes j16 >= 8 the sines, and the partner lane (j16 ^ 8, same frequencies)
+// hands over the other half, so each table byte is requested once per row group.
+__device__ __forceinline__ void load_cos_sin_half(const float* cos_t, const float* sin_t, int tok, int j16,
+                                                  f32x4& h0, f32x4& h1) {
+  const float* src = ((j16 < 8) ? cos_t : sin_t) + tok * 64 + 8 * (j16 & 7);
+  h0 = reinterpret_cast<const f32x4*>(src)[0];
+  h1 = reinterpret_cast<const f32x4*>(src)[1];
+}
+
+__device__ __forceinline__ void split_cos_sin(const f32x4& h0, const f32x4& h1, int j16, float* c, float* s) {
+  const bool lo = j16 < 8;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    c[e] = c0[e]; c[4 + e] = c1[e]; s[e] = s0[e]; s[4 + e] = s1[e];
+  for (int e = 0; e < 8; ++e) {
+    const float mine = (e < 4) ? h0[e & 3] : h1[e & 3];
+    const float other = row_ror<8>(mine);
+    c[e] = lo ? mine : other;
+    s[e] = lo ? other : mine;
   }
 }
 
@@ -139,30 +186,38 @@ __device__ __forceinline__ u32x4 pack8v(const float* f) {
 #define AX_TILE(b) __shared__ __attribute__((aligned(16))) uint8_t t##b[kTileBytes]
 template <int B>
 __device__ __forceinline__ uint8_t* pick(uint8_t* t0, uint8_t* t1, uint8_t* t2, uint8_t* t3, uint8_t* t4,
-                                         uint8_t* t5, uint8_t* t6) {
+                                         uint8_t* t5) {
   if constexpr (B == 0) return t0;
   else if constexpr (B == 1) return t1;
   else if constexpr (B == 2) return t2;
   else if constexpr (B == 3) return t3;
   else if constexpr (B == 4) return t4;
-  else if constexpr (B == 5) return t5;
-  else return t6;
+  else return t5;
 }
 
 // NORM: q and the own k arrive raw and are normed + roped here (the layer step); otherwise
 // both arrive roped (attention only).
 //
-// Wave roles. Waves 4..7 only issue the direct-to-LDS cache loads and then mark each block
-// ready (wait for their own loads, barrier). Waves 0..3 do everything else: the query
-// norm/RoPE, the own-token rows, the attention and the partials. Keeping ordinary loads
-// and LDS-DMA loads in different waves keeps each wave's vmcnt in order, so no wave ever
-// has to drain its queue early.
+// Wave roles (12 waves, 3 per SIMD).
+// - Waves 8..11 (loaders) only issue direct-to-LDS loads - the 128 query rows of the head,
+//   then the cache blocks of the split - and count each landed block in LDS. Keeping
+//   ordinary loads and LDS-DMA loads in different waves keeps each wave's vmcnt in order,
+//   so no wave ever has to drain its queue early; the counters (not barriers) let the loads
+//   run ahead of the arithmetic.
+// - Waves 0..7 (compute) norm/rope the queries in place in LDS and handle the own-token
+//   rows, then wave w takes query rows 32 (w & 3) .. +31 over the blocks of parity w >> 2.
+//   The two waves of a query group share a SIMD, so one's matrix-core work overlaps the
+//   other's softmax. At the end the odd-parity wave hands its (m, l, O) to the even one
+//   through LDS, which merges them and writes the split's partial.
 template <int NB, bool NORM>
 __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
-  AX_TILE(0); AX_TILE(1); AX_TILE(2); AX_TILE(3); AX_TILE(4); AX_TILE(5); AX_TILE(6);
+  AX_TILE(0); AX_TILE(1); AX_TILE(2); AX_TILE(3); AX_TILE(4); AX_TILE(5);
   __shared__ __attribute__((aligned(16))) uint8_t qlds[kQBytes];
   // roped own-token K rows (row tok, chunks swizzled like the tile row they stand in for)
   __shared__ __attribute__((aligned(16))) uint8_t kown[kT * 256];
+  __shared__ float mlx[4][2][32];  // merge hand-off: (m, l) of the odd-parity waves per query row
+  // hand-off counters
+  __shared__ int cnt[kNCnt];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -175,10 +230,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
   // blocks holding own-token rows that need the tail step (norm of k and/or cache tail write)
   const bool own_tail = a.own_tail != 0;
 
-  if (wave >= 4) {
-    // ---------------- loader waves: K row groups w and w+4, V row groups w and w+4 (4 rows each)
-    const int w = wave - 4;
-    lds_barrier();  // the compute waves have issued their query / table loads: they go first
+  if (tid < kNCnt) cnt[tid] = 0;
+  if (wave < kComputeWaves) {
+    // Each compute wave fetches the 16 query rows it norms (rows 32p + 4 wave .. +3, p = 0..3)
+    // ahead of the cache stream; lane l lands at 16 l of the 1 KB, so it fetches the chunk
+    // that the row's swizzle puts there.
+    const uint16_t* qh = a.q + (long long)(2 * g) * kT * kD;  // q heads 2g, 2g+1: 128 rows, contiguous
+    static_for<4>([&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      const int row = 32 * p + 4 * wave + (lane >> 4);
+      const uint16_t* src = qh + row * kD + 8 * ((lane & 15) ^ kswz(row));
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(qlds + (32 * p + 4 * wave) * 256), 16, 0, 0);
+    });
+  }
+  lds_barrier();  // start: counters cleared (the only workgroup barrier)
+
+  if (wave >= kComputeWaves) {
+    // ---------------- loader waves: of each block the K row groups w and w+4 and the V row
+    // groups w and w+4 (4 rows each)
+    const int w = wave - kComputeWaves;
     const uint16_t* kc = a.Kc + head_off;
     const uint16_t* vc = a.Vc + head_off;
     const uint16_t* kt = a.kt_base + g * a.tail_stride;
@@ -186,7 +256,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
     // DMA of block b: this wave's K row groups w, w+4 and V row groups w, w+4.
     auto issue_block = [&](auto bc) {
       constexpr int b = decltype(bc)::value;
-      uint8_t* tile = pick<b>(t0, t1, t2, t3, t4, t5, t6);
+      uint8_t* tile = pick<b>(t0, t1, t2, t3, t4, t5);
       static_for<2>([&](auto hc) {
         constexpr int half = decltype(hc)::value;
         const int grp = w + 4 * half;
@@ -198,41 +268,39 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
         const uint16_t* ks = (in_cache ? kc : kt) + row * kD + 8 * ((lane & 15) ^ kswz(rloc));
         const uint16_t* vs = (in_cache ? vc : vt) + row * kD + 8 * ((lane & 15) ^ vswz(rloc));
         // (own-token K rows land here too but are read from kown instead)
-        __builtin_amdgcn_global_load_lds(ks, (lds_void*)(tile + grp * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vs, (lds_void*)(tile + kTileBytes / 2 + grp * 1024), 16, 0, 0);
+        // non-temporal: the cache rows are read once per step and should not push other data
+        // out of L2
+        __builtin_amdgcn_global_load_lds(ks, (lds_void*)(tile + grp * 1024), 16, 0, kNonTemporal);
+        __builtin_amdgcn_global_load_lds(vs, (lds_void*)(tile + kTileBytes / 2 + grp * 1024), 16, 0, kNonTemporal);
       });
     };
     // The CU's memory queue throttles issue, so only kDmaDepth blocks are kept in flight:
-    // block b + kDmaDepth is issued right after block b is handed over, and the barriers
-    // never wait for the issue of loads that are not needed yet.
-    static_for<(NB < kDmaDepth ? NB : kDmaDepth)>([&](auto bc) { issue_block(bc); });
-    lds_barrier();  // queries and own-token K rows written by the compute waves
+    // block b + kDmaDepth is issued right after block b has landed, and no count waits for
+    // the issue of loads that are not needed yet.
+    constexpr int D = NB < kDmaDepth ? NB : kDmaDepth;
+    static_for<D>([&](auto bc) { issue_block(bc); });
     static_for<NB>([&](auto bc) {
       constexpr int b = decltype(bc)::value;
-      constexpr int later = (b + kDmaDepth - 1 < NB - 1 ? b + kDmaDepth - 1 : NB - 1) - b;
+      constexpr int later = (b + D - 1 < NB - 1 ? b + D - 1 : NB - 1) - b;
       wait_vmcnt<4 * later>();  // loads are issued in block order: block b has landed
-      lds_barrier();
-      if constexpr (b + kDmaDepth < NB) issue_block(std::integral_constant<int, b + kDmaDepth>{});
+      arrive(&cnt[kCntBlock + b], lane);
+      if constexpr (b + D < NB) issue_block(std::integral_constant<int, b + D>{});
     });
     return;
   }
 
-  // ---------------- compute waves (256 threads)
+  // ---------------- compute waves (512 threads)
   const int j16 = tid & 15;
-  const int r16 = tid >> 4;  // 0..15
-  // 1. Issue every load of the prologue, then release the loader waves (start barrier), so
-  //    these small loads sit ahead of the cache stream in the CU's memory queue.
-  //    Query pass p covers folded row 16p + r16 (q head 2g + row/64, token row % 64), so token
-  //    16(p&3) + r16; own-token row tok = 16p + r16 (p < 4) uses the same cos/sin.
-  u32x4 qraw[8], graw, gkraw, kraw[4], vraw[4];
-  float qc[4][8], qs[4][8];
-#pragma unroll
-  for (int p = 0; p < 8; ++p)
-    qraw[p] = *reinterpret_cast<const u32x4*>(a.q + ((long long)(2 * g) * kT + 16 * p + r16) * kD + 8 * j16);
+  const int r16 = tid >> 4;  // 0..31
+  // 1. Prologue loads. Query pass p (0..3) covers folded row 32p + r16 (q head 2g + row/64,
+  //    token row % 64), so token set p & 1: token r16 or 32 + r16; own-token row set p (0..1)
+  //    is token 32p + r16 and uses the same cos/sin. Wave w's rows are the ones it fetched.
+  u32x4 graw, gkraw, kraw[2], vraw[2];
+  f32x4 cs_h[2][2];
   if constexpr (NORM) {
     graw = *reinterpret_cast<const u32x4*>(a.gq + 8 * j16);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) load_cos_sin(a.cos_t, a.sin_t, 16 * p + r16, j16, qc[p], qs[p]);
+    for (int p = 0; p < 2; ++p) load_cos_sin_half(a.cos_t, a.sin_t, 32 * p + r16, j16, cs_h[p][0], cs_h[p][1]);
   }
   const bool has_own = own_tail && k_end > a.S;  // this split holds own-token rows
   if (has_own) {
@@ -240,46 +308,61 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
     const uint16_t* vt = a.vt_base + g * a.tail_stride;
     if constexpr (NORM) gkraw = *reinterpret_cast<const u32x4*>(a.gk + 8 * j16);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int tok = 16 * p + r16;
+    for (int p = 0; p < 2; ++p) {
+      const int tok = 32 * p + r16;
       kraw[p] = *reinterpret_cast<const u32x4*>(kt + (long long)tok * kD + 8 * j16);
       vraw[p] = *reinterpret_cast<const u32x4*>(vt + (long long)tok * kD + 8 * j16);
     }
   }
-  lds_barrier();  // start: loader waves begin the cache stream
-
-  // 2. queries -> LDS (normed and roped unless given roped)
-  {
-    float qg[8];
-    if constexpr (NORM) unpack8v(graw, qg);
+  float qc[2][8], qs[2][8];
+  if constexpr (NORM) {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int r = 16 * p + r16;
-      u32x4 v = qraw[p];
-      if constexpr (NORM) {
-        float x[8];
-        unpack8v(v, x);
-        norm_rope_row16(x, qg, qc[p & 3], qs[p & 3], a.eps, j16);
-        v = pack8v(x);
-      }
-      *reinterpret_cast<u32x4*>(qlds + r * 256 + 16 * (j16 ^ kswz(r))) = v;
+    for (int p = 0; p < 2; ++p) split_cos_sin(cs_h[p][0], cs_h[p][1], j16, qc[p], qs[p]);
+  }
+  // 2. this wave's query rows, normed and roped in place in LDS (unless they came roped)
+  wait_vmcnt<0>();  // its query rows and every prologue load have landed
+  if constexpr (NORM) {
+    // all rows are read before any is written back, so the reads need not wait on writes
+    float qg[8], A[2][8], B[2][8];
+    unpack8v(graw, qg);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) rope_coef(qg, qc[p], qs[p], j16, A[p], B[p]);
+    u32x4 qv[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = 32 * p + r16;
+      qv[p] = *reinterpret_cast<const u32x4*>(qlds + r * 256 + 16 * (j16 ^ kswz(r)));
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      float x[8];
+      unpack8v(qv[p], x);
+      norm_rope_row16(x, A[p & 1], B[p & 1], a.eps);
+      qv[p] = pack8v(x);
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int r = 32 * p + r16;
+      *reinterpret_cast<u32x4*>(qlds + r * 256 + 16 * (j16 ^ kswz(r))) = qv[p];
     }
   }
   // 3. own-token rows of this split: K normed + roped (or taken roped) into kown and the cache
-  //    tail, V copied to the cache tail
+  //    tail, V copied to the cache tail (the stores come after every load has been waited
+  //    for, so no later wait includes them)
   if (has_own) {
     float gk[8];
     if constexpr (NORM) unpack8v(gkraw, gk);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int tok = 16 * p + r16;
+    for (int p = 0; p < 2; ++p) {
+      const int tok = 32 * p + r16;
       const int vk = a.S + tok;
       if (vk >= k_begin && vk < k_end) {
         u32x4 kv = kraw[p];
         if constexpr (NORM) {
-          float x[8];
+          float x[8], A[8], B[8];
           unpack8v(kv, x);
-          norm_rope_row16(x, gk, qc[p], qs[p], a.eps, j16);
+          rope_coef(gk, qc[p], qs[p], j16, A, B);
+          norm_rope_row16(x, A, B, a.eps);
           kv = pack8v(x);
         }
         const int rr = (vk - k_begin) & (kBlk - 1);
@@ -290,17 +373,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
       }
     }
   }
-  lds_barrier();  // queries and own-token K rows are in LDS
+  arrive(&cnt[kCntQNormed], lane);
+  await(&cnt[kCntQNormed], kComputeWaves);  // all 128 query rows and the own-token K rows are in LDS
 
+  const int qgrp = wave & 3;  // query rows 32 qgrp .. +31
+  const int par = wave >> 2;  // blocks b with b % 2 == par
   const int n = lane & 31;
   const int h = lane >> 5;
+  const int qrow = 32 * qgrp + n;
   bf16x8 qf[8];
-  {
-    const int qrow = 32 * wave + n;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      qf[kk] = *reinterpret_cast<const bf16x8*>(qlds + qrow * 256 + 16 * ((dcol(kk, h) >> 3) ^ kswz(qrow)));
-  }
+  for (int kk = 0; kk < 8; ++kk)
+    qf[kk] = *reinterpret_cast<const bf16x8*>(qlds + qrow * 256 + 16 * ((dcol(kk, h) >> 3) ^ kswz(qrow)));
+  arrive(&cnt[kCntQRead], lane);  // this wave no longer reads qlds
 
   f32x16 o[4];
 #pragma unroll
@@ -311,130 +396,172 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
   const float sc = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
   const int krow = perm_key(n);
 
-  // S^T = K Q^T of block b: K fragments from LDS (own-token rows from kown), then 8 MFMAs.
-  auto issue_qk = [&](auto bc) -> f32x16 {
-    constexpr int b = decltype(bc)::value;
-    const int kb = k_begin + b * kBlk;
-    const uint8_t* tk = pick<b>(t0, t1, t2, t3, t4, t5, t6);
-    const int kvk = kb + krow;
-    const uint8_t* krow_base = (own_tail && kvk >= a.S) ? kown + (kvk - a.S) * 256 : tk + krow * 256;
-    bf16x8 kf[8];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      kf[kk] = *reinterpret_cast<const bf16x8*>(krow_base + 16 * ((dcol(kk, h) >> 3) ^ kswz(krow)));
-    f32x16 s;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
-    return s;
-  };
-
-  // Software pipeline over the blocks: while the matrix cores run block b+1's S^T, the wave
-  // does block b's softmax; then block b's PV. Blocks past the split end (only in a short
-  // last split) are fully masked: they add nothing, and block 0 always holds at least one
-  // key, so m_run is finite from block 0 on.
-  lds_barrier();  // block 0 is in LDS
-  f32x16 s_cur = issue_qk(std::integral_constant<int, 0>{});
+  // Blocks of this wave's parity. A block past the split end (only in a short split) is
+  // skipped, but still awaited and counted as consumed, so that a consumed tile is never
+  // written by a load still in flight; the first block a wave processes holds at least one
+  // visible key, so m_run is finite after it.
   static_for<NB>([&](auto bc) {
     constexpr int b = decltype(bc)::value;
     const int kb = k_begin + b * kBlk;
-    const uint8_t* tv = pick<b>(t0, t1, t2, t3, t4, t5, t6) + kTileBytes / 2;
-    // V^T operands of block b: lane group G = lane >> 4, i = lane & 15 points at row
-    // 16c + 8(G>>1) + 4*half + i/4, columns 32t + 16(G&1) + 4(i&3) .. +3; the transpose
-    // read hands lane i of the group column 32t + 16(G&1) + i of 4 consecutive rows.
-    v4i16 vt[2][4][2];
-    {
-      const int G = lane >> 4, i = lane & 15;
+    if ((b & 1) != par) return;
+    uint8_t* tile = pick<b>(t0, t1, t2, t3, t4, t5);
+    await(&cnt[kCntBlock + b], kLoaderWaves);
+    if (kb < k_end) {
+      // S^T = K Q^T: K fragments from LDS (own-token rows from kown), then 8 MFMAs.
+      f32x16 s;
+      {
+        const int kvk = kb + krow;
+        const uint8_t* krow_base = (own_tail && kvk >= a.S) ? kown + (kvk - a.S) * 256 : tile + krow * 256;
+        bf16x8 kf[8];
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+        for (int kk = 0; kk < 8; ++kk)
+          kf[kk] = *reinterpret_cast<const bf16x8*>(krow_base + 16 * ((dcol(kk, h) >> 3) ^ kswz(krow)));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+      }
+      if (kb + kBlk > k_end) {  // only a split's last block can be partial
+        // accumulator element i of lane half h is key perm_key(8(i>>2) + 4h + (i&3)) = 8h + kofs(i)
+        const int lim = k_end - kb - 8 * h;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kofs = 16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3);
+          s[i] = (kofs < lim) ? s[i] : -INFINITY;
+        }
+      }
+      float bmax = s[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) bmax = fmaxf(bmax, s[i]);
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+      // The exponent reference m_run only moves when some row's max exceeds it by more than
+      // kRescale (log2 units): p stays below 2^kRescale, exact for the final normalisation,
+      // and the O rescale (64 multiplies) runs only on such jumps.
+      const float m_blk = bmax * sc;
+      if constexpr (b < 2) {
+        m_run = m_blk;  // this wave's first block: O and l are still zero
+      } else if (__any(m_blk > m_run + kRescale)) {
+        const float m_new = fmaxf(m_run, m_blk);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+      }
+      // v_exp_f32 directly: arguments are <= kRescale or -inf (masked)
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sc, -m_run));
+        psum += s[i];
+      }
+      l_run += psum;
+      // O^T += V^T P^T, in two halves of 16 keys. V^T operands: lane group G = lane >> 4,
+      // i = lane & 15 points at row 16c + 8(G>>1) + 4*half + i/4, columns 32t + 16(G&1) +
+      // 4(i&3) .. +3; the transpose read hands lane i of the group column 32t + 16(G&1) + i of
+      // 4 consecutive rows.
+      const uint8_t* tv = tile + kTileBytes / 2;
+      const int G = lane >> 4, li = lane & 15;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        bf16x8 pb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pb[j] = (__bf16)s[8 * c + j];
+        v4i16 vt[4][2];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
-            const int row = 16 * c + 8 * (G >> 1) + 4 * hf + (i >> 2);
-            const int chunk = 4 * t + 2 * (G & 1) + ((i & 3) >> 1);
-            vt[c][t][hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_v4i16*)(tv + row * 256 + 16 * (chunk ^ vswz(row)) + 8 * (i & 1)));
+            const int row = 16 * c + 8 * (G >> 1) + 4 * hf + (li >> 2);
+            const int chunk = 4 * t + 2 * (G & 1) + ((li & 3) >> 1);
+            vt[t][hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_v4i16*)(tv + row * 256 + 16 * (chunk ^ vswz(row)) + 8 * (li & 1)));
           }
-    }
-    f32x16 s_next;
-    if constexpr (b + 1 < NB) {
-      lds_barrier();  // block b+1 is in LDS
-      s_next = issue_qk(std::integral_constant<int, b + 1>{});
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    f32x16 s = s_cur;
-    if (__builtin_expect(kb + kBlk > k_end, 0)) {  // only a split's last block can be partial
-      // accumulator element i of lane half h is key perm_key(8(i>>2) + 4h + (i&3)) = 8h + kofs(i)
-      const int lim = k_end - kb - 8 * h;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kofs = 16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3);
-        s[i] = (kofs < lim) ? s[i] : -INFINITY;
+        for (int t = 0; t < 4; ++t) {
+          const v4i16 both[2] = {vt[t][0], vt[t][1]};
+          bf16x8 vf;
+          __builtin_memcpy(&vf, both, 16);
+          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[t], 0, 0, 0);
+        }
       }
     }
-    float bmax = s[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) bmax = fmaxf(bmax, s[i]);
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-    // The exponent reference m_run only moves when some row's max exceeds it by more than
-    // kRescale (log2 units): p stays below 2^kRescale, exact for the final normalisation,
-    // and the O rescale (64 multiplies) runs only on such jumps (always on block 0).
-    const float m_blk = bmax * sc;
-    if (__any(m_blk > m_run + kRescale)) {
-      const float m_new = fmaxf(m_run, m_blk);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on block 0
-      m_run = m_new;
-      l_run *= alpha;
+    arrive(&cnt[kCntDone + b], lane);
+  });
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  // Merge of the two parities. The odd wave's O goes to a 16 KB region that nobody reads any
+  // more: the tile of block qgrp once its four readers are done with it, or for qgrp >= NB a
+  // half of the query buffer once every compute wave holds its query fragments. Layout is
+  // lane-major: slot j = 4t + jj holds accumulator elements 4jj .. 4jj+3 of tile t.
+  if constexpr (NB >= 2) {
+    uint8_t* region;
+    int* freed;
+    int need;
+    if (qgrp < NB) {
+      region = qgrp == 0 ? t0 : qgrp == 1 ? t1 : qgrp == 2 ? t2 : t3;
+      freed = &cnt[kCntDone + qgrp];
+      need = 4;
+    } else {
+      region = qlds + (qgrp - NB) * kTileBytes;
+      freed = &cnt[kCntQRead];
+      need = kComputeWaves;
+    }
+    f32x4* xo = reinterpret_cast<f32x4*>(region) + lane;
+    if (par == 1) {
+      await(freed, need);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
-    }
-    // v_exp_f32 directly: arguments are <= kRescale or -inf (masked)
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sc, -m_run));
-      psum += s[i];
-    }
-    l_run += psum;
-    bf16x8 pb[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pb[c][j] = (__bf16)s[8 * c + j];
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const v4i16 both[2] = {vt[c][t][0], vt[c][t][1]};
-        bf16x8 vf;
-        __builtin_memcpy(&vf, both, 16);
-        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[c], o[t], 0, 0, 0);
+        for (int jj = 0; jj < 4; ++jj)
+          xo[(4 * t + jj) * 64] = f32x4{o[t][4 * jj], o[t][4 * jj + 1], o[t][4 * jj + 2], o[t][4 * jj + 3]};
+      if (h == 0) {
+        mlx[qgrp][0][n] = m_run;
+        mlx[qgrp][1][n] = l_tot;
       }
-    if constexpr (b + 1 < NB) s_cur = s_next;
-  });
-
-  const int qrow = 32 * wave + n;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const long long part = (long long)g * a.n_split + split;
-  // Partial O in the accumulator layout, lane-major: slot j = 4t + jj holds, for query row
-  // 32*wave + n, the 4 columns 32t + 8jj + 4h .. +3 (accumulator elements 4jj .. 4jj+3 of
-  // tile t); one store instruction writes 1 KB contiguously.
-  f32x4* po = reinterpret_cast<f32x4*>(a.po) + (part * 4 + wave) * (16 * 64) + lane;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const f32x4 v = {o[t][4 * jj], o[t][4 * jj + 1], o[t][4 * jj + 2], o[t][4 * jj + 3]};
-      po[(4 * t + jj) * 64] = v;
+      arrive(&cnt[kCntMerge + qgrp], lane);
+      return;
     }
-  if (h == 0) {
-    a.pm[part * kQRows + qrow] = m_run;
-    a.pl[part * kQRows + qrow] = l_tot;
+    await(&cnt[kCntMerge + qgrp], 1);
+    const float m_o = mlx[qgrp][0][n];
+    const float l_o = mlx[qgrp][1][n];
+    const float m_new = fmaxf(m_run, m_o);  // m_run is finite: block 0 holds a visible key
+    const float ae = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float ao = __builtin_amdgcn_exp2f(m_o - m_new);  // 0 if the odd wave saw no key
+    m_run = m_new;
+    const float l_all = ae * l_tot + ao * l_o;
+    const long long part = (long long)g * a.n_split + split;
+    f32x4* po = reinterpret_cast<f32x4*>(a.po) + (part * 4 + qgrp) * (16 * 64) + lane;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 x = xo[(4 * t + jj) * 64];
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = ae * o[t][4 * jj + e] + ao * x[e];
+        po[(4 * t + jj) * 64] = v;
+      }
+    if (h == 0) {
+      a.pm[part * kQRows + qrow] = m_run;
+      a.pl[part * kQRows + qrow] = l_all;
+    }
+  } else {
+    // a single block: the odd-parity waves hold nothing
+    if (par == 1) return;
+    const long long part = (long long)g * a.n_split + split;
+    f32x4* po = reinterpret_cast<f32x4*>(a.po) + (part * 4 + qgrp) * (16 * 64) + lane;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        po[(4 * t + jj) * 64] = f32x4{o[t][4 * jj], o[t][4 * jj + 1], o[t][4 * jj + 2], o[t][4 * jj + 3]};
+    if (h == 0) {
+      a.pm[part * kQRows + qrow] = m_run;
+      a.pl[part * kQRows + qrow] = l_tot;
+    }
   }
 }
 
@@ -532,8 +659,7 @@ hipError_t launch_attn(const AttnPlan& plan, const AttnLaunch& p, hipStream_t st
     case 3: e = launch_nb<3>(a, st); break;
     case 4: e = launch_nb<4>(a, st); break;
     case 5: e = launch_nb<5>(a, st); break;
-    case 6: e = launch_nb<6>(a, st); break;
-    default: e = launch_nb<7>(a, st); break;
+    default: e = launch_nb<6>(a, st); break;
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_attn_combine, dim3(kHkv * 16), dim3(256), 0, st, a.po, a.pm, a.pl, p.out, plan.n_split);

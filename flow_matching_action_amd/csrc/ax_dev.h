@@ -72,11 +72,27 @@ __device__ __forceinline__ float row_ror(float x) {
 
 // RMSNorm + rotate_half RoPE of one 128-wide row held by a group of 16 consecutive
 // lanes, 8 elements per lane (lane j16 holds columns 8*j16 .. 8*j16+7). The row partner
-// of column c +- 64 sits 8 lanes away. All lanes of the wave must call this together.
-// The sum of squares is a rotate-by-8/4/2/1 butterfly, which leaves the same bits in all
-// 16 lanes. x: the 8 inputs; g: the 8 gammas; c, s: cos/sin for columns (8*j16+e) mod 64.
-__device__ __forceinline__ void norm_rope_row16(float* x, const float* g, const float* c,
-                                                const float* s, float eps, int j16) {
+// of column c +- 64 sits 8 lanes away. All lanes of the wave must call these together.
+//
+// With y = x * inv * gamma (inv = 1/sqrt(mean(x^2) + eps)), the rotation of column j < 64 is
+// y_j cos_j - y_{j+64} sin_j and of column j + 64 is y_{j+64} cos_j + y_j sin_j, so
+//   out_e = inv * (x_e * A_e + x'_e * B_e),  A_e = gamma_e cos_e,  B_e = -+ gamma'_e sin_e
+// where ' is the partner column; A and B depend only on the token and the gamma vector and
+// are formed once per token (rope_coef), the per-row work is norm_rope_row16.
+// g: the 8 gammas; c, s: cos/sin for columns (8*j16+e) mod 64.
+__device__ __forceinline__ void rope_coef(const float* g, const float* c, const float* s, int j16, float* A,
+                                          float* B) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float gp = row_ror<8>(g[e]);
+    A[e] = g[e] * c[e];
+    B[e] = ((j16 < 8) ? -gp : gp) * s[e];  // lower half: x c - x' s; upper half: x c + x' s
+  }
+}
+
+// x: the 8 inputs, replaced by the outputs. The sum of squares is a rotate-by-8/4/2/1
+// butterfly, which leaves the same bits in all 16 lanes.
+__device__ __forceinline__ void norm_rope_row16(float* x, const float* A, const float* B, float eps) {
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
@@ -85,15 +101,11 @@ __device__ __forceinline__ void norm_rope_row16(float* x, const float* g, const 
   ss += row_ror<2>(ss);
   ss += row_ror<1>(ss);
   const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / kD) + eps);  // v_rsq_f32
-  float y[8];
+  float p[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) y[e] = x[e] * inv * g[e];
-  const float sgn = (j16 < 8) ? -1.0f : 1.0f;  // lower half: x c - x' s; upper half: x c + x' s
+  for (int e = 0; e < 8; ++e) p[e] = row_ror<8>(x[e]);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float p = row_ror<8>(y[e]);
-    x[e] = y[e] * c[e] + sgn * p * s[e];
-  }
+  for (int e = 0; e < 8; ++e) x[e] = inv * __builtin_fmaf(p[e], B[e], x[e] * A[e]);
 }
 
 }  // namespace ax

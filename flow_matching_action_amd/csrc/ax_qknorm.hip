@@ -59,7 +59,9 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(QkArgs a) {
     const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
     c[0] = c0.x; c[1] = c0.y; c[2] = c0.z; c[3] = c0.w; c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
     s[0] = s0.x; s[1] = s0.y; s[2] = s0.z; s[3] = s0.w; s[4] = s1.x; s[5] = s1.y; s[6] = s1.z; s[7] = s1.w;
-    norm_rope_row16(x, g, c, s, a.eps, j16);
+    float A[8], B[8];
+    rope_coef(g, c, s, j16, A, B);
+    norm_rope_row16(x, A, B, a.eps);
     if (live) {
       uint16_t* dst = is_q ? a.q_out + (long long)rr * kD
                            : a.k_dst + head * a.kv_head_stride + (a.kv_row0 + tok) * kD;

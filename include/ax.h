@@ -120,8 +120,8 @@ int ax_qk_norm_rope_tail(const uint16_t* q_in, const uint16_t* k_in, const uint1
 
 /*
  * Bytes of caller-owned device workspace that ax_expert_attn and
- * ax_expert_layer_attn need for (S, Smax): split partials (float32) plus the
- * roped q of the composite call. 0 if (S, Smax) is invalid.
+ * ax_expert_layer_attn need for (S, Smax): the per-split partial outputs,
+ * running maxima and row sums (float32). 0 if (S, Smax) is invalid.
  */
 size_t ax_expert_attn_workspace_bytes(int S, int Smax);
 
