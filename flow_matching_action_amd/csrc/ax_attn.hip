@@ -542,11 +542,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
         f32x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = ae * o[t][4 * jj + e] + ao * x[e];
-        po[(4 * t + jj) * 64] = v;
+        __builtin_nontemporal_store(v, &po[(4 * t + jj) * 64]);
       }
     if (h == 0) {
-      a.pm[part * kQRows + qrow] = m_run;
-      a.pl[part * kQRows + qrow] = l_all;
+      __builtin_nontemporal_store(m_run, &a.pm[part * kQRows + qrow]);
+      __builtin_nontemporal_store(l_all, &a.pl[part * kQRows + qrow]);
     }
   } else {
     // a single block: the odd-parity waves hold nothing
@@ -557,52 +557,96 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
-        po[(4 * t + jj) * 64] = f32x4{o[t][4 * jj], o[t][4 * jj + 1], o[t][4 * jj + 2], o[t][4 * jj + 3]};
+        __builtin_nontemporal_store(f32x4{o[t][4 * jj], o[t][4 * jj + 1], o[t][4 * jj + 2], o[t][4 * jj + 3]},
+                                    &po[(4 * t + jj) * 64]);
     if (h == 0) {
-      a.pm[part * kQRows + qrow] = m_run;
-      a.pl[part * kQRows + qrow] = l_tot;
+      __builtin_nontemporal_store(m_run, &a.pm[part * kQRows + qrow]);
+      __builtin_nontemporal_store(l_tot, &a.pl[part * kQRows + qrow]);
     }
   }
 }
 
-// Combine. Thread -> (head g, query row q, 4 columns d0..d0+3); it reads one float4 of each
-// split's partial (slot and lane of the accumulator layout above), then
-// out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c.
-// Grid: 8 heads x 16 blocks of 256 threads; block: 32 rows x 8 column quads.
-__global__ __launch_bounds__(256) void k_attn_combine(const float* po, const float* pm, const float* pl,
+// Combine: out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c, M = max_c m_c.
+// Workgroup (head g, rows 8r .. 8r+7, column half hc): 512 threads in 4 split groups of 128
+// (8 rows x 16 column quads); group k reduces splits k, k + 4, ..., issuing the loads of up to
+// kCombBatch splits before using any of them, so the whole partial set is in flight at once.
+// The 8 rows of a (slot, half) of the accumulator layout are one 128-byte line. The groups meet
+// in LDS.
+constexpr int kCombGroups = 4;
+constexpr int kCombBatch = 8;
+__global__ __launch_bounds__(512) void k_attn_combine(const float* po, const float* pm, const float* pl,
                                                       uint16_t* out, int n_split) {
+  __shared__ float sM[kCombGroups][8], sL[kCombGroups][8];
+  __shared__ f32x4 sA[kCombGroups][128];
   const int g = blockIdx.x % kHkv;
-  const int rest = blockIdx.x / kHkv;   // 0..15
-  const int wave = rest & 3;            // query rows 32*wave .. +31
-  const int quad0 = (rest >> 2) * 8;    // column quads quad0 .. quad0+7 of 32
-  const int n = threadIdx.x & 31;
-  const int quad = quad0 + (threadIdx.x >> 5);
-  const int q = 32 * wave + n;
-  const int d0 = 4 * quad;              // = 32t + 8jj + 4h
-  const int t = d0 >> 5, jj = (d0 >> 3) & 3, h = (d0 >> 2) & 1;
-  const int slot = 4 * t + jj, lane = n + 32 * h;
+  const int rest = blockIdx.x / kHkv;   // 0..31
+  const int rblk = rest >> 1;           // rows 8 rblk .. +7
+  const int hc = rest & 1;              // column quads 16 hc .. +15
+  const int grp = threadIdx.x >> 7;
+  const int t = threadIdx.x & 127;
+  const int rloc = t >> 4;
+  const int quad = 16 * hc + (t & 15);
+  const int q = 8 * rblk + rloc;
+  const int d0 = 4 * quad;              // = 32 tt + 8 jj + 4 h
+  const int tt = d0 >> 5, jj = (d0 >> 3) & 3, h = (d0 >> 2) & 1;
+  const int slot = 4 * tt + jj, lane = (q & 31) + 32 * h;
   const float* pmg = pm + (long long)g * n_split * kQRows + q;
   const float* plg = pl + (long long)g * n_split * kQRows + q;
-  const f32x4* pog = reinterpret_cast<const f32x4*>(po) + ((long long)g * n_split * 4 + wave) * (16 * 64) +
+  const f32x4* pog = reinterpret_cast<const f32x4*>(po) + ((long long)g * n_split * 4 + (q >> 5)) * (16 * 64) +
                      slot * 64 + lane;
   const long long pstride = 4 * 16 * 64;  // float4s per split partial
-  float M = -INFINITY;
-#pragma unroll 8
-  for (int c = 0; c < n_split; ++c) M = fmaxf(M, pmg[(long long)c * kQRows]);
-  float L = 0.f;
+  float M = -INFINITY, L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int c = 0; c < n_split; ++c) {
-    const float w = __builtin_amdgcn_exp2f(pmg[(long long)c * kQRows] - M);
-    L += w * plg[(long long)c * kQRows];
-    const f32x4 v = pog[(long long)c * pstride];
-    acc[0] += w * v[0]; acc[1] += w * v[1]; acc[2] += w * v[2]; acc[3] += w * v[3];
+  for (int c0 = grp; c0 < n_split; c0 += kCombGroups * kCombBatch) {
+    float mv[kCombBatch], lv[kCombBatch];
+    f32x4 ov[kCombBatch];
+#pragma unroll
+    for (int k = 0; k < kCombBatch; ++k) {
+      const int c = min(c0 + kCombGroups * k, n_split - 1);  // past the end: a repeat, weighted 0 below
+      mv[k] = pmg[(long long)c * kQRows];
+      lv[k] = plg[(long long)c * kQRows];
+      ov[k] = pog[(long long)c * pstride];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the batch is issued before any is used
+    float Mb = M;
+#pragma unroll
+    for (int k = 0; k < kCombBatch; ++k)
+      if (c0 + kCombGroups * k < n_split) Mb = fmaxf(Mb, mv[k]);
+    const float r = __builtin_amdgcn_exp2f(M - Mb);  // 0 while M is -inf
+    L *= r;
+    acc[0] *= r; acc[1] *= r; acc[2] *= r; acc[3] *= r;
+    M = Mb;
+#pragma unroll
+    for (int k = 0; k < kCombBatch; ++k) {
+      const float w = (c0 + kCombGroups * k < n_split) ? __builtin_amdgcn_exp2f(mv[k] - M) : 0.f;
+      L += w * lv[k];
+      acc[0] += w * ov[k][0]; acc[1] += w * ov[k][1]; acc[2] += w * ov[k][2]; acc[3] += w * ov[k][3];
+    }
   }
-  const float inv = 1.0f / L;
-  uint2 r;
-  r.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-  r.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-  *reinterpret_cast<uint2*>(out + ((long long)g * kQRows + q) * kD + d0) = r;
+  if ((t & 15) == 0) {
+    sM[grp][rloc] = M;
+    sL[grp][rloc] = L;
+  }
+  sA[grp][t] = acc;
+  __syncthreads();
+  if (grp != 0) return;
+  float Mt = sM[0][rloc];  // group 0 holds split 0, so Mt is finite
+#pragma unroll
+  for (int k = 1; k < kCombGroups; ++k) Mt = fmaxf(Mt, sM[k][rloc]);
+  float Lt = 0.f;
+  f32x4 At = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < kCombGroups; ++k) {
+    const float w = __builtin_amdgcn_exp2f(sM[k][rloc] - Mt);  // 0 for a group without splits
+    Lt += w * sL[k][rloc];
+    const f32x4 v = sA[k][t];
+    At[0] += w * v[0]; At[1] += w * v[1]; At[2] += w * v[2]; At[3] += w * v[3];
+  }
+  const float inv = 1.0f / Lt;
+  uint2 o2;
+  o2.x = pack_bf16x2(At[0] * inv, At[1] * inv);
+  o2.y = pack_bf16x2(At[2] * inv, At[3] * inv);
+  *reinterpret_cast<uint2*>(out + ((long long)g * kQRows + q) * kD + d0) = o2;
 }
 
 AttnPlan attn_plan(int S, int /*Smax*/) {
@@ -662,7 +706,7 @@ hipError_t launch_attn(const AttnPlan& plan, const AttnLaunch& p, hipStream_t st
     default: e = launch_nb<6>(a, st); break;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_combine, dim3(kHkv * 16), dim3(256), 0, st, a.po, a.pm, a.pl, p.out, plan.n_split);
+  hipLaunchKernelGGL(k_attn_combine, dim3(kHkv * 32), dim3(512), 0, st, a.po, a.pm, a.pl, p.out, plan.n_split);
   return hipGetLastError();
 }
 
