@@ -8,7 +8,13 @@ S = 4700, bf16. Steps rotate over 64 distinct layer caches (2.1 GB, far beyond t
 timed steps are one hipGraph replay, bracketed by device synchronisation and
 timed with HIP events on the stream the graph runs on.
 
+The roofline figures are those of the dominant kernel, the fused norm + RoPE + tail
+write + split attention launch: a second graph of the same K steps, with that launch
+alone, is timed the same way, and its algorithmic bytes (the step's, less the output
+that the combine writes) are divided by its average launch time.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --calibrate-copy BYTES   (a plain copy of known size, for counter runs)
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -38,6 +44,9 @@ def algorithmic_bytes(S: int, Smax: int) -> int:
     tail = 2 * 8 * 64 * row
     out = 16 * 64 * row
     return visible + q_in + kv_in + tail + out
+
+
+OUT_BYTES = 16 * 64 * 128 * 2
 
 
 def algorithmic_flops(S: int) -> int:
@@ -72,7 +81,7 @@ class RotatingWorkload:
         self.cos = torch.from_numpy(cos).to(dev)
         self.sin = torch.from_numpy(sin).to(dev)
         self.out = [torch.empty((16, 64, 128), dtype=torch.bfloat16, device=dev) for _ in range(n_layers)]
-        self.ws = torch.empty(ax.expert_attn_workspace_bytes(S, Smax), dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(ax.expert_attn_workspace_bytes(S, Smax), dtype=torch.uint8, device=dev)
         for t in self.K + self.V:
             assert t.shape == (8, Smax, 128) and t.is_contiguous()
         torch.cuda.synchronize()
@@ -84,6 +93,13 @@ class RotatingWorkload:
         self.ax.expert_layer_attn(self.q[j], self.k[j], self.v[j], self.gq[l], self.gk[l], self.cos, self.sin, EPS,
                                   self.K[l], self.V[l], self.S, self.Smax, self.out[l], self.ws, stream=stream)
 
+    def step_attention_only(self, i: int, stream=None):
+        """Step i without the combine: the dominant launch alone."""
+        l = i % self.n_layers
+        j = i % self.n_sets
+        self.ax.expert_layer_attn_split(self.q[j], self.k[j], self.v[j], self.gq[l], self.gk[l], self.cos, self.sin,
+                                        EPS, self.K[l], self.V[l], self.S, self.Smax, self.ws, stream=stream)
+
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
@@ -94,8 +110,9 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(per_launch_alg: float):
-    """HBM bytes per step from the committed counter summary, if it was taken on the current kernels."""
+def load_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter summary, if the summary
+    was taken on the current kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic_expert_layer_attn_smax8192_s4700.txt")
     if not os.path.exists(path):
         return None
@@ -108,7 +125,7 @@ def load_traffic(per_launch_alg: float):
     if vals.get("kernel_source_hash") != kernel_source_hash():
         return None
     try:
-        return float(vals["hbm_bytes_per_step"])
+        return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -136,6 +153,44 @@ def cpu_baseline(n_layers: int = 6) -> dict:
                       f"median per layer; numpy float64 on the host"}
 
 
+def timed_graph(torch, stream, enqueue, first: int, K: int, replays: int) -> list:
+    """Capture enqueue(first .. first+K-1) as one graph; wall time of each replay (ms), HIP events on stream."""
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(K):
+                enqueue(first + i, stream)
+    torch.cuda.synchronize()
+    times_ms = []
+    for _ in range(max(1, replays)):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        times_ms.append(e0.elapsed_time(e1))
+    return times_ms
+
+
+def calibrate_copy(nbytes: int) -> int:
+    """Copy nbytes (multiple of 16) from one device buffer to another, 5 times, for byte-counter calibration."""
+    import torch
+    from flow_matching_action_amd import ax
+    torch.cuda.set_device(0)
+    src = torch.ones(nbytes // 16 * 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        ax.copy_words(src, dst, nbytes // 16)
+    torch.cuda.synchronize()
+    ok = bool(torch.equal(src, dst))
+    print(json.dumps({"calibrate_copy_bytes": nbytes // 16 * 16, "launches": 5, "ok": ok}), flush=True)
+    return 0 if ok else 1
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,7 +198,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=N_LAYERS * N_EULER)
     ap.add_argument("--replays", type=int, default=5, help="timed replays of the K-step graph (median reported)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run the plain copy kernel on BYTES (for rocprofv3 --pmc calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        return calibrate_copy(args.calibrate_copy)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the expert-attention step is measured on a single MI355X); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
@@ -167,32 +226,19 @@ def main() -> int:
             wl.step(i, stream)
     torch.cuda.synchronize()
 
-    # capture the K timed steps as one graph
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        with torch.cuda.graph(graph, stream=stream):
-            for i in range(K):
-                wl.step(W + i, stream)
-    torch.cuda.synchronize()
-
-    times_ms = []
-    for _ in range(max(1, args.replays)):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            e0.record(stream)
-            graph.replay()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        times_ms.append(e0.elapsed_time(e1))
+    # the K timed steps as one graph (headline), then the dominant launch alone over the same steps
+    times_ms = timed_graph(torch, stream, wl.step, W, K, args.replays)
     ms_total = statistics.median(times_ms)
     us_layer = ms_total * 1e3 / K
     out_ok = all(bool(torch.isfinite(o.float()).all()) for o in wl.out)
+    attn_ms = timed_graph(torch, stream, wl.step_attention_only, W, K, args.replays)
+    us_attn = statistics.median(attn_ms) * 1e3 / K
 
     b_alg = algorithmic_bytes(S, SMAX)
     gbs = b_alg / (us_layer * 1e-6) / 1e9
-    traffic = load_traffic(b_alg)
+    b_attn = b_alg - OUT_BYTES
+    gbs_attn = b_attn / (us_attn * 1e-6) / 1e9
+    traffic = load_traffic()
     result = {
         "metric": METRIC,
         "value": round(us_layer, 3),
@@ -210,12 +256,15 @@ def main() -> int:
                                "(2.1 GB, cold), fresh q/k/v per (Euler step, layer), hipGraph of K steps",
                    "Smax": SMAX, "S": S, "layers_rotated": N_LAYERS, "rope_delta": ROPE_DELTA},
         "achieved_hbm_gbs": round(gbs, 1),
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbs_attn, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs_attn / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "expert_layer_attn step (all kernels of one step)",
-                     "algorithmic_bytes_per_step": b_alg,
-                     "algorithmic_flops_per_step": algorithmic_flops(S)},
+                     "kernel": "k_attn_fused (q/k norm + RoPE + tail write + split attention), one launch per step",
+                     "kernel_us_per_launch": round(us_attn, 3),
+                     "algorithmic_bytes_per_launch": b_attn,
+                     "algorithmic_flops_per_launch": algorithmic_flops(S),
+                     "step_algorithmic_bytes": b_alg,
+                     "step_frac": round(gbs / HBM_PEAK_GBS, 4)},
         "replays_ms": [round(t, 4) for t in times_ms],
         "outputs_finite": out_ok,
     }

@@ -62,12 +62,17 @@ lib.ax_expert_attn.argtypes = [_P, _P, _P, _P, _P, _I, _I, _P, _P, ctypes.c_size
 lib.ax_expert_layer_attn.restype = _I
 lib.ax_expert_layer_attn.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _I, _I, _P, _P,
                                      ctypes.c_size_t, _P]
+lib.ax_expert_layer_attn_split.restype = _I
+lib.ax_expert_layer_attn_split.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _I, _I, _P,
+                                           ctypes.c_size_t, _P]
+lib.ax_expert_attn_combine.restype = _I
+lib.ax_expert_attn_combine.argtypes = [_P, ctypes.c_size_t, _I, _I, _P, _P]
 lib.ax_copy_words.restype = _I
 lib.ax_copy_words.argtypes = [_P, _P, ctypes.c_size_t, _P]
 
 EXPORTS = ("ax_abi_version", "ax_strerror", "ax_rope_tables", "ax_qk_norm_rope", "ax_cache_tail_write",
            "ax_qk_norm_rope_tail", "ax_expert_attn_workspace_bytes", "ax_expert_attn",
-           "ax_expert_layer_attn", "ax_copy_words")
+           "ax_expert_layer_attn", "ax_expert_layer_attn_split", "ax_expert_attn_combine", "ax_copy_words")
 
 
 def _check(fn: str, code: int) -> None:
@@ -143,6 +148,20 @@ def expert_layer_attn(q_in, k_in, v_in, gamma_q, gamma_k, rope_cos, rope_sin, ep
         _ptr(q_in), _ptr(k_in), _ptr(v_in), _ptr(gamma_q), _ptr(gamma_k), _ptr(rope_cos), _ptr(rope_sin),
         float(eps), _ptr(Kc), _ptr(Vc), int(S), int(Smax), _ptr(out), _ptr(ws),
         ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
+
+
+def expert_layer_attn_split(q_in, k_in, v_in, gamma_q, gamma_k, rope_cos, rope_sin, eps, Kc, Vc, S: int,
+                            Smax: int, ws, stream=None):
+    _check("ax_expert_layer_attn_split", lib.ax_expert_layer_attn_split(
+        _ptr(q_in), _ptr(k_in), _ptr(v_in), _ptr(gamma_q), _ptr(gamma_k), _ptr(rope_cos), _ptr(rope_sin),
+        float(eps), _ptr(Kc), _ptr(Vc), int(S), int(Smax), _ptr(ws),
+        ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
+
+
+def expert_attn_combine(ws, S: int, Smax: int, out, stream=None):
+    _check("ax_expert_attn_combine", lib.ax_expert_attn_combine(
+        _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, int(S), int(Smax), _ptr(out),
+        _stream(stream)))
 
 
 def copy_words(src, dst, n_words16: int, stream=None):

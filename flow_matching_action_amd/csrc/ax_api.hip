@@ -154,6 +154,31 @@ int ax_expert_layer_attn(const uint16_t* q_in, const uint16_t* k_in, const uint1
   return status(ax::launch_attn(plan, p, as_stream(stream)));
 }
 
+int ax_expert_layer_attn_split(const uint16_t* q_in, const uint16_t* k_in, const uint16_t* v_in,
+                               const uint16_t* gamma_q, const uint16_t* gamma_k, const float* rope_cos,
+                               const float* rope_sin, float eps, uint16_t* Kc, uint16_t* Vc, int S, int Smax,
+                               void* ws, size_t ws_bytes, void* stream) {
+  int r = check_ptrs({q_in, k_in, v_in, gamma_q, gamma_k, rope_cos, rope_sin, Kc, Vc, ws});
+  if (r == AX_OK) r = check_shape(S, Smax);
+  if (r == AX_OK) r = check_eps(eps);
+  if (r == AX_OK) r = check_ws(ws, ws_bytes, S, Smax);
+  if (r == AX_OK) r = check_device();
+  if (r != AX_OK) return r;
+  const ax::AttnPlan plan = ax::attn_plan(S, Smax);
+  ax::AttnLaunch p{q_in, gamma_q, gamma_k, rope_cos, rope_sin, eps, k_in, v_in, Kc, Vc, nullptr, ws, S, Smax,
+                   /*q_norm=*/1, /*tail_norm=*/1};
+  return status(ax::launch_attn_split(plan, p, as_stream(stream)));
+}
+
+int ax_expert_attn_combine(const void* ws, size_t ws_bytes, int S, int Smax, uint16_t* out, void* stream) {
+  int r = check_ptrs({ws, out});
+  if (r == AX_OK) r = check_shape(S, Smax);
+  if (r == AX_OK) r = check_ws(ws, ws_bytes, S, Smax);
+  if (r == AX_OK) r = check_device();
+  if (r != AX_OK) return r;
+  return status(ax::launch_attn_combine(ax::attn_plan(S, Smax), ws, out, as_stream(stream)));
+}
+
 int ax_copy_words(const void* src, void* dst, size_t n_words16, void* stream) {
   int r = check_ptrs({src, dst});
   if (r == AX_OK) r = check_device();

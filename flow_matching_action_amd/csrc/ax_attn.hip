@@ -678,10 +678,36 @@ static hipError_t launch_nb(const FusedArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_attn(const AttnPlan& plan, const AttnLaunch& p, hipStream_t st) {
-  FusedArgs a;
+// Partial buffers inside the workspace.
+struct WsLayout {
+  float* po;
+  float* pm;
+  float* pl;
+};
+static WsLayout ws_layout(const AttnPlan& plan, const void* ws) {
   const size_t parts = (size_t)kHkv * plan.n_split;
-  char* ws = static_cast<char*>(p.ws);
+  char* w = static_cast<char*>(const_cast<void*>(ws));
+  WsLayout l;
+  l.po = reinterpret_cast<float*>(w);
+  l.pm = reinterpret_cast<float*>(w + align256(parts * kD * kQRows * 4));
+  l.pl = reinterpret_cast<float*>(w + align256(parts * kD * kQRows * 4) + align256(parts * kQRows * 4));
+  return l;
+}
+
+hipError_t launch_attn_combine(const AttnPlan& plan, const void* ws, uint16_t* out, hipStream_t st) {
+  const WsLayout l = ws_layout(plan, ws);
+  hipLaunchKernelGGL(k_attn_combine, dim3(kHkv * 32), dim3(512), 0, st, l.po, l.pm, l.pl, out, plan.n_split);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn(const AttnPlan& plan, const AttnLaunch& p, hipStream_t st) {
+  const hipError_t e = launch_attn_split(plan, p, st);
+  if (e != hipSuccess) return e;
+  return launch_attn_combine(plan, p.ws, p.out, st);
+}
+
+hipError_t launch_attn_split(const AttnPlan& plan, const AttnLaunch& p, hipStream_t st) {
+  FusedArgs a;
   a.q = p.q; a.gq = p.gq; a.gk = p.gk; a.cos_t = p.cos_t; a.sin_t = p.sin_t; a.eps = p.eps;
   a.own_tail = p.k_tail != nullptr;
   if (a.own_tail) {
@@ -691,9 +717,8 @@ hipError_t launch_attn(const AttnPlan& plan, const AttnLaunch& p, hipStream_t st
     a.tail_stride = (long long)p.Smax * kD;
   }
   a.Kc = p.Kc; a.Vc = p.Vc;
-  a.po = reinterpret_cast<float*>(ws);
-  a.pm = reinterpret_cast<float*>(ws + align256(parts * kD * kQRows * 4));
-  a.pl = reinterpret_cast<float*>(ws + align256(parts * kD * kQRows * 4) + align256(parts * kQRows * 4));
+  const WsLayout l = ws_layout(plan, p.ws);
+  a.po = l.po; a.pm = l.pm; a.pl = l.pl;
   a.S = p.S; a.Smax = p.Smax; a.n_split = plan.n_split; a.kps = plan.keys_per_split;
   a.q_norm = p.q_norm; a.tail_norm = p.tail_norm;
   hipError_t e;
@@ -705,9 +730,7 @@ hipError_t launch_attn(const AttnPlan& plan, const AttnLaunch& p, hipStream_t st
     case 5: e = launch_nb<5>(a, st); break;
     default: e = launch_nb<6>(a, st); break;
   }
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_combine, dim3(kHkv * 32), dim3(512), 0, st, a.po, a.pm, a.pl, p.out, plan.n_split);
-  return hipGetLastError();
+  return e;
 }
 
 __global__ __launch_bounds__(256) void k_copy_words(const u32x4* src, u32x4* dst, size_t n) {

@@ -53,7 +53,9 @@ struct AttnLaunch {
   int q_norm, tail_norm;
 };
 
-hipError_t launch_attn(const AttnPlan& plan, const AttnLaunch& p, hipStream_t st);
+hipError_t launch_attn(const AttnPlan& plan, const AttnLaunch& p, hipStream_t st);        // both
+hipError_t launch_attn_split(const AttnPlan& plan, const AttnLaunch& p, hipStream_t st);  // partials
+hipError_t launch_attn_combine(const AttnPlan& plan, const void* ws, uint16_t* out, hipStream_t st);
 
 hipError_t launch_copy_words(const void* src, void* dst, size_t n, hipStream_t st);
 

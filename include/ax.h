@@ -145,14 +145,35 @@ int ax_expert_attn(const uint16_t* q_roped, const uint16_t* k_own, const uint16_
                    size_t ws_bytes, void* stream);
 
 /*
- * The whole attention step of one layer: ax_qk_norm_rope_tail followed by
- * ax_expert_attn on its roped q (k_own = v_own = NULL). Updates the cache
- * tail of Kc/Vc and writes out [16][64][128]. Inputs as above.
+ * The whole attention step of one layer: the result of ax_qk_norm_rope_tail
+ * followed by ax_expert_attn on its roped q (k_own = v_own = NULL), bit for
+ * bit, in two launches (norm + RoPE + tail write + split attention in one
+ * kernel, then the combine). Updates the cache tail of Kc/Vc and writes out
+ * [16][64][128]. Inputs as above.
  */
 int ax_expert_layer_attn(const uint16_t* q_in, const uint16_t* k_in, const uint16_t* v_in,
                          const uint16_t* gamma_q, const uint16_t* gamma_k, const float* rope_cos,
                          const float* rope_sin, float eps, uint16_t* Kc, uint16_t* Vc, int S,
                          int Smax, uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The two launches of ax_expert_layer_attn, for callers that time or order
+ * them separately (same pages and passages as above).
+ * ax_expert_layer_attn_split: q/k RMSNorm, RoPE, the cache tail write and the
+ * split attention; every split's partial (unnormalised O, running max, row
+ * sum; float32) is left in ws. ax_expert_attn_combine: the log-sum-exp
+ * combine of the partials in ws for the same (S, Smax) into out. The two in
+ * this order on one stream with the same ws equal ax_expert_layer_attn. The
+ * combine reads only ws; it is undefined unless the split call for (S, Smax)
+ * ran before it on ws.
+ */
+int ax_expert_layer_attn_split(const uint16_t* q_in, const uint16_t* k_in, const uint16_t* v_in,
+                               const uint16_t* gamma_q, const uint16_t* gamma_k,
+                               const float* rope_cos, const float* rope_sin, float eps,
+                               uint16_t* Kc, uint16_t* Vc, int S, int Smax, void* ws,
+                               size_t ws_bytes, void* stream);
+int ax_expert_attn_combine(const void* ws, size_t ws_bytes, int S, int Smax, uint16_t* out,
+                           void* stream);
 
 /*
  * Measurement helper: dst[i] = src[i] for n 16-byte words, one plain

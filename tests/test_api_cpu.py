@@ -106,6 +106,26 @@ def test_attn_validation_codes():
     assert ax.lib.ax_copy_words(None, FAKE, 1, None) == ax.AX_E_NULL
 
 
+def test_split_and_combine_validation_codes():
+    sp = ax.lib.ax_expert_layer_attn_split
+
+    def split(q=FAKE, Kc=FAKE, S=128, Smax=256, eps=1e-6, ws=FAKE, ws_bytes=1 << 30):
+        return sp(q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, eps, Kc, FAKE, S, Smax, ws, ws_bytes, None)
+
+    assert split(q=None) == ax.AX_E_NULL
+    assert split(Kc=MIS) == ax.AX_E_ALIGN
+    assert split(S=193) == ax.AX_E_SHAPE
+    assert split(eps=float("nan")) == ax.AX_E_ARG
+    assert split(ws_bytes=16) == ax.AX_E_WORKSPACE
+    assert split(ws=FAKE + 16) == ax.AX_E_WORKSPACE
+    cb = ax.lib.ax_expert_attn_combine
+    assert cb(None, 1 << 30, 128, 256, FAKE, None) == ax.AX_E_NULL
+    assert cb(FAKE, 1 << 30, 128, 256, None, None) == ax.AX_E_NULL
+    assert cb(FAKE, 1 << 30, 128, 256, MIS, None) == ax.AX_E_ALIGN
+    assert cb(FAKE, 1 << 30, -1, 256, FAKE, None) == ax.AX_E_SHAPE
+    assert cb(FAKE, 8, 128, 256, FAKE, None) == ax.AX_E_WORKSPACE
+
+
 def test_no_device_is_reported_not_launched():
     import torch
     if torch.cuda.is_available():

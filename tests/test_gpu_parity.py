@@ -159,6 +159,22 @@ def test_attn_with_own_kv_path(ax):
     assert np.array_equal(down(Kc), down(L.Kc)) and np.array_equal(down(Vc), down(L.Vc))
 
 
+def test_split_then_combine_equals_layer(ax):
+    # The two launches called separately give the composite call's output and cache bit for bit.
+    inp = synth.workload_inputs(synth.HEADLINE)
+    say("expert_layer_attn_split + expert_attn_combine vs expert_layer_attn, headline workload")
+    L = Layer(inp, ax)
+    ref_bits = L.run(ax)
+    Kc, Vc = up(inp["Kc"]), up(inp["Vc"])
+    out = torch.empty_like(L.out)
+    ws = torch.zeros_like(L.ws)
+    ax.expert_layer_attn_split(L.q, L.k, L.v, L.gq, L.gk, L.cos, L.sin, 1e-6, Kc, Vc, L.S, L.Smax, ws)
+    ax.expert_attn_combine(ws, L.S, L.Smax, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(down(out), ref_bits)
+    assert np.array_equal(down(Kc), down(L.Kc)) and np.array_equal(down(Vc), down(L.Vc))
+
+
 def test_repeat_is_bitwise_deterministic(ax):
     inp = synth.workload_inputs(synth.HEADLINE)
     say("determinism x3, headline workload")
