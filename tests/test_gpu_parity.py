@@ -209,3 +209,29 @@ def test_graph_replay_equals_eager(ax):
         torch.cuda.synchronize()
         assert np.array_equal(down(L.out), eager), f"replay {rep}"
         torch.randn(1 << 20, device=DEV).sum().item()   # eager work between replays
+
+
+@pytest.mark.parametrize("step,layer", [(0, 0), (0, 31), (0, 63), (9, 0), (9, 31), (9, 63)])
+def test_throughput_sequence_matches_oracle(ax, step, layer):
+    # The benchmark's own inputs (seeded on the device: 64 layer caches, fresh q/k/v per
+    # (Euler step, layer)) in its launch configuration, copied back and checked against the oracle.
+    S, Smax = 4700, 8192
+    say(f"throughput sequence, Euler step {step}, layer {layer}")
+    Kc, Vc = synth.device_cache(Smax, S, layer, DEV)
+    Kc, Vc = Kc.contiguous(), Vc.contiguous()
+    q, k, v = (t.contiguous() for t in synth.device_qkv(step, layer, DEV))
+    gq, gk = (t.contiguous() for t in synth.device_gammas(layer, DEV))
+    bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)  # noqa: E731
+    inp = {"q": bits(q), "k": bits(k), "v": bits(v), "gq": bits(gq), "gk": bits(gk), "Kc": bits(Kc),
+           "Vc": bits(Vc), "S": S, "Smax": Smax, "rope_delta": 0}
+    ref = ref_layer(inp)
+    cos, sin = ax.rope_tables(S)
+    cos, sin = torch.from_numpy(cos).to(DEV), torch.from_numpy(sin).to(DEV)
+    out = torch.empty((16, 64, 128), dtype=torch.bfloat16, device=DEV)
+    ws = torch.zeros(ax.expert_attn_workspace_bytes(S, Smax), dtype=torch.uint8, device=DEV)
+    ax.expert_layer_attn(q, k, v, gq, gk, cos, sin, 1e-6, Kc, Vc, S, Smax, out, ws)
+    torch.cuda.synchronize()
+    check_out(bits(out), ref, f"sequence s={step} l={layer}")
+    assert np.array_equal(bits(Vc)[:, Smax - 64:], inp["v"])
+    assert np.array_equal(bits(Vc)[:, :Smax - 64], inp["Vc"][:, :Smax - 64])
+    assert np.array_equal(bits(Kc)[:, :Smax - 64], inp["Kc"][:, :Smax - 64])
