@@ -73,6 +73,7 @@ struct FusedArgs {
   float* pm;               // [8][n_split][128]
   float* pl;
   int S, Smax, n_split, kps;
+  int n_cache_split;       // splits over cache keys [0, S); split n_cache_split holds the 64 own tokens
   int q_norm, tail_norm;
 };
 
@@ -224,8 +225,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
   const int g = blockIdx.x % kHkv;
   const int split = blockIdx.x / kHkv;
   const int n_keys = a.S + kT;
-  const int k_begin = split * a.kps;
-  const int k_end = min(k_begin + a.kps, n_keys);
+  // Cache splits cover [0, S) in kps-key ranges; the last split holds just the 64 own-token
+  // keys, so that its extra work (own k norm, tail write) falls on a short split.
+  const bool own_split = split >= a.n_cache_split;
+  const int k_begin = own_split ? a.S : split * a.kps;
+  const int k_end = own_split ? n_keys : min(k_begin + a.kps, a.S);
   const long long head_off = (long long)g * a.Smax * kD;
   // blocks holding own-token rows that need the tail step (norm of k and/or cache tail write)
   const bool own_tail = a.own_tail != 0;
@@ -652,13 +656,16 @@ __global__ __launch_bounds__(512) void k_attn_combine(const float* po, const flo
 AttnPlan attn_plan(int S, int /*Smax*/) {
   AttnPlan p;
   p.n_keys = S + kT;
-  const int target = 32;  // splits per head: 8 heads x 32 = 256 workgroups, one per CU
-  int kps = (p.n_keys + target - 1) / target;
+  // 31 cache splits + the own-token split per head: 8 heads x 32 = 256 workgroups, one per CU
+  const int target = 31;
+  int kps = (S + target - 1) / target;
   if (kps < kBlk) kps = kBlk;
   if (kps > kBlk * kMaxNB) kps = kBlk * kMaxNB;
   p.keys_per_split = kps;
-  p.n_split = (p.n_keys + kps - 1) / kps;
+  p.n_cache_split = (S + kps - 1) / kps;
+  p.n_split = p.n_cache_split + 1;
   p.blocks = (kps + kBlk - 1) / kBlk;
+  if (p.blocks < kT / kBlk) p.blocks = kT / kBlk;
   return p;
 }
 
@@ -720,6 +727,7 @@ hipError_t launch_attn_split(const AttnPlan& plan, const AttnLaunch& p, hipStrea
   const WsLayout l = ws_layout(plan, p.ws);
   a.po = l.po; a.pm = l.pm; a.pl = l.pl;
   a.S = p.S; a.Smax = p.Smax; a.n_split = plan.n_split; a.kps = plan.keys_per_split;
+  a.n_cache_split = plan.n_cache_split;
   a.q_norm = p.q_norm; a.tail_norm = p.tail_norm;
   hipError_t e;
   switch (plan.blocks) {

@@ -27,10 +27,11 @@ hipError_t launch_tail_copy(const uint16_t* k, const uint16_t* v, uint16_t* Kc, 
 
 // Split-KV attention plan for one (S, Smax).
 struct AttnPlan {
-  int n_keys;      // S + 64 visible keys per kv head
-  int n_split;     // key splits per kv head
-  int keys_per_split;
-  int blocks;      // 32-key blocks per split (kernel variant)
+  int n_keys;        // S + 64 visible keys per kv head
+  int n_split;       // key splits per kv head: n_cache_split over [0, S), then one over the own tokens
+  int n_cache_split;
+  int keys_per_split;  // of the cache splits (the last one may be shorter)
+  int blocks;        // 32-key blocks per split (kernel variant), at least the own split's 2
 };
 
 AttnPlan attn_plan(int S, int Smax);
