@@ -82,7 +82,12 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Chunk swizzles (16-byte chunk index within a 256-byte row).
-__device__ __forceinline__ int kswz(int r) { return r & 15; }
+// Query rows are read by consecutive lanes from consecutive rows: all 4 row bits.
+__device__ __forceinline__ int qswz(int r) { return r & 15; }
+// K rows are read by 8-lane groups from rows {0..3, 8..11} + 4j (the MFMA row order pi below):
+// bits 0, 1 and 3 of the row make those 8 rows hit 8 distinct 16-byte bank groups. The
+// swizzle stays below 8, so chunks c and c + 8 keep their 128-byte distance.
+__device__ __forceinline__ int kswz(int r) { return (r & 3) | ((r >> 1) & 4); }
 // V rows: the swizzle only depends on row & 3, so all transpose reads of a lane share two
 // base addresses (t even / odd) plus immediate offsets, and still spread a 16-lane group
 // over 8 distinct chunks.
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
     static_for<4>([&](auto pc) {
       constexpr int p = decltype(pc)::value;
       const int row = 32 * p + 4 * wave + (lane >> 4);
-      const uint16_t* src = qh + row * kD + 8 * ((lane & 15) ^ kswz(row));
+      const uint16_t* src = qh + row * kD + 8 * ((lane & 15) ^ qswz(row));
       __builtin_amdgcn_global_load_lds(src, (lds_void*)(qlds + (32 * p + 4 * wave) * 256), 16, 0, 0);
     });
   }
@@ -335,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int r = 32 * p + r16;
-      qv[p] = *reinterpret_cast<const u32x4*>(qlds + r * 256 + 16 * (j16 ^ kswz(r)));
+      qv[p] = *reinterpret_cast<const u32x4*>(qlds + r * 256 + 16 * (j16 ^ qswz(r)));
     }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -347,7 +352,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int r = 32 * p + r16;
-      *reinterpret_cast<u32x4*>(qlds + r * 256 + 16 * (j16 ^ kswz(r))) = qv[p];
+      *reinterpret_cast<u32x4*>(qlds + r * 256 + 16 * (j16 ^ qswz(r))) = qv[p];
     }
   }
   // 3. own-token rows of this split: K normed + roped (or taken roped) into kown and the cache
@@ -388,7 +393,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
   bf16x8 qf[8];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk)
-    qf[kk] = *reinterpret_cast<const bf16x8*>(qlds + qrow * 256 + 16 * ((dcol(kk, h) >> 3) ^ kswz(qrow)));
+    qf[kk] = *reinterpret_cast<const bf16x8*>(qlds + qrow * 256 + 16 * ((dcol(kk, h) >> 3) ^ qswz(qrow)));
   arrive(&cnt[kCntQRead], lane);  // this wave no longer reads qlds
 
   f32x16 o[4];
@@ -399,6 +404,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
   float m_run = -INFINITY, l_run = 0.f;  // running max in log2 units of the scaled score, row sum
   const float sc = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
   const int krow = perm_key(n);
+  // Per-lane LDS offsets, fixed for the loop: a block only adds its tile's (constant) base.
+  // K fragment kk is chunk dcol(kk, h) / 8 = 4h + (kk & 3) + 8 (kk >> 2) of row krow; the
+  // swizzle leaves the + 8, so koff[kk & 3] + 128 (kk >> 2).
+  int koff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) koff[j] = krow * 256 + 16 * ((4 * h + j) ^ kswz(krow));
+  // V^T operands: lane group G = lane >> 4, li = lane & 15 reads row 16c + 8(G>>1) + 4 hf +
+  // li/4 at chunk 4t + 2(G&1) + ((li&3)>>1) (columns 32t + 16(G&1) + 4(li&3) .. +3); the
+  // swizzle depends only on row & 3 = (li/4) & 3, so t = 0, 1 have their own offsets and
+  // t = 2, 3 add 8 chunks. The transpose read hands lane li of the group column
+  // 32t + 16(G&1) + li of 4 consecutive rows.
+  const int G = lane >> 4, li = lane & 15;
+  const int vrow0 = 8 * (G >> 1) + (li >> 2);
+  const int vx = 2 * (G & 1) + ((li & 3) >> 1);
+  const int voff[2] = {vrow0 * 256 + 16 * (vx ^ vswz(vrow0)) + 8 * (li & 1),
+                       vrow0 * 256 + 16 * ((4 + vx) ^ vswz(vrow0)) + 8 * (li & 1)};
 
   // Blocks of this wave's parity. A block past the split end (only in a short split) is
   // skipped, but still awaited and counted as consumed, so that a consumed tile is never
@@ -414,12 +435,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
       // S^T = K Q^T: K fragments from LDS (own-token rows from kown), then 8 MFMAs.
       f32x16 s;
       {
-        const int kvk = kb + krow;
-        const uint8_t* krow_base = (own_tail && kvk >= a.S) ? kown + (kvk - a.S) * 256 : tile + krow * 256;
         bf16x8 kf[8];
+        if (!own_tail || kb + kBlk <= a.S) {  // no own-token row in the block
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-          kf[kk] = *reinterpret_cast<const bf16x8*>(krow_base + 16 * ((dcol(kk, h) >> 3) ^ kswz(krow)));
+          for (int kk = 0; kk < 8; ++kk)
+            kf[kk] = *reinterpret_cast<const bf16x8*>(tile + koff[kk & 3] + 128 * (kk >> 2));
+        } else {
+          // own-token row tok stands in kown at row tok, swizzled like tile row krow
+          const int kvk = kb + krow;
+          const bool own = kvk >= a.S;
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) {
+            const int off = koff[kk & 3] + 128 * (kk >> 2);
+            kf[kk] = *reinterpret_cast<const bf16x8*>(own ? kown + (kvk - a.S) * 256 + (off - krow * 256) : tile + off);
+          }
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
@@ -462,12 +492,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
         psum += s[i];
       }
       l_run += psum;
-      // O^T += V^T P^T, in two halves of 16 keys. V^T operands: lane group G = lane >> 4,
-      // i = lane & 15 points at row 16c + 8(G>>1) + 4*half + i/4, columns 32t + 16(G&1) +
-      // 4(i&3) .. +3; the transpose read hands lane i of the group column 32t + 16(G&1) + i of
-      // 4 consecutive rows.
+      // O^T += V^T P^T, in two halves of 16 keys (operand layout at voff above).
       const uint8_t* tv = tile + kTileBytes / 2;
-      const int G = lane >> 4, li = lane & 15;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         bf16x8 pb;
@@ -477,12 +503,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            const int row = 16 * c + 8 * (G >> 1) + 4 * hf + (li >> 2);
-            const int chunk = 4 * t + 2 * (G & 1) + ((li & 3) >> 1);
+          for (int hf = 0; hf < 2; ++hf)
             vt[t][hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_v4i16*)(tv + row * 256 + 16 * (chunk ^ vswz(row)) + 8 * (li & 1)));
-          }
+                (lds_v4i16*)(tv + (16 * c + 4 * hf) * 256 + 128 * (t >> 1) + voff[t & 1]));
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const v4i16 both[2] = {vt[t][0], vt[t][1]};
