@@ -93,6 +93,14 @@ __device__ __forceinline__ int kswz(int r) { return (r & 3) | ((r >> 1) & 4); }
 // over 8 distinct chunks.
 __device__ __forceinline__ int vswz(int r) { return 2 * (r & 3); }
 
+// A lane's value and that of lane ^ 32, in either order: v_permlane32_swap exchanges the upper
+// half of one operand with the lower half of the other, so fed the same value twice, each of
+// its two results holds one of the pair in every lane. A VALU exchange, unlike ds_bpermute.
+__device__ __forceinline__ float2 pair32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return float2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
 // Row order inside a 32-key block seen by the MFMA: swap bits 2 and 3.
 __device__ __forceinline__ int perm_key(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
@@ -454,6 +462,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
         for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+        // Keep four K reads in flight ahead of the dependent MFMA chain: 4 reads, then
+        // (MFMA, read) x 4, then the last 4 MFMAs. Left to itself the scheduler waits for
+        // each read right before its MFMA, which exposes the LDS latency eight times.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
       if (kb + kBlk > k_end) {  // only a split's last block can be partial
         // accumulator element i of lane half h is key perm_key(8(i>>2) + 4h + (i&3)) = 8h + kofs(i)
@@ -467,7 +485,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
       float bmax = s[0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) bmax = fmaxf(bmax, s[i]);
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+      {
+        const float2 pr = pair32(bmax);
+        bmax = fmaxf(pr.x, pr.y);
+      }
       // The exponent reference m_run only moves when some row's max exceeds it by more than
       // kRescale (log2 units): p stays below 2^kRescale, exact for the final normalisation,
       // and the O rescale (64 multiplies) runs only on such jumps.
@@ -518,7 +539,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
     arrive(&cnt[kCntDone + b], lane);
   });
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float2 l_pair = pair32(l_run);
+  const float l_tot = l_pair.x + l_pair.y;
   // Merge of the two parities. The odd wave's O goes to a 16 KB region that nobody reads any
   // more: the tile of block qgrp once its four readers are done with it, or for qgrp >= NB a
   // half of the query buffer once every compute wave holds its query fragments. Layout is
