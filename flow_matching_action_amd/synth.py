@@ -13,6 +13,14 @@ RMSNorm gammas as 1 + 0.1 * N(0, 1). Cache rows [S, Smax-64) (rows the mask
 hides; the pages' tests fill them with 7.0) are then overwritten with 7.0,
 exactly representable in bf16 (0x40E0). Rows [Smax-64, Smax) keep their random
 draws: they are scratch that the tail write replaces.
+
+fp8 caches (e4m3 codes + one float32 scale per (kv head, row)): the cache
+values are N(0, 1) draws before quantisation. Each row gets a random
+power-of-two scale 2^-e, e uniform in {4, 5, 6}, and its codes are torch's
+nearest-even cast of x * 2^e (clipped to +-448) to float8_e4m3fn, so that
+code * scale ~ x. These are input recipes, not the per-row max rule that the
+layer applies to its own rows: this module holds no quantiser of the method.
+Hidden rows hold the code of 7.0 with scale 1.
 """
 from __future__ import annotations
 
@@ -26,6 +34,7 @@ N_KV_HEADS = 8
 N_TOK = 64
 HEAD_DIM = 128
 BF16_SEVEN = 0x40E0
+E4M3_SEVEN = 0x4E   # 1.75 * 2^2
 
 
 @dataclass(frozen=True)
@@ -82,6 +91,52 @@ def workload_inputs(w: LayerWorkload) -> dict:
     return layer_inputs(w.Smax, w.S, w.seed, w.rope_delta, w.filler)
 
 
+def f32_to_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """float32 array -> e4m3 codes (uint8): torch's CPU cast to float8_e4m3fn after clipping to +-448."""
+    t = torch.from_numpy(np.clip(np.ascontiguousarray(x, dtype=np.float32), -448.0, 448.0))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
+def layer_inputs_fp8(Smax: int, S: int, seed: int, rope_delta: int = 0, filler: float | None = 7.0,
+                     n_kv: int = N_KV_HEADS, n_q: int = N_Q_HEADS, n_tok: int = N_TOK,
+                     d: int = HEAD_DIM) -> dict:
+    """Inputs of one layer with an fp8 cache: Kc8, Vc8 [n_kv,Smax,d] uint8 e4m3 codes, Ks, Vs
+    [n_kv,Smax] float32 scales; q, k, v, gq, gk as bf16 bits (as ``layer_inputs``).
+
+    Draw order: K cache values, V cache values, q, own k, own v, the two gammas, then the
+    scale exponents of the K rows and of the V rows.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+
+    def draw(*shape):
+        return rng.standard_normal(shape, dtype=np.float32)
+
+    Kx = draw(n_kv, Smax, d)
+    Vx = draw(n_kv, Smax, d)
+    q = f32_to_bf16_bits(draw(n_q, n_tok, d))
+    k = f32_to_bf16_bits(draw(n_kv, n_tok, d))
+    v = f32_to_bf16_bits(draw(n_kv, n_tok, d))
+    gq = f32_to_bf16_bits(1.0 + 0.1 * draw(d))
+    gk = f32_to_bf16_bits(1.0 + 0.1 * draw(d))
+    ek = rng.integers(4, 7, size=(n_kv, Smax))
+    ev = rng.integers(4, 7, size=(n_kv, Smax))
+    Kc8 = f32_to_e4m3_codes(Kx * np.exp2(ek).astype(np.float32)[..., None])
+    Vc8 = f32_to_e4m3_codes(Vx * np.exp2(ev).astype(np.float32)[..., None])
+    Ks = np.exp2(-ek).astype(np.float32)
+    Vs = np.exp2(-ev).astype(np.float32)
+    if filler is not None and Smax - n_tok > S:
+        fc = f32_to_e4m3_codes(np.array([filler], np.float32))[0]
+        for c8, sc in ((Kc8, Ks), (Vc8, Vs)):
+            c8[:, S:Smax - n_tok, :] = fc
+            sc[:, S:Smax - n_tok] = 1.0
+    return {"Kc8": Kc8, "Ks": Ks, "Vc8": Vc8, "Vs": Vs, "q": q, "k": k, "v": v, "gq": gq, "gk": gk,
+            "S": S, "Smax": Smax, "rope_delta": rope_delta}
+
+
+def workload_inputs_fp8(w: LayerWorkload) -> dict:
+    return layer_inputs_fp8(w.Smax, w.S, w.seed, w.rope_delta, w.filler)
+
+
 # ---- the 64-layer x 10-step sequence, generated on the device ------------------------------------
 # 64 distinct caches (2.1 GB at Smax 8192, far beyond the 256 MB Infinity Cache), fresh q / own k / own v
 # for every (step, layer). Seeds: cache l -> 4000 + l, q/k/v of (step s, layer l) -> 5000 + 64 s + l,
@@ -99,6 +154,21 @@ def device_cache(Smax: int, S: int, layer: int, device, filler: float = 7.0):
     if Smax - N_TOK > S:
         kv[:, :, S:Smax - N_TOK, :] = filler
     return kv[0], kv[1]
+
+
+def device_cache_fp8(Smax: int, S: int, layer: int, device, filler: float = 7.0):
+    """fp8 K and V cache of one layer on the device: codes (uint8 [8, Smax, 128]) and scales
+    (float32 [8, Smax]) of each, by the recipe of ``layer_inputs_fp8`` (seed 8000 + layer)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(8000 + layer)
+    x = torch.randn((2, N_KV_HEADS, Smax, HEAD_DIM), generator=g, device=device, dtype=torch.float32)
+    e = torch.randint(4, 7, (2, N_KV_HEADS, Smax), generator=g, device=device).to(torch.float32)
+    codes = (x * torch.exp2(e)[..., None]).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    scales = torch.exp2(-e)
+    if Smax - N_TOK > S:
+        codes[:, :, S:Smax - N_TOK, :] = E4M3_SEVEN
+        scales[:, :, S:Smax - N_TOK] = 1.0
+    return codes[0], scales[0], codes[1], scales[1]
 
 
 def device_qkv(step: int, layer: int, device):

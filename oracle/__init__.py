@@ -10,16 +10,18 @@ Everything is written from the pages' description of the method (page
 in NumPy float64, with no blocking, fusion or reordering beyond the plain
 definition. Its bf16 and e4m3 codecs are its own.
 """
-from .codecs import bf16_bits_to_f64, f64_to_bf16_bits
+from .codecs import E4M3_MAX, bf16_bits_to_f64, e4m3_bits_to_f64, f64_to_bf16_bits, f64_to_e4m3_bits
 from .expert_attn import (
     HEAD_DIM, N_KV_HEADS, N_Q_HEADS, N_TOK, EPS, ROPE_THETA, MASK_MIN,
     rms_norm, rope_tables, rotate_half, apply_rope, build_mask, place_tail,
     attention, attention_partial, lse_combine, expert_attn_layer,
+    quantize_rows_e4m3, dequantize_rows_e4m3, expert_attn_layer_fp8,
 )
 
 __all__ = [
-    "bf16_bits_to_f64", "f64_to_bf16_bits",
+    "bf16_bits_to_f64", "f64_to_bf16_bits", "e4m3_bits_to_f64", "f64_to_e4m3_bits", "E4M3_MAX",
     "HEAD_DIM", "N_KV_HEADS", "N_Q_HEADS", "N_TOK", "EPS", "ROPE_THETA", "MASK_MIN",
     "rms_norm", "rope_tables", "rotate_half", "apply_rope", "build_mask", "place_tail",
     "attention", "attention_partial", "lse_combine", "expert_attn_layer",
+    "quantize_rows_e4m3", "dequantize_rows_e4m3", "expert_attn_layer_fp8",
 ]

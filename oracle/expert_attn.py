@@ -39,7 +39,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .codecs import bf16_bits_to_f64, f64_to_bf16_bits
+from .codecs import E4M3_MAX, bf16_bits_to_f64, e4m3_bits_to_f64, f64_to_bf16_bits, f64_to_e4m3_bits
 
 # Model constants of the action expert (page code/alpamayo_tt/EXPERT_NOTES.md,
 # table "Layouts": q/k/v heads [1,16,64,128] and [1,8,64,128]; cos/sin at theta
@@ -223,3 +223,82 @@ def expert_attn_layer(q_in, k_in, v_in, gamma_q, gamma_k, Kc, Vc, S: int, Smax: 
     out = attention(q_roped, bf16_bits_to_f64(Kc_new), bf16_bits_to_f64(Vc_new), mask, d ** -0.5)
     return {"out": out, "q_roped": q_roped, "k_roped": k_roped, "k_tail_bits": k_tail_bits,
             "v_tail_bits": v_tail_bits, "Kc_new": Kc_new, "Vc_new": Vc_new}
+
+
+# ---- fp8 cache variant ---------------------------------------------------------------------------
+# The pages offer an 8-bit cache (bfp8, a block floating-point format: page code/alpamayo_tt/expert.py,
+# TTExpert.__init__, the kv_cache dtype map; page code/alpamayo_tt/EXPERT_NOTES.md, the decode row for
+# the bfp8 cache in the attention timing table). Here the cache rows are e4m3 codes with one float32
+# scale per (kv head, row): value = e4m3(code) * scale. The own rows that the layer writes into the
+# tail are quantised with the per-row rule below (the reading taken for the tail write of such a
+# cache: the cache stores the cache dtype, page code/alpamayo_tt/expert.py, TTExpert.layer, the
+# typecast before fill_cache).
+
+def quantize_rows_e4m3(x_f32) -> tuple[np.ndarray, np.ndarray]:
+    """Per-row e4m3 quantisation: (codes [..., D] uint8, scales [...] float32).
+
+    scale = max_j |x_j| / 448 (float32 division, nearest-even), or 1.0 for an
+    all-zero row; code_j = e4m3 rounding (nearest, ties to even, saturating) of
+    the float32 quotient x_j / scale. Both divisions are done in float32, the
+    precision in which the kernel takes the same decisions, so the codes are
+    defined bit for bit.
+    """
+    x = np.asarray(x_f32, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    y = (x / scale[..., None]).astype(np.float32)
+    return f64_to_e4m3_bits(y.astype(np.float64)), scale
+
+
+def dequantize_rows_e4m3(codes, scales) -> np.ndarray:
+    """value = e4m3(code) * scale in float64 (exact: a 4-bit by 24-bit significand product)."""
+    return e4m3_bits_to_f64(codes) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+def expert_attn_layer_fp8(q_in, k_in, v_in, gamma_q, gamma_k, Kc8, Ks, Vc8, Vs, S: int, Smax: int,
+                          rope_delta: int = 0, eps: float = EPS, theta: float = ROPE_THETA) -> dict:
+    """One layer's attention step over an e4m3 cache with per-row float32 scales.
+
+    As ``expert_attn_layer`` (page code/alpamayo_tt/expert.py, ``TTExpert.layer``), except for the
+    cache format: Kc8/Vc8 [Hkv, Smax, D] uint8 e4m3 codes, Ks/Vs [Hkv, Smax] float32 scales. The own
+    roped k (rounded to bf16, the activation format) and the own bf16 v are quantised row by row
+    with ``quantize_rows_e4m3`` into rows [Smax-64, Smax); attention then reads the dequantised
+    cache under the same 0/-1e9 mask.
+
+    Returns ``out`` [Hq, 64, D] float64, ``q_roped``, ``k_roped``, the tail codes and scales
+    (``k_tail_codes``, ``k_tail_scales``, ``v_tail_codes``, ``v_tail_scales``) and the updated
+    caches ``Kc8_new``, ``Ks_new``, ``Vc8_new``, ``Vs_new``.
+    """
+    q_in = np.asarray(q_in, dtype=np.uint16)
+    n_tok = q_in.shape[1]
+    d = q_in.shape[-1]
+    if Kc8.shape[1] != Smax or Vc8.shape[1] != Smax or Ks.shape[1] != Smax or Vs.shape[1] != Smax:
+        raise ValueError("cache length does not match Smax")
+    if S < 0 or S > Smax - n_tok:
+        raise ValueError(f"need 0 <= S <= Smax - {n_tok}")
+    q = bf16_bits_to_f64(q_in)
+    k = bf16_bits_to_f64(k_in)
+    gq = bf16_bits_to_f64(gamma_q)
+    gk = bf16_bits_to_f64(gamma_k)
+    cos, sin = rope_tables(S + rope_delta, n_tok, d, theta)
+    q_roped = apply_rope(rms_norm(q, gq, eps), cos, sin)
+    k_roped = apply_rope(rms_norm(k, gk, eps), cos, sin)
+    k_bf16 = bf16_bits_to_f64(f64_to_bf16_bits(k_roped)).astype(np.float32)
+    v_bf16 = bf16_bits_to_f64(v_in).astype(np.float32)
+    k_codes, k_scales = quantize_rows_e4m3(k_bf16)
+    v_codes, v_scales = quantize_rows_e4m3(v_bf16)
+    Kc8_new = place_tail(np.asarray(Kc8, dtype=np.uint8), k_codes, n_tok)
+    Vc8_new = place_tail(np.asarray(Vc8, dtype=np.uint8), v_codes, n_tok)
+    Ks_new = np.array(Ks, dtype=np.float32, copy=True)
+    Vs_new = np.array(Vs, dtype=np.float32, copy=True)
+    Ks_new[:, Smax - n_tok:] = k_scales
+    Vs_new[:, Smax - n_tok:] = v_scales
+    rep = q.shape[0] // Kc8.shape[0]
+    mask = build_mask(S, Smax, rep * n_tok, n_tok)
+    K = dequantize_rows_e4m3(Kc8_new, Ks_new)
+    V = dequantize_rows_e4m3(Vc8_new, Vs_new)
+    out = attention(q_roped, K, V, mask, d ** -0.5)
+    return {"out": out, "q_roped": q_roped, "k_roped": k_roped,
+            "k_tail_codes": k_codes, "k_tail_scales": k_scales,
+            "v_tail_codes": v_codes, "v_tail_scales": v_scales,
+            "Kc8_new": Kc8_new, "Ks_new": Ks_new, "Vc8_new": Vc8_new, "Vs_new": Vs_new}
