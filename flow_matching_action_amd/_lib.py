@@ -67,12 +67,29 @@ lib.ax_expert_layer_attn_split.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_
                                            ctypes.c_size_t, _P]
 lib.ax_expert_attn_combine.restype = _I
 lib.ax_expert_attn_combine.argtypes = [_P, ctypes.c_size_t, _I, _I, _P, _P]
+lib.ax_expert_attn_fp8_workspace_bytes.restype = ctypes.c_size_t
+lib.ax_expert_attn_fp8_workspace_bytes.argtypes = [_I, _I]
+lib.ax_cache_tail_write_fp8.restype = _I
+lib.ax_cache_tail_write_fp8.argtypes = [_P, _P, _P, _P, _P, _P, _I, _P]
+lib.ax_expert_attn_fp8.restype = _I
+lib.ax_expert_attn_fp8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, ctypes.c_size_t, _P]
+lib.ax_expert_layer_attn_fp8.restype = _I
+lib.ax_expert_layer_attn_fp8.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, _I, _I, _P,
+                                         _P, ctypes.c_size_t, _P]
+lib.ax_expert_layer_attn_fp8_split.restype = _I
+lib.ax_expert_layer_attn_fp8_split.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, _I,
+                                               _I, _P, ctypes.c_size_t, _P]
+lib.ax_expert_attn_fp8_combine.restype = _I
+lib.ax_expert_attn_fp8_combine.argtypes = [_P, ctypes.c_size_t, _I, _I, _P, _P]
 lib.ax_copy_words.restype = _I
 lib.ax_copy_words.argtypes = [_P, _P, ctypes.c_size_t, _P]
 
 EXPORTS = ("ax_abi_version", "ax_strerror", "ax_rope_tables", "ax_qk_norm_rope", "ax_cache_tail_write",
            "ax_qk_norm_rope_tail", "ax_expert_attn_workspace_bytes", "ax_expert_attn",
-           "ax_expert_layer_attn", "ax_expert_layer_attn_split", "ax_expert_attn_combine", "ax_copy_words")
+           "ax_expert_layer_attn", "ax_expert_layer_attn_split", "ax_expert_attn_combine",
+           "ax_expert_attn_fp8_workspace_bytes", "ax_cache_tail_write_fp8", "ax_expert_attn_fp8",
+           "ax_expert_layer_attn_fp8", "ax_expert_layer_attn_fp8_split", "ax_expert_attn_fp8_combine",
+           "ax_copy_words")
 
 
 def _check(fn: str, code: int) -> None:
@@ -162,6 +179,46 @@ def expert_attn_combine(ws, S: int, Smax: int, out, stream=None):
     _check("ax_expert_attn_combine", lib.ax_expert_attn_combine(
         _ptr(ws), ws.numel() * ws.element_size() if ws is not None else 0, int(S), int(Smax), _ptr(out),
         _stream(stream)))
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size() if t is not None else 0
+
+
+def expert_attn_fp8_workspace_bytes(S: int, Smax: int) -> int:
+    return int(lib.ax_expert_attn_fp8_workspace_bytes(int(S), int(Smax)))
+
+
+def cache_tail_write_fp8(k_roped, v, Kc8, Ks, Vc8, Vs, Smax: int, stream=None):
+    _check("ax_cache_tail_write_fp8", lib.ax_cache_tail_write_fp8(
+        _ptr(k_roped), _ptr(v), _ptr(Kc8), _ptr(Ks), _ptr(Vc8), _ptr(Vs), int(Smax), _stream(stream)))
+
+
+def expert_attn_fp8(q_roped, k_own, v_own, Kc8, Ks, Vc8, Vs, S: int, Smax: int, out, ws, stream=None):
+    _check("ax_expert_attn_fp8", lib.ax_expert_attn_fp8(
+        _ptr(q_roped), _ptr(k_own), _ptr(v_own), _ptr(Kc8), _ptr(Ks), _ptr(Vc8), _ptr(Vs), int(S), int(Smax),
+        _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def expert_layer_attn_fp8(q_in, k_in, v_in, gamma_q, gamma_k, rope_cos, rope_sin, eps, Kc8, Ks, Vc8, Vs, S: int,
+                          Smax: int, out, ws, stream=None):
+    _check("ax_expert_layer_attn_fp8", lib.ax_expert_layer_attn_fp8(
+        _ptr(q_in), _ptr(k_in), _ptr(v_in), _ptr(gamma_q), _ptr(gamma_k), _ptr(rope_cos), _ptr(rope_sin),
+        float(eps), _ptr(Kc8), _ptr(Ks), _ptr(Vc8), _ptr(Vs), int(S), int(Smax), _ptr(out), _ptr(ws), _nbytes(ws),
+        _stream(stream)))
+
+
+def expert_layer_attn_fp8_split(q_in, k_in, v_in, gamma_q, gamma_k, rope_cos, rope_sin, eps, Kc8, Ks, Vc8, Vs,
+                                S: int, Smax: int, ws, stream=None):
+    _check("ax_expert_layer_attn_fp8_split", lib.ax_expert_layer_attn_fp8_split(
+        _ptr(q_in), _ptr(k_in), _ptr(v_in), _ptr(gamma_q), _ptr(gamma_k), _ptr(rope_cos), _ptr(rope_sin),
+        float(eps), _ptr(Kc8), _ptr(Ks), _ptr(Vc8), _ptr(Vs), int(S), int(Smax), _ptr(ws), _nbytes(ws),
+        _stream(stream)))
+
+
+def expert_attn_fp8_combine(ws, S: int, Smax: int, out, stream=None):
+    _check("ax_expert_attn_fp8_combine", lib.ax_expert_attn_fp8_combine(
+        _ptr(ws), _nbytes(ws), int(S), int(Smax), _ptr(out), _stream(stream)))
 
 
 def copy_words(src, dst, n_words16: int, stream=None):

@@ -179,6 +179,92 @@ int ax_expert_attn_combine(const void* ws, size_t ws_bytes, int S, int Smax, uin
   return status(ax::launch_attn_combine(ax::attn_plan(S, Smax), ws, out, as_stream(stream)));
 }
 
+// ---- fp8 cache ------------------------------------------------------------------------------
+
+size_t ax_expert_attn_fp8_workspace_bytes(int S, int Smax) {
+  if (check_shape(S, Smax) != AX_OK) return 0;
+  return ax::attn_partials_bytes(ax::attn_plan_f8(S, Smax));
+}
+
+static int check_ws_f8(const void* ws, size_t ws_bytes, int S, int Smax) {
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return AX_E_WORKSPACE;
+  return ws_bytes >= ax_expert_attn_fp8_workspace_bytes(S, Smax) ? AX_OK : AX_E_WORKSPACE;
+}
+
+int ax_cache_tail_write_fp8(const uint16_t* k_roped, const uint16_t* v, uint8_t* Kc8, float* Ks, uint8_t* Vc8,
+                            float* Vs, int Smax, void* stream) {
+  int r = check_ptrs({k_roped, v, Kc8, Ks, Vc8, Vs});
+  if (r == AX_OK) r = check_shape(0, Smax);
+  if (r == AX_OK) r = check_device();
+  if (r != AX_OK) return r;
+  return status(ax::launch_tail_quant_f8(k_roped, v, Kc8, Ks, Vc8, Vs, Smax, as_stream(stream)));
+}
+
+int ax_expert_attn_fp8(const uint16_t* q_roped, const uint16_t* k_own, const uint16_t* v_own, uint8_t* Kc8,
+                       float* Ks, uint8_t* Vc8, float* Vs, int S, int Smax, uint16_t* out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  int r = check_ptrs({q_roped, Kc8, Ks, Vc8, Vs, out, ws});
+  if (r == AX_OK && ((k_own == nullptr) != (v_own == nullptr))) r = AX_E_NULL;
+  if (r == AX_OK && k_own && (!aligned16(k_own) || !aligned16(v_own))) r = AX_E_ALIGN;
+  if (r == AX_OK) r = check_shape(S, Smax);
+  if (r == AX_OK) r = check_ws_f8(ws, ws_bytes, S, Smax);
+  if (r == AX_OK) r = check_device();
+  if (r != AX_OK) return r;
+  const ax::AttnPlan plan = ax::attn_plan_f8(S, Smax);
+  ax::AttnLaunchF8 p{q_roped, nullptr, nullptr, nullptr, nullptr, 0.f, k_own, v_own, Kc8, Ks, Vc8, Vs, out, ws,
+                     S, Smax, /*q_norm=*/0};
+  return status(ax::launch_attn_f8(plan, p, as_stream(stream)));
+}
+
+static int check_layer_f8(const uint16_t* q_in, const uint16_t* k_in, const uint16_t* v_in, const uint16_t* gamma_q,
+                          const uint16_t* gamma_k, const float* rope_cos, const float* rope_sin, float eps,
+                          uint8_t* Kc8, float* Ks, uint8_t* Vc8, float* Vs, int S, int Smax, void* ws,
+                          size_t ws_bytes) {
+  int r = check_ptrs({q_in, k_in, v_in, gamma_q, gamma_k, rope_cos, rope_sin, Kc8, Ks, Vc8, Vs, ws});
+  if (r == AX_OK) r = check_shape(S, Smax);
+  if (r == AX_OK) r = check_eps(eps);
+  if (r == AX_OK) r = check_ws_f8(ws, ws_bytes, S, Smax);
+  if (r == AX_OK) r = check_device();
+  return r;
+}
+
+int ax_expert_layer_attn_fp8(const uint16_t* q_in, const uint16_t* k_in, const uint16_t* v_in,
+                             const uint16_t* gamma_q, const uint16_t* gamma_k, const float* rope_cos,
+                             const float* rope_sin, float eps, uint8_t* Kc8, float* Ks, uint8_t* Vc8, float* Vs,
+                             int S, int Smax, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  int r = out == nullptr ? AX_E_NULL : aligned16(out) ? AX_OK : AX_E_ALIGN;
+  if (r == AX_OK)
+    r = check_layer_f8(q_in, k_in, v_in, gamma_q, gamma_k, rope_cos, rope_sin, eps, Kc8, Ks, Vc8, Vs, S, Smax, ws,
+                       ws_bytes);
+  if (r != AX_OK) return r;
+  const ax::AttnPlan plan = ax::attn_plan_f8(S, Smax);
+  ax::AttnLaunchF8 p{q_in, gamma_q, gamma_k, rope_cos, rope_sin, eps, k_in, v_in, Kc8, Ks, Vc8, Vs, out, ws,
+                     S, Smax, /*q_norm=*/1};
+  return status(ax::launch_attn_f8(plan, p, as_stream(stream)));
+}
+
+int ax_expert_layer_attn_fp8_split(const uint16_t* q_in, const uint16_t* k_in, const uint16_t* v_in,
+                                   const uint16_t* gamma_q, const uint16_t* gamma_k, const float* rope_cos,
+                                   const float* rope_sin, float eps, uint8_t* Kc8, float* Ks, uint8_t* Vc8,
+                                   float* Vs, int S, int Smax, void* ws, size_t ws_bytes, void* stream) {
+  const int r = check_layer_f8(q_in, k_in, v_in, gamma_q, gamma_k, rope_cos, rope_sin, eps, Kc8, Ks, Vc8, Vs, S,
+                               Smax, ws, ws_bytes);
+  if (r != AX_OK) return r;
+  const ax::AttnPlan plan = ax::attn_plan_f8(S, Smax);
+  ax::AttnLaunchF8 p{q_in, gamma_q, gamma_k, rope_cos, rope_sin, eps, k_in, v_in, Kc8, Ks, Vc8, Vs, nullptr, ws,
+                     S, Smax, /*q_norm=*/1};
+  return status(ax::launch_attn_f8_split(plan, p, as_stream(stream)));
+}
+
+int ax_expert_attn_fp8_combine(const void* ws, size_t ws_bytes, int S, int Smax, uint16_t* out, void* stream) {
+  int r = check_ptrs({ws, out});
+  if (r == AX_OK) r = check_shape(S, Smax);
+  if (r == AX_OK) r = check_ws_f8(ws, ws_bytes, S, Smax);
+  if (r == AX_OK) r = check_device();
+  if (r != AX_OK) return r;
+  return status(ax::launch_attn_combine(ax::attn_plan_f8(S, Smax), ws, out, as_stream(stream)));
+}
+
 int ax_copy_words(const void* src, void* dst, size_t n_words16, void* stream) {
   int r = check_ptrs({src, dst});
   if (r == AX_OK) r = check_device();

@@ -1,0 +1,239 @@
+// Device-side pieces shared by the split-KV attention kernels (bf16 and fp8 caches):
+// launch shape, the LDS hand-off counters, the MFMA operand layouts, and the query
+// norm/RoPE helpers. The kernels themselves are in ax_attn.hip and ax_attn_f8.hip.
+#pragma once
+#include "ax_dev.h"
+
+namespace ax {
+
+constexpr int kBlk = 32;                      // keys per block
+constexpr int kQBytes = kQRows * kD * 2;      // 32 KB: the 128 query rows in bf16
+constexpr int kComputeWaves = 8;
+constexpr int kLoaderWaves = 4;
+constexpr int kThreads = 64 * (kComputeWaves + kLoaderWaves);
+constexpr int kMaxBlocks = 12;                // blocks per split in any kernel variant
+// LDS hand-off counters: queries normed, query fragments read, block b landed, block b
+// consumed, merge data of query group q ready
+constexpr int kCntQNormed = 0, kCntQRead = 1, kCntBlock = 2;
+constexpr int kCntDone = kCntBlock + kMaxBlocks, kCntMerge = kCntDone + kMaxBlocks, kNCnt = kCntMerge + 4;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescale = 8.0f;              // lazy-rescale threshold (log2 units)
+constexpr int kNonTemporal = 2;               // cache-policy operand of a load: nt
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Chunk swizzles (16-byte chunk index within a row: 16 chunks in a bf16 row, 8 in an fp8 row).
+// Query rows are read by consecutive lanes from consecutive rows: all 4 row bits.
+__device__ __forceinline__ int qswz(int r) { return r & 15; }
+// K rows are read by 8-lane groups from rows {0..3, 8..11} + 4j (the MFMA row order pi below):
+// bits 0, 1 and 3 of the row make those 8 rows hit 8 distinct 16-byte bank groups. The
+// swizzle stays below 8, so chunks c and c + 8 keep their 128-byte distance.
+__device__ __forceinline__ int kswz(int r) { return (r & 3) | ((r >> 1) & 4); }
+// A lane's value and that of lane ^ 32, in either order: v_permlane32_swap exchanges the upper
+// half of one operand with the lower half of the other, so fed the same value twice, each of
+// its two results holds one of the pair in every lane. A VALU exchange, unlike ds_bpermute.
+__device__ __forceinline__ float2 pair32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return float2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
+// Row order inside a 32-key block seen by the MFMA: swap bits 2 and 3.
+__device__ __forceinline__ int perm_key(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+// Head-dim chunk (8 columns) used by k-step kk in lane half h: half h holds columns
+// [32h, 32h+32) and [64+32h, 96+32h), so a RoPE pair (j, j+64) stays in one lane.
+__device__ __forceinline__ int dcol(int kk, int h) { return (kk < 4) ? 32 * h + 8 * kk : 64 + 32 * h + 8 * (kk - 4); }
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt bits [3:0]
+// and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
+
+// Workgroup barrier for LDS hand-offs: this wave's LDS writes are complete (lgkmcnt), then
+// s_barrier; the memory clobber keeps the compiler from moving memory accesses across it.
+// Unlike __syncthreads() there is no release fence, which would also drain this wave's
+// direct-to-LDS loads of later blocks (callers wait for exactly the loads they need).
+// The scheduling fences keep the compiler from hoisting arithmetic (and the waits for its
+// operands) above the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// In-workgroup hand-off counters in LDS. A producer wave bumps a counter once its data is
+// in LDS; consumers poll it. Unlike s_barrier this never makes a producer wait for its
+// consumers, so the cache stream runs ahead of the arithmetic as far as the LDS tiles
+// allow (tiles are never reused within a launch, so there is nothing to wait for).
+// The increment is written as inline asm: the compiler cannot tell an LDS atomic from the
+// direct-to-LDS loads still in flight and would drain them all (vmcnt(0)) before it.
+typedef __attribute__((address_space(3))) int lds_int;
+__device__ __forceinline__ void arrive(int* cnt, int lane) {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's own LDS writes come first
+  if (lane == 0) {
+    const unsigned off = (unsigned)(uintptr_t)(lds_int*)cnt;
+    asm volatile("ds_add_u32 %0, %1" ::"v"(off), "v"(1) : "memory");
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The wait is bounded (about 30 ms at 2.4 GHz, thousands of times any real wait) so that a
+// wave always exits even if a count were wrong; the results would then be wrong, not hung.
+constexpr int kSpinLimit = 1 << 20;
+__device__ __forceinline__ void await(int* cnt, int n) {
+  __builtin_amdgcn_sched_barrier(0);
+  for (int spin = 0; spin < kSpinLimit; ++spin) {
+    if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >= n)
+      break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// RoPE table values of token tok for the 8 frequencies 8 (j16 & 7) .. +7: lanes j16 < 8 load
+// the cosines, lanes j16 >= 8 the sines, and the partner lane (j16 ^ 8, same frequencies)
+// hands over the other half, so each table byte is requested once per row group.
+__device__ __forceinline__ void load_cos_sin_half(const float* cos_t, const float* sin_t, int tok, int j16,
+                                                  f32x4& h0, f32x4& h1) {
+  const float* src = ((j16 < 8) ? cos_t : sin_t) + tok * 64 + 8 * (j16 & 7);
+  h0 = reinterpret_cast<const f32x4*>(src)[0];
+  h1 = reinterpret_cast<const f32x4*>(src)[1];
+}
+
+__device__ __forceinline__ void split_cos_sin(const f32x4& h0, const f32x4& h1, int j16, float* c, float* s) {
+  const bool lo = j16 < 8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float mine = (e < 4) ? h0[e & 3] : h1[e & 3];
+    const float other = row_ror<8>(mine);
+    c[e] = lo ? mine : other;
+    s[e] = lo ? other : mine;
+  }
+}
+
+__device__ __forceinline__ void unpack8v(const u32x4& v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(v[i] << 16);
+    f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ u32x4 pack8v(const float* f) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+  return r;
+}
+
+
+// RMSNorm + RoPE in place in LDS of the query rows 32p + r16 (p = 0..3) that this lane's
+// 16-lane group holds (columns 8 j16 .. +7), rows swizzled by qswz. graw: the 8 gammas of the
+// lane; qc/qs: cos/sin of token sets p & 1. All rows are read before any is written back.
+__device__ __forceinline__ void norm_rope_query_rows(uint8_t* qlds, const u32x4& graw, const float (&qc)[2][8],
+                                                     const float (&qs)[2][8], int j16, int r16, float eps) {
+  float qg[8], A[2][8], B[2][8];
+  unpack8v(graw, qg);
+#pragma unroll
+  for (int p = 0; p < 2; ++p) rope_coef(qg, qc[p], qs[p], j16, A[p], B[p]);
+  u32x4 qv[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = 32 * p + r16;
+    qv[p] = *reinterpret_cast<const u32x4*>(qlds + r * 256 + 16 * (j16 ^ qswz(r)));
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    float x[8];
+    unpack8v(qv[p], x);
+    norm_rope_row16(x, A[p & 1], B[p & 1], eps);
+    qv[p] = pack8v(x);
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = 32 * p + r16;
+    *reinterpret_cast<u32x4*>(qlds + r * 256 + 16 * (j16 ^ qswz(r))) = qv[p];
+  }
+}
+
+
+// End of a split: the two parity waves of query group qgrp hold (m, l, O) over disjoint
+// blocks. The odd wave hands its O (16 KB: slot j = 4t + jj of the accumulator layout, 1 KB
+// per slot, slots 0..7 at xlo and 8..15 at xhi) and (m, l) to the even one through LDS, once
+// region_free() says nobody reads those regions any more; the even wave rescales both to
+// the larger m and stores the split's partial (float32, non-temporal: the combine reads it
+// once). With a single block (two_parities false) the odd wave holds nothing.
+// Partial layout: O at po + ((part * 4 + qgrp) * 16 + j) * 64 + lane (float4 units), m and l
+// at pm / pl + part * 128 + query row.
+template <typename RegionFree>
+__device__ __forceinline__ void merge_and_store_partial(const f32x16 (&o)[4], float m_run, float l_run,
+                                                        bool two_parities, int par, int qgrp, int lane,
+                                                        uint8_t* xlo, uint8_t* xhi, RegionFree&& region_free,
+                                                        float (*mlx)[2][32], int* cnt, float* po_all,
+                                                        float* pm, float* pl, long long part) {
+  const int n = lane & 31;
+  const int h = lane >> 5;
+  const int qrow = 32 * qgrp + n;
+  const float2 l_pair = pair32(l_run);
+  const float l_tot = l_pair.x + l_pair.y;
+  f32x4* po = reinterpret_cast<f32x4*>(po_all) + (part * 4 + qgrp) * (16 * 64) + lane;
+  if (!two_parities) {
+    if (par == 1) return;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        __builtin_nontemporal_store(f32x4{o[t][4 * jj], o[t][4 * jj + 1], o[t][4 * jj + 2], o[t][4 * jj + 3]},
+                                    &po[(4 * t + jj) * 64]);
+    if (h == 0) {
+      __builtin_nontemporal_store(m_run, &pm[part * kQRows + qrow]);
+      __builtin_nontemporal_store(l_tot, &pl[part * kQRows + qrow]);
+    }
+    return;
+  }
+  auto slot = [&](int j) { return reinterpret_cast<f32x4*>(j < 8 ? xlo + j * 1024 : xhi + (j - 8) * 1024) + lane; };
+  if (par == 1) {
+    region_free();
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *slot(4 * t + jj) = f32x4{o[t][4 * jj], o[t][4 * jj + 1], o[t][4 * jj + 2], o[t][4 * jj + 3]};
+    if (h == 0) {
+      mlx[qgrp][0][n] = m_run;
+      mlx[qgrp][1][n] = l_tot;
+    }
+    arrive(&cnt[kCntMerge + qgrp], lane);
+    return;
+  }
+  await(&cnt[kCntMerge + qgrp], 1);
+  const float m_o = mlx[qgrp][0][n];
+  const float l_o = mlx[qgrp][1][n];
+  const float m_new = fmaxf(m_run, m_o);  // m_run is finite: block 0 holds a visible key
+  const float ae = __builtin_amdgcn_exp2f(m_run - m_new);
+  const float ao = __builtin_amdgcn_exp2f(m_o - m_new);  // 0 if the odd wave saw no key
+  const float l_all = ae * l_tot + ao * l_o;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const f32x4 x = *slot(4 * t + jj);
+      f32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = ae * o[t][4 * jj + e] + ao * x[e];
+      __builtin_nontemporal_store(v, &po[(4 * t + jj) * 64]);
+    }
+  if (h == 0) {
+    __builtin_nontemporal_store(m_new, &pm[part * kQRows + qrow]);
+    __builtin_nontemporal_store(l_all, &pl[part * kQRows + qrow]);
+  }
+}
+
+}  // namespace ax

@@ -34,8 +34,18 @@ struct AttnPlan {
   int blocks;        // 32-key blocks per split (kernel variant), at least the own split's 2
 };
 
-AttnPlan attn_plan(int S, int Smax);
+AttnPlan attn_plan(int S, int Smax);     // bf16 cache
+AttnPlan attn_plan_f8(int S, int Smax);  // fp8 cache (longer splits: a block is half the bytes)
 size_t attn_partials_bytes(const AttnPlan& p);
+
+// Partial buffers inside the workspace: O [8][n_split][4][16][64] float4, then m and l
+// [8][n_split][128] float, each 256-byte aligned.
+struct WsLayout {
+  float* po;
+  float* pm;
+  float* pl;
+};
+WsLayout ws_layout(const AttnPlan& plan, const void* ws);
 
 struct AttnLaunch {
   const uint16_t* q;       // [16][64][128] (== folded [8][128][128]): raw if q_norm, else roped
@@ -53,6 +63,30 @@ struct AttnLaunch {
   int S, Smax;
   int q_norm, tail_norm;
 };
+
+// fp8 cache: e4m3 codes [8][Smax][128] with a float32 scale per (kv head, row) [8][Smax].
+struct AttnLaunchF8 {
+  const uint16_t* q;       // [16][64][128]: raw if q_norm, else roped
+  const uint16_t* gq;
+  const uint16_t* gk;
+  const float* cos_t;
+  const float* sin_t;
+  float eps;
+  const uint16_t* k_own;   // own k [8][64][128] (raw if q_norm, else roped), or null: tail already in the cache
+  const uint16_t* v_own;
+  uint8_t* Kc;
+  float* Ks;
+  uint8_t* Vc;
+  float* Vs;
+  uint16_t* out;
+  void* ws;
+  int S, Smax;
+  int q_norm;
+};
+hipError_t launch_attn_f8(const AttnPlan& plan, const AttnLaunchF8& p, hipStream_t st);        // both
+hipError_t launch_attn_f8_split(const AttnPlan& plan, const AttnLaunchF8& p, hipStream_t st);  // partials
+hipError_t launch_tail_quant_f8(const uint16_t* k, const uint16_t* v, uint8_t* Kc, float* Ks, uint8_t* Vc,
+                                float* Vs, int Smax, hipStream_t st);
 
 hipError_t launch_attn(const AttnPlan& plan, const AttnLaunch& p, hipStream_t st);        // both
 hipError_t launch_attn_split(const AttnPlan& plan, const AttnLaunch& p, hipStream_t st);  // partials

@@ -176,6 +176,66 @@ int ax_expert_attn_combine(const void* ws, size_t ws_bytes, int S, int Smax, uin
                            void* stream);
 
 /*
+ * fp8 KV cache. The pages offer an 8-bit cache for the same step (page
+ * code/alpamayo_tt/expert.py, TTExpert.__init__, the kv_cache dtype map;
+ * page code/alpamayo_tt/EXPERT_NOTES.md, the bfp8-cache row of the decode
+ * attention timing). Here a cache row is 128 OCP e4m3 codes ("fn": bias 7,
+ * no infinities, 0x7F/0xFF NaN, max 448) with one float32 scale:
+ *   Kc8, Vc8 [8][Smax][128] uint8 (128 bytes per row), Ks, Vs [8][Smax] float
+ *   value of element (g, j, d) = e4m3(Kc8[g][j][d]) * Ks[g][j]
+ * Own rows written into the tail are quantised per row:
+ *   scale = max_d |x_d| / 448 (1.0 for an all-zero row),
+ *   code_d = e4m3 nearest-even, saturating to +-448, of x_d / scale,
+ * both divisions in float32; x is the bf16 roped own k, or the bf16 own v.
+ * Pointers as for the bf16 cache (16-byte aligned device memory owned by the
+ * caller); the other conventions above apply unchanged.
+ */
+
+/* Workspace bytes of the fp8 calls for (S, Smax); 0 if invalid. */
+size_t ax_expert_attn_fp8_workspace_bytes(int S, int Smax);
+
+/*
+ * Tail write into an fp8 cache: rows (g, i) of k_roped and v [8][64][128]
+ * bf16 quantised by the rule above into Kc8/Ks and Vc8/Vs row Smax - 64 + i.
+ * Every other row and scale is left untouched.
+ */
+int ax_cache_tail_write_fp8(const uint16_t* k_roped, const uint16_t* v, uint8_t* Kc8, float* Ks,
+                            uint8_t* Vc8, float* Vs, int Smax, void* stream);
+
+/*
+ * ax_expert_attn over an fp8 cache: if k_own/v_own (roped k, v; bf16) are
+ * both non-NULL their quantised rows are written to the tail first, if both
+ * are NULL the tail is taken as already written. Scores and the value sum use
+ * the dequantised rows: each e4m3 code is converted exactly to bf16 for the
+ * matrix cores, the key scales multiply the float32 scores and the value
+ * scales the float32 softmax weights before they are rounded to bf16.
+ * ws: at least ax_expert_attn_fp8_workspace_bytes(S, Smax) bytes, 256-byte
+ * aligned.
+ */
+int ax_expert_attn_fp8(const uint16_t* q_roped, const uint16_t* k_own, const uint16_t* v_own,
+                       uint8_t* Kc8, float* Ks, uint8_t* Vc8, float* Vs, int S, int Smax,
+                       uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The whole attention step of one layer over an fp8 cache (ax_expert_layer_attn
+ * with the tail quantised): q/k RMSNorm + RoPE, the own rows quantised into the
+ * tail (k after rounding the roped k to bf16), attention, combine; two launches.
+ * The _split / _combine pair are those two launches, as for the bf16 cache.
+ */
+int ax_expert_layer_attn_fp8(const uint16_t* q_in, const uint16_t* k_in, const uint16_t* v_in,
+                             const uint16_t* gamma_q, const uint16_t* gamma_k, const float* rope_cos,
+                             const float* rope_sin, float eps, uint8_t* Kc8, float* Ks, uint8_t* Vc8,
+                             float* Vs, int S, int Smax, uint16_t* out, void* ws, size_t ws_bytes,
+                             void* stream);
+int ax_expert_layer_attn_fp8_split(const uint16_t* q_in, const uint16_t* k_in, const uint16_t* v_in,
+                                   const uint16_t* gamma_q, const uint16_t* gamma_k,
+                                   const float* rope_cos, const float* rope_sin, float eps,
+                                   uint8_t* Kc8, float* Ks, uint8_t* Vc8, float* Vs, int S, int Smax,
+                                   void* ws, size_t ws_bytes, void* stream);
+int ax_expert_attn_fp8_combine(const void* ws, size_t ws_bytes, int S, int Smax, uint16_t* out,
+                               void* stream);
+
+/*
  * Measurement helper: dst[i] = src[i] for n 16-byte words, one plain
  * streaming copy kernel. Used to calibrate hardware byte counters against a
  * transfer of known size. Pointers 16-byte aligned.

@@ -131,3 +131,45 @@ def test_no_device_is_reported_not_launched():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present: the valid call would launch")
     assert _layer() == ax.AX_E_UNSUPPORTED
+
+
+def test_fp8_workspace_bytes():
+    assert ax.expert_attn_fp8_workspace_bytes(128, 256) > 0
+    assert ax.expert_attn_fp8_workspace_bytes(8128, 8192) > 0
+    assert ax.expert_attn_fp8_workspace_bytes(193, 256) == 0
+    assert ax.expert_attn_fp8_workspace_bytes(0, 63) == 0
+    # fp8 splits hold up to 384 keys (bf16: 192): never more partials than the bf16 plan
+    for S, Smax in ((4700, 8192), (8128, 8192), (65472, 65536)):
+        assert ax.expert_attn_fp8_workspace_bytes(S, Smax) <= ax.expert_attn_workspace_bytes(S, Smax)
+
+
+def test_fp8_validation_codes():
+    lf = ax.lib.ax_expert_layer_attn_fp8
+
+    def layer(q=FAKE, Kc=FAKE, Ks=FAKE, Vs=FAKE, S=128, Smax=256, eps=1e-6, out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+        return lf(q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, eps, Kc, Ks, FAKE, Vs, S, Smax, out, ws, ws_bytes, None)
+
+    assert layer(q=None) == ax.AX_E_NULL
+    assert layer(Ks=None) == ax.AX_E_NULL
+    assert layer(out=None) == ax.AX_E_NULL
+    assert layer(Vs=MIS) == ax.AX_E_ALIGN
+    assert layer(out=MIS) == ax.AX_E_ALIGN
+    assert layer(S=193) == ax.AX_E_SHAPE
+    assert layer(eps=float("nan")) == ax.AX_E_ARG
+    assert layer(ws_bytes=16) == ax.AX_E_WORKSPACE
+    assert layer(ws=FAKE + 16) == ax.AX_E_WORKSPACE
+    sp = ax.lib.ax_expert_layer_attn_fp8_split
+    assert sp(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6, FAKE, None, FAKE, FAKE, 128, 256, FAKE, 1 << 30,
+              None) == ax.AX_E_NULL
+    assert sp(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-6, FAKE, FAKE, FAKE, FAKE, 128, 256, FAKE, 16,
+              None) == ax.AX_E_WORKSPACE
+    at = ax.lib.ax_expert_attn_fp8
+    assert at(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 128, 256, FAKE, FAKE, 1 << 30, None) == ax.AX_E_NULL
+    assert at(FAKE, MIS, MIS, FAKE, FAKE, FAKE, FAKE, 128, 256, FAKE, FAKE, 1 << 30, None) == ax.AX_E_ALIGN
+    assert at(FAKE, None, None, FAKE, FAKE, FAKE, FAKE, 300, 256, FAKE, FAKE, 1 << 30, None) == ax.AX_E_SHAPE
+    tw = ax.lib.ax_cache_tail_write_fp8
+    assert tw(FAKE, FAKE, FAKE, None, FAKE, FAKE, 256, None) == ax.AX_E_NULL
+    assert tw(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 63, None) == ax.AX_E_SHAPE
+    cb = ax.lib.ax_expert_attn_fp8_combine
+    assert cb(FAKE, 8, 128, 256, FAKE, None) == ax.AX_E_WORKSPACE
+    assert cb(FAKE, 1 << 30, 128, 256, None, None) == ax.AX_E_NULL
