@@ -13,7 +13,11 @@ write + split attention launch: a second graph of the same K steps, with that la
 alone, is timed the same way, and its algorithmic bytes (the step's, less the output
 that the combine writes) are divided by its average launch time.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+The fp8-cache variant (e4m3 codes + float32 row scales) is measured the same way on its own
+workload, Smax = 8192, S = 8128 (the full cache), over 64 rotating fp8 caches (1.1 GB), and
+reported under "fp8" in the same line.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-fp8]
        python bench.py --calibrate-copy BYTES   (a plain copy of known size, for counter runs)
 Prints one JSON line.
 """
@@ -51,6 +55,20 @@ OUT_BYTES = 16 * 64 * 128 * 2
 
 def algorithmic_flops(S: int) -> int:
     return 2 * 2 * 8 * 128 * (S + 64) * 128   # QK^T and PV, 128 folded rows per kv head
+
+
+S_FP8 = 8128
+
+
+def algorithmic_bytes_fp8(S: int, Smax: int) -> int:
+    """As algorithmic_bytes for an e4m3 cache: 128 code bytes per visible row (K and V) plus its float32
+    scale, the tail write of codes and scales; q, own k/v and the output stay bf16."""
+    visible = 2 * 8 * (S + 64) * (128 + 4)
+    q_in = 16 * 64 * 256
+    kv_in = 2 * 8 * 64 * 256
+    tail = 2 * 8 * 64 * (128 + 4)
+    out = 16 * 64 * 256
+    return visible + q_in + kv_in + tail + out
 
 
 class RotatingWorkload:
@@ -108,6 +126,45 @@ def kernel_source_hash() -> str:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
+
+
+class RotatingWorkloadF8:
+    """64 fp8 layer caches (synth.device_cache_fp8) at Smax=8192, S=8128, sharing the q/k/v sets and gammas of
+    the bf16 workload."""
+
+    def __init__(self, ax, torch, wl: RotatingWorkload, Smax: int = SMAX, S: int = S_FP8):
+        from flow_matching_action_amd import synth
+        dev = "cuda:0"
+        self.ax, self.wl, self.Smax, self.S = ax, wl, Smax, S
+        self.Kc, self.Ks, self.Vc, self.Vs = [], [], [], []
+        for l in range(wl.n_layers):
+            kc, ks, vc, vs = synth.device_cache_fp8(Smax, S, l, dev)
+            for lst, t in ((self.Kc, kc), (self.Ks, ks), (self.Vc, vc), (self.Vs, vs)):
+                lst.append(t.contiguous())
+        cos, sin = ax.rope_tables(S + ROPE_DELTA)
+        self.cos = torch.from_numpy(cos).to(dev)
+        self.sin = torch.from_numpy(sin).to(dev)
+        self.out = [torch.empty((16, 64, 128), dtype=torch.bfloat16, device=dev) for _ in range(wl.n_layers)]
+        self.ws = torch.zeros(ax.expert_attn_fp8_workspace_bytes(S, Smax), dtype=torch.uint8, device=dev)
+        for t in self.Kc + self.Vc:
+            assert t.shape == (8, Smax, 128) and t.dtype == torch.uint8 and t.is_contiguous()
+        for t in self.Ks + self.Vs:
+            assert t.shape == (8, Smax) and t.dtype == torch.float32 and t.is_contiguous()
+        torch.cuda.synchronize()
+
+    def _args(self, i):
+        wl = self.wl
+        l, j = i % wl.n_layers, i % wl.n_sets
+        return (wl.q[j], wl.k[j], wl.v[j], wl.gq[l], wl.gk[l], self.cos, self.sin, EPS,
+                self.Kc[l], self.Ks[l], self.Vc[l], self.Vs[l], self.S, self.Smax), l
+
+    def step(self, i: int, stream=None):
+        a, l = self._args(i)
+        self.ax.expert_layer_attn_fp8(*a, self.out[l], self.ws, stream=stream)
+
+    def step_attention_only(self, i: int, stream=None):
+        a, _ = self._args(i)
+        self.ax.expert_layer_attn_fp8_split(*a, self.ws, stream=stream)
 
 
 def load_traffic():
@@ -198,6 +255,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=N_LAYERS * N_EULER)
     ap.add_argument("--replays", type=int, default=5, help="timed replays of the K-step graph (median reported)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache workload")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run the plain copy kernel on BYTES (for rocprofv3 --pmc calibration)")
     args = ap.parse_args()
@@ -268,6 +326,40 @@ def main() -> int:
         "replays_ms": [round(t, 4) for t in times_ms],
         "outputs_finite": out_ok,
     }
+    if not args.no_fp8:
+        wl8 = RotatingWorkloadF8(ax, torch, wl)
+        with torch.cuda.stream(stream):
+            for i in range(W):
+                wl8.step(i, stream)
+        torch.cuda.synchronize()
+        t8 = timed_graph(torch, stream, wl8.step, W, K, args.replays)
+        us8 = statistics.median(t8) * 1e3 / K
+        a8 = timed_graph(torch, stream, wl8.step_attention_only, W, K, args.replays)
+        us8_attn = statistics.median(a8) * 1e3 / K
+        b8 = algorithmic_bytes_fp8(S_FP8, SMAX)
+        b8_attn = b8 - OUT_BYTES
+        f8 = algorithmic_flops(S_FP8)
+        ok8 = all(bool(torch.isfinite(o.float()).all()) for o in wl8.out)
+        out_ok = out_ok and ok8
+        result["outputs_finite"] = out_ok
+        result["fp8"] = {
+            "workload": "expert attention layer step, fp8 e4m3 cache with float32 row scales, Smax=8192 S=8128, "
+                        "64 rotating layer caches (1.1 GB, cold), fresh q/k/v per (Euler step, layer), "
+                        "hipGraph of K steps",
+            "value": round(us8, 3), "unit": "us/layer",
+            "achieved_hbm_gbs": round(b8 / (us8 * 1e-6) / 1e9, 1),
+            "roofline": {"bound": "hbm", "achieved": round(b8_attn / (us8_attn * 1e-6) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(b8_attn / (us8_attn * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "k_attn_f8 (q/k norm + RoPE + quantised tail write + split attention)",
+                         "kernel_us_per_launch": round(us8_attn, 3),
+                         "algorithmic_bytes_per_launch": b8_attn,
+                         "algorithmic_flops_per_launch": f8,
+                         "matrix_tflops": round(f8 / (us8_attn * 1e-6) / 1e12, 1),
+                         "matrix_peak_tflops_bf16": 2500.0},
+            "replays_ms": [round(t, 4) for t in t8],
+            "outputs_finite": ok8,
+        }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)
