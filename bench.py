@@ -119,15 +119,6 @@ class RotatingWorkload:
                                         EPS, self.K[l], self.V[l], self.S, self.Smax, self.ws, stream=stream)
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "flow_matching_action_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
-    return h.hexdigest()[:16]
-
-
 class RotatingWorkloadF8:
     """64 fp8 layer caches (synth.device_cache_fp8) at Smax=8192, S=8128, sharing the q/k/v sets and gammas of
     the bf16 workload."""
@@ -167,10 +158,31 @@ class RotatingWorkloadF8:
         self.ax.expert_layer_attn_fp8_split(*a, self.ws, stream=stream)
 
 
-def load_traffic():
+# Sources that define each measured kernel: a committed counter summary is used only while they are
+# unchanged since the counters were taken.
+KERNEL_SOURCES = {
+    "bf16": ("ax_attn.hip", "ax_attn_common.h", "ax_dev.h"),
+    "fp8": ("ax_attn_f8.hip", "ax_attn_common.h", "ax_dev.h"),
+}
+TRAFFIC_FILES = {
+    "bf16": "traffic_expert_layer_attn_smax8192_s4700.txt",
+    "fp8": "traffic_expert_layer_attn_fp8_smax8192_s8128.txt",
+}
+
+
+def kernel_source_hash(which: str = "bf16") -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "flow_matching_action_amd", "csrc")
+    for name in KERNEL_SOURCES[which]:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(which: str = "bf16"):
     """HBM bytes per launch of the dominant kernel from the committed counter summary, if the summary
     was taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", "traffic_expert_layer_attn_smax8192_s4700.txt")
+    path = os.path.join(ROOT, "profiles", TRAFFIC_FILES[which])
     if not os.path.exists(path):
         return None
     vals = {}
@@ -179,7 +191,7 @@ def load_traffic():
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_hash") != kernel_source_hash():
+    if vals.get("kernel_source_hash") != kernel_source_hash(which):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -350,7 +362,8 @@ def main() -> int:
             "achieved_hbm_gbs": round(b8 / (us8 * 1e-6) / 1e9, 1),
             "roofline": {"bound": "hbm", "achieved": round(b8_attn / (us8_attn * 1e-6) / 1e9, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(b8_attn / (us8_attn * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                         "frac": round(b8_attn / (us8_attn * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "traffic": load_traffic("fp8"),
                          "kernel": "k_attn_f8 (q/k norm + RoPE + quantised tail write + split attention)",
                          "kernel_us_per_launch": round(us8_attn, 3),
                          "algorithmic_bytes_per_launch": b8_attn,
