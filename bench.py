@@ -27,6 +27,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -170,12 +171,19 @@ TRAFFIC_FILES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank lines: edits to comments do not change a kernel."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash(which: str = "bf16") -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "flow_matching_action_amd", "csrc")
     for name in KERNEL_SOURCES[which]:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name)) as f:
+            h.update(name.encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -15,24 +15,24 @@
 // give the same softmax).
 //
 // gfx950 mapping
-// - One workgroup of 16 waves per (kv head, key split); workgroup id w -> head w % 8,
-//   which the dispatcher places on XCD w % 8, so a head's splits share one L2.
-// - Keys go in blocks of 32 visible keys (visible key v < S is cache row v; v >= S is
-//   own token v - S). Every wave issues one 1 KB direct-to-LDS load per block
-//   (global_load_lds, 16 bytes per lane) - waves 0..7 the K rows, 8..15 the V rows -
-//   for all blocks of the split before anything waits, so a CU keeps its whole share
-//   of the cache in flight from 16 waves. Each block has its own LDS tile; rows are
-//   256 bytes with the 16-byte chunks XOR-swizzled by row.
-// - The 128 query rows are normed and roped by all 1024 threads (16 lanes per row,
-//   the same arithmetic as the stand-alone norm/RoPE kernel) into LDS; the rows of
-//   own tokens are normed/roped in LDS by the block that holds them, which also
-//   writes them to the cache tail.
-// - Waves 0..3 compute, wave w owning query rows 32w..32w+31: S^T = K Q^T on
-//   v_mfma_f32_32x32x16_bf16 (A = K rows, B = Q^T), so each lane holds one query
-//   row's scores; O^T = V^T P^T with V^T read straight from row-major V by
-//   ds_read_tr16_b64 and P^T taken from the S^T accumulator. Inside a block MFMA row
-//   m reads key pi(m) (bits 2 and 3 swapped), which makes the 8 keys a lane supplies
-//   to one PV step consecutive.
+// - One workgroup of 12 waves per (kv head, key split); workgroup id w -> head w % 8,
+//   which the dispatcher places on XCD w % 8, so a head's splits share one L2. The cache
+//   keys [0, S) are cut into splits of at most 6 blocks of 32 keys; the 64 own tokens
+//   form one more split of their own.
+// - Waves 8..11 (loaders) stream the split's K/V rows into per-block LDS tiles with
+//   direct-to-LDS loads (global_load_lds, 16 bytes per lane), a few blocks ahead, and
+//   count each landed block in LDS; rows are 256 bytes with the 16-byte chunks
+//   XOR-swizzled by row.
+// - Waves 0..7 (compute) fetch and norm/rope the 128 query rows in place in LDS (16
+//   lanes per row, the same arithmetic as the stand-alone norm/RoPE kernel); in the own
+//   split they also norm/rope the own k rows and write the cache tail. Then wave w takes
+//   query rows 32 (w & 3) .. +31 over the blocks of parity w >> 2: S^T = K Q^T on
+//   v_mfma_f32_32x32x16_bf16 (A = K rows, B = Q^T), so each lane holds one query row's
+//   scores; O^T = V^T P^T with V^T read straight from row-major V by ds_read_tr16_b64
+//   and P^T taken from the S^T accumulator. Inside a block MFMA row m reads key pi(m)
+//   (bits 2 and 3 swapped), which makes the 8 keys a lane supplies to one PV step
+//   consecutive. The two parity waves of a query group merge through LDS and the even
+//   one stores the split's partial.
 #include "ax_attn_common.h"
 #include "ax_launch.h"
 
