@@ -235,3 +235,19 @@ def test_throughput_sequence_matches_oracle(ax, step, layer):
     assert np.array_equal(bits(Vc)[:, Smax - 64:], inp["v"])
     assert np.array_equal(bits(Vc)[:, :Smax - 64], inp["Vc"][:, :Smax - 64])
     assert np.array_equal(bits(Kc)[:, :Smax - 64], inp["Kc"][:, :Smax - 64])
+
+
+def test_workspace_reuse_across_shapes(ax):
+    # One workspace serves calls of different (S, Smax) in any order: nothing a call leaves in
+    # it changes a later call's result.
+    shapes = [(4700, 8192, 61), (128, 256, 62), (8128, 8192, 63), (4700, 8192, 64), (0, 64, 65)]
+    nbytes = max(ax.expert_attn_workspace_bytes(S, Smax) for S, Smax, _ in shapes)
+    ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device=DEV)   # garbage on entry is allowed
+    for S, Smax, seed in shapes:
+        inp = synth.layer_inputs(Smax, S, seed=seed)
+        say(f"shared workspace, S={S} Smax={Smax}")
+        shared = Layer(inp, ax)
+        shared.ws = ws
+        got = shared.run(ax)
+        fresh = Layer(inp, ax).run(ax)
+        assert np.array_equal(got, fresh), (S, Smax)
