@@ -171,6 +171,36 @@ def device_cache_fp8(Smax: int, S: int, layer: int, device, filler: float = 7.0)
     return codes[0], scales[0], codes[1], scales[1]
 
 
+def decode_inputs(Smax: int, pos: int, seed: int, rope_delta: int = 0, n_kv: int = N_KV_HEADS,
+                  n_q: int = 64, d: int = HEAD_DIM) -> dict:
+    """Inputs of one text-model decode step as bf16 bits: Kc, Vc [n_kv,Smax,d], q [n_q,d] (64 query
+    heads of the one new token), k, v [n_kv,d], gq, gk [d]. Draw order: K cache, V cache, q, k, v, the
+    two gammas (1 + 0.1 N(0,1)). Rows [pos, Smax) of the caches hold 7.0: row pos is replaced by the
+    step's own k/v, the rows after it are not yet written."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+
+    def draw(*shape):
+        return rng.standard_normal(shape, dtype=np.float32)
+
+    Kc = f32_to_bf16_bits(draw(n_kv, Smax, d))
+    Vc = f32_to_bf16_bits(draw(n_kv, Smax, d))
+    q = f32_to_bf16_bits(draw(n_q, d))
+    k = f32_to_bf16_bits(draw(n_kv, d))
+    v = f32_to_bf16_bits(draw(n_kv, d))
+    gq = f32_to_bf16_bits(1.0 + 0.1 * draw(d))
+    gk = f32_to_bf16_bits(1.0 + 0.1 * draw(d))
+    Kc[:, pos:] = BF16_SEVEN
+    Vc[:, pos:] = BF16_SEVEN
+    return {"Kc": Kc, "Vc": Vc, "q": q, "k": k, "v": v, "gq": gq, "gk": gk, "pos": pos, "Smax": Smax,
+            "rope_delta": rope_delta}
+
+
+def device_decode_qkv(step: int, layer: int, device):
+    """q [64,128], k and v [8,128] (bf16 tensors) of one text-model decode step (seed 9000 + 64 step + layer)."""
+    t = _dev_normal_bf16((64 + 2 * N_KV_HEADS, HEAD_DIM), 9000 + 64 * step + layer, device)
+    return t[:64], t[64:64 + N_KV_HEADS], t[64 + N_KV_HEADS:]
+
+
 def device_qkv(step: int, layer: int, device):
     """q [16,64,128], own k and v [8,64,128] (bf16 tensors) of one (step, layer)."""
     t = _dev_normal_bf16((N_Q_HEADS + 2 * N_KV_HEADS, N_TOK, HEAD_DIM), 5000 + 64 * step + layer, device)
