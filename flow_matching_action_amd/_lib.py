@@ -81,6 +81,11 @@ lib.ax_expert_layer_attn_fp8_split.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctype
                                                _I, _P, ctypes.c_size_t, _P]
 lib.ax_expert_attn_fp8_combine.restype = _I
 lib.ax_expert_attn_fp8_combine.argtypes = [_P, ctypes.c_size_t, _I, _I, _P, _P]
+lib.ax_text_decode_workspace_bytes.restype = ctypes.c_size_t
+lib.ax_text_decode_workspace_bytes.argtypes = [_I, _I]
+lib.ax_text_decode_attn.restype = _I
+lib.ax_text_decode_attn.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _I, _I, _P, _P,
+                                    ctypes.c_size_t, _P]
 lib.ax_copy_words.restype = _I
 lib.ax_copy_words.argtypes = [_P, _P, ctypes.c_size_t, _P]
 
@@ -89,7 +94,7 @@ EXPORTS = ("ax_abi_version", "ax_strerror", "ax_rope_tables", "ax_qk_norm_rope",
            "ax_expert_layer_attn", "ax_expert_layer_attn_split", "ax_expert_attn_combine",
            "ax_expert_attn_fp8_workspace_bytes", "ax_cache_tail_write_fp8", "ax_expert_attn_fp8",
            "ax_expert_layer_attn_fp8", "ax_expert_layer_attn_fp8_split", "ax_expert_attn_fp8_combine",
-           "ax_copy_words")
+           "ax_text_decode_workspace_bytes", "ax_text_decode_attn", "ax_copy_words")
 
 
 def _check(fn: str, code: int) -> None:
@@ -219,6 +224,17 @@ def expert_layer_attn_fp8_split(q_in, k_in, v_in, gamma_q, gamma_k, rope_cos, ro
 def expert_attn_fp8_combine(ws, S: int, Smax: int, out, stream=None):
     _check("ax_expert_attn_fp8_combine", lib.ax_expert_attn_fp8_combine(
         _ptr(ws), _nbytes(ws), int(S), int(Smax), _ptr(out), _stream(stream)))
+
+
+def text_decode_workspace_bytes(pos: int, Smax: int) -> int:
+    return int(lib.ax_text_decode_workspace_bytes(int(pos), int(Smax)))
+
+
+def text_decode_attn(q_in, k_in, v_in, gamma_q, gamma_k, rope_cos, rope_sin, eps, Kc, Vc, pos: int, Smax: int, out,
+                     ws, stream=None):
+    _check("ax_text_decode_attn", lib.ax_text_decode_attn(
+        _ptr(q_in), _ptr(k_in), _ptr(v_in), _ptr(gamma_q), _ptr(gamma_k), _ptr(rope_cos), _ptr(rope_sin),
+        float(eps), _ptr(Kc), _ptr(Vc), int(pos), int(Smax), _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def copy_words(src, dst, n_words16: int, stream=None):

@@ -265,6 +265,28 @@ int ax_expert_attn_fp8_combine(const void* ws, size_t ws_bytes, int S, int Smax,
   return status(ax::launch_attn_combine(ax::attn_plan_f8(S, Smax), ws, out, as_stream(stream)));
 }
 
+// ---- text-model decode step -------------------------------------------------------------------
+
+size_t ax_text_decode_workspace_bytes(int pos, int Smax) {
+  if (Smax < 1 || Smax > AX_SMAX_LIMIT || pos < 0 || pos >= Smax) return 0;
+  return ax::decode_partials_bytes(ax::decode_plan(pos));
+}
+
+int ax_text_decode_attn(const uint16_t* q_in, const uint16_t* k_in, const uint16_t* v_in, const uint16_t* gamma_q,
+                        const uint16_t* gamma_k, const float* rope_cos, const float* rope_sin, float eps,
+                        uint16_t* Kc, uint16_t* Vc, int pos, int Smax, uint16_t* out, void* ws, size_t ws_bytes,
+                        void* stream) {
+  int r = check_ptrs({q_in, k_in, v_in, gamma_q, gamma_k, rope_cos, rope_sin, Kc, Vc, out, ws});
+  if (r == AX_OK && (Smax < 1 || Smax > AX_SMAX_LIMIT || pos < 0 || pos >= Smax)) r = AX_E_SHAPE;
+  if (r == AX_OK) r = check_eps(eps);
+  if (r == AX_OK && ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || ws_bytes < ax_text_decode_workspace_bytes(pos, Smax)))
+    r = AX_E_WORKSPACE;
+  if (r == AX_OK) r = check_device();
+  if (r != AX_OK) return r;
+  ax::DecodeLaunch p{q_in, k_in, v_in, gamma_q, gamma_k, rope_cos, rope_sin, eps, Kc, Vc, out, ws, pos, Smax};
+  return status(ax::launch_decode(ax::decode_plan(pos), p, as_stream(stream)));
+}
+
 int ax_copy_words(const void* src, void* dst, size_t n_words16, void* stream) {
   int r = check_ptrs({src, dst});
   if (r == AX_OK) r = check_device();

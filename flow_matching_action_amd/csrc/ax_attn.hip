@@ -66,11 +66,6 @@ struct FusedArgs {
   int q_norm, tail_norm;
 };
 
-// V rows: the swizzle only depends on row & 3, so all transpose reads of a lane share two
-// base addresses (t even / odd) plus immediate offsets, and still spread a 16-lane group
-// over 8 distinct chunks.
-__device__ __forceinline__ int vswz(int r) { return 2 * (r & 3); }
-
 // The LDS tiles are distinct objects so that the compiler's wait counting can tell the
 // direct-to-LDS loads of one block from another block and from the query buffer.
 #define AX_TILE(b) __shared__ __attribute__((aligned(16))) uint8_t t##b[kTileBytes]

@@ -31,6 +31,10 @@ __device__ __forceinline__ int qswz(int r) { return r & 15; }
 // bits 0, 1 and 3 of the row make those 8 rows hit 8 distinct 16-byte bank groups. The
 // swizzle stays below 8, so chunks c and c + 8 keep their 128-byte distance.
 __device__ __forceinline__ int kswz(int r) { return (r & 3) | ((r >> 1) & 4); }
+// V rows of a bf16 tile: the swizzle only depends on row & 3, so all transpose reads of a
+// lane share two base addresses (t even / odd) plus immediate offsets, and still spread a
+// 16-lane group over 8 distinct chunks.
+__device__ __forceinline__ int vswz(int r) { return 2 * (r & 3); }
 // A lane's value and that of lane ^ 32, in either order: v_permlane32_swap exchanges the upper
 // half of one operand with the lower half of the other, so fed the same value twice, each of
 // its two results holds one of the pair in every lane. A VALU exchange, unlike ds_bpermute.

@@ -1,0 +1,418 @@
+// Single-token decode attention of the text model: the attention part of one decode step of a
+// layer with 64 query heads and 8 kv heads of width 128.
+//
+// What is computed: page code/alpamayo_tt/text.py, TTTextModel._layer_decode - q and k of the
+// new token RMSNormed per head and roped at position pos + rope_delta, the roped k and the v
+// written into cache row pos (paged_update_cache), then every query head h attends to rows
+// [0, pos] of kv head h / 8 with scale 1/sqrt(128) (scaled_dot_product_attention_decode with
+// cur_pos = pos). The key range is split and the splits combined as in the expert step:
+//   m_c = max_j s_j, l_c = sum_j 2^(s_j - m_c), O_c = sum_j 2^(s_j - m_c) v_j,
+//   out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c,  s_j = log2(e) (q . k_j) / sqrt(128).
+//
+// gfx950 mapping
+// - One workgroup of 8 waves per (kv head, key split of at most 8 blocks of 32 keys); 32 splits
+//   per head when the keys allow, so 256 workgroups stream the cache once.
+// - Waves 4..7 (loaders) stream the split's blocks into their own LDS tiles (direct-to-LDS
+//   loads, rows 256 bytes, swizzled as in the expert kernel), a few blocks ahead, and count
+//   each landed block in LDS. Key pos comes from the new token's raw k / v instead of the
+//   cache; the compute wave that consumes its block norms and ropes that k row in the tile
+//   and writes both rows to cache row pos.
+// - Waves 0..3 (compute): wave 0 norms and ropes the 8 query rows of the kv head into LDS;
+//   wave w consumes blocks w, w + 4. The 8 rows are the first 8 of the 32 rows of the expert
+//   kernel's MFMA layout (S^T = K Q^T on v_mfma_f32_32x32x16_bf16, O^T = V^T P^T with V^T read
+//   by ds_read_tr16_b64); rows 8..31 are zero. The step is bound by the cache stream, which
+//   the unused rows do not touch.
+// - The compute waves merge their (m, l, O) through LDS; wave 0 stores the split's partial
+//   (8 rows). k_decode_combine then reduces the splits of each of the 64 output rows.
+#include "ax_attn_common.h"
+#include "ax_launch.h"
+
+namespace ax {
+
+constexpr int kDecQHeads = 64;
+constexpr int kDecRows = kDecQHeads / kHkv;   // 8 query rows (heads) per kv head
+constexpr int kDecCompute = 4;                // compute waves
+constexpr int kDecThreads = 64 * 2 * kDecCompute;  // + as many loader waves
+constexpr int kDecDepth = 3;                  // blocks in flight per loader wave
+// LDS hand-off counters: query rows normed, block b landed, merge data of the compute waves ready
+constexpr int kDcQ = 0, kDcBlock = 1, kDcMerge = kDcBlock + 8, kDcN = kDcMerge + 1;
+constexpr int kDecMaxNB = 8;                  // blocks per split (LDS: 8 x 16 KB)
+constexpr int kDecTile = 2 * kBlk * kD * 2;   // K 8 KB + V 8 KB
+
+struct DecArgs {
+  const uint16_t* q;      // [64][128] raw
+  const uint16_t* k;      // [8][128] raw
+  const uint16_t* v;      // [8][128]
+  const uint16_t* gq;
+  const uint16_t* gk;
+  const float* cos_t;     // [64]: cos of (pos + rope_delta) * theta^(-2j/128)
+  const float* sin_t;
+  float eps;
+  uint16_t* Kc;           // [8][Smax][128]
+  uint16_t* Vc;
+  float* po;              // [8][n_split][8 rows][128]
+  float* pm;              // [8][n_split][8]
+  float* pl;
+  int pos, Smax, n_split, kps;
+};
+
+template <int NB>
+__global__ __launch_bounds__(kDecThreads, 1) void k_decode_attn(DecArgs a) {
+  static_assert(NB >= 1 && NB <= kDecMaxNB, "blocks per split");
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[NB][kDecTile];
+  __shared__ __attribute__((aligned(16))) uint8_t qlds[kDecRows * 256];
+  // merge hand-off of compute waves 1..3: O of rows 0..7 (slot j, lane (row, half)), m and l
+  __shared__ f32x4 mo[kDecCompute - 1][16][16];
+  __shared__ float mml[kDecCompute - 1][2][kDecRows];
+  __shared__ int cnt[kDcN];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int j16 = lane & 15;
+  const int g = blockIdx.x % kHkv;
+  const int split = blockIdx.x / kHkv;
+  const int n_keys = a.pos + 1;
+  const int k_begin = split * a.kps;
+  const int k_end = min(k_begin + a.kps, n_keys);
+  const long long head_row = (long long)g * a.Smax;
+
+  if (tid < kDcN) cnt[tid] = 0;
+  lds_barrier();  // counters cleared (the only workgroup barrier)
+
+  if (wave >= kDecCompute) {
+    // ---------------- loader waves: rows 8w .. 8w+7 of each block, K then V (two 1 KB loads each)
+    const int w = wave - kDecCompute;
+    auto issue_block = [&](auto bc) {
+      constexpr int b = decltype(bc)::value;
+      uint8_t* tile = &tiles[b][0];
+      static_for<2>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int r = 8 * w + 4 * i + (lane >> 4);
+        int kk = k_begin + b * kBlk + r;
+        kk = kk < k_end ? kk : k_begin;  // rows past the split end reload a visible row (masked)
+        const bool is_new = kk == a.pos;
+        const uint16_t* ks = is_new ? a.k + (long long)g * kD : a.Kc + (head_row + kk) * kD;
+        const uint16_t* vs = is_new ? a.v + (long long)g * kD : a.Vc + (head_row + kk) * kD;
+        __builtin_amdgcn_global_load_lds(ks + 8 * ((lane & 15) ^ kswz(r)), (lds_void*)(tile + (8 * w + 4 * i) * 256),
+                                         16, 0, kNonTemporal);
+        __builtin_amdgcn_global_load_lds(vs + 8 * ((lane & 15) ^ vswz(r)),
+                                         (lds_void*)(tile + kDecTile / 2 + (8 * w + 4 * i) * 256), 16, 0, kNonTemporal);
+      });
+    };
+    constexpr int D = NB < kDecDepth ? NB : kDecDepth;
+    static_for<D>([&](auto bc) { issue_block(bc); });
+    static_for<NB>([&](auto bc) {
+      constexpr int b = decltype(bc)::value;
+      constexpr int later = (b + D - 1 < NB - 1 ? b + D - 1 : NB - 1) - b;
+      wait_vmcnt<4 * later>();  // four loads per block, in block order: block b has landed
+      arrive(&cnt[kDcBlock + b], lane);
+      if constexpr (b + D < NB) issue_block(std::integral_constant<int, b + D>{});
+    });
+    return;
+  }
+
+  // ---------------- compute waves
+  const u32x4 graw = *reinterpret_cast<const u32x4*>(a.gq + 8 * j16);
+  const u32x4 gkraw = *reinterpret_cast<const u32x4*>(a.gk + 8 * j16);
+  f32x4 cs_h[2];
+  load_cos_sin_half(a.cos_t, a.sin_t, 0, j16, cs_h[0], cs_h[1]);
+  if (wave == 0) {
+    // the 8 query rows of head g: rows 4i + (lane >> 4), i = 0, 1 (lane l lands at 16 l)
+    static_for<2>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const int row = 4 * i + (lane >> 4);
+      const uint16_t* src = a.q + (long long)(kDecRows * g + row) * kD + 8 * ((lane & 15) ^ qswz(row));
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(qlds + 4 * i * 256), 16, 0, 0);
+    });
+  }
+  float qc[8], qs[8], A[8], B[8];
+  split_cos_sin(cs_h[0], cs_h[1], j16, qc, qs);
+  wait_vmcnt<0>();
+  if (wave == 0) {
+    // norm + RoPE of the query rows in place, 16 lanes per row, 4 rows per pass
+    float qg[8];
+    unpack8v(graw, qg);
+    rope_coef(qg, qc, qs, j16, A, B);
+    u32x4 qv[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int r = 4 * p + (lane >> 4);
+      qv[p] = *reinterpret_cast<const u32x4*>(qlds + r * 256 + 16 * (j16 ^ qswz(r)));
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      float x[8];
+      unpack8v(qv[p], x);
+      norm_rope_row16(x, A, B, a.eps);
+      qv[p] = pack8v(x);
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int r = 4 * p + (lane >> 4);
+      *reinterpret_cast<u32x4*>(qlds + r * 256 + 16 * (j16 ^ qswz(r))) = qv[p];
+    }
+    arrive(&cnt[kDcQ], lane);
+  }
+  await(&cnt[kDcQ], 1);
+
+  const int n = lane & 31;
+  const int h = lane >> 5;
+  bf16x8 qf[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    if (n < kDecRows) {
+      qf[kk] = *reinterpret_cast<const bf16x8*>(qlds + n * 256 + 16 * ((dcol(kk, h) >> 3) ^ qswz(n)));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[kk][e] = (__bf16)0.f;
+    }
+  }
+
+  f32x16 o[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sc = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
+  const int krow = perm_key(n);
+  int koff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) koff[j] = krow * 256 + 16 * ((4 * h + j) ^ kswz(krow));
+  const int G = lane >> 4, li = lane & 15;
+  const int vrow0 = 8 * (G >> 1) + (li >> 2);
+  const int vx = 2 * (G & 1) + ((li & 3) >> 1);
+  const int voff[2] = {vrow0 * 256 + 16 * (vx ^ vswz(vrow0)) + 8 * (li & 1),
+                       vrow0 * 256 + 16 * ((4 + vx) ^ vswz(vrow0)) + 8 * (li & 1)};
+
+  static_for<NB>([&](auto bc) {
+    constexpr int b = decltype(bc)::value;
+    if (b % kDecCompute != wave) return;
+    const int kb = k_begin + b * kBlk;
+    await(&cnt[kDcBlock + b], kDecCompute);
+    if (kb >= k_end) return;
+    uint8_t* tile = &tiles[b][0];
+    // (a split's last block can reach past the split's end: key pos must be one of this split's)
+    if (a.pos >= kb && a.pos < min(kb + kBlk, k_end) && lane < 16) {
+      // the new token's k row: norm + RoPE in place, then both rows to cache row pos
+      const int r = a.pos - kb;
+      u32x4* kp = reinterpret_cast<u32x4*>(tile + r * 256 + 16 * (j16 ^ kswz(r)));
+      const u32x4 vraw = *reinterpret_cast<const u32x4*>(tile + kDecTile / 2 + r * 256 + 16 * (j16 ^ vswz(r)));
+      float gkv[8], x[8];
+      unpack8v(gkraw, gkv);
+      rope_coef(gkv, qc, qs, j16, A, B);
+      unpack8v(*kp, x);
+      norm_rope_row16(x, A, B, a.eps);
+      const u32x4 kr = pack8v(x);
+      *kp = kr;
+      const long long dst = (head_row + a.pos) * kD + 8 * j16;
+      *reinterpret_cast<u32x4*>(a.Kc + dst) = kr;
+      *reinterpret_cast<u32x4*>(a.Vc + dst) = vraw;
+    }
+    f32x16 s;
+    {
+      bf16x8 kf[8];
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(tile + koff[kk & 3] + 128 * (kk >> 2));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+    }
+    if (kb + kBlk > k_end) {
+      const int lim = k_end - kb - 8 * h;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kofs = 16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3);
+        s[i] = (kofs < lim) ? s[i] : -INFINITY;
+      }
+    }
+    float bmax = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) bmax = fmaxf(bmax, s[i]);
+    {
+      const float2 pr = pair32(bmax);
+      bmax = fmaxf(pr.x, pr.y);
+    }
+    const float m_blk = bmax * sc;
+    if constexpr (b < kDecCompute) {
+      m_run = m_blk;  // the wave's first block holds a visible key
+    } else if (__any(m_blk > m_run + kRescale)) {
+      const float m_new = fmaxf(m_run, m_blk);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sc, -m_run));
+      psum += s[i];
+    }
+    l_run += psum;
+    const uint8_t* tv = tile + kDecTile / 2;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[8 * c + e];
+      v4i16 vt[4][2];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          vt[t][hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16*)(tv + (16 * c + 4 * hf) * 256 + 128 * (t >> 1) + voff[t & 1]));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const v4i16 both[2] = {vt[t][0], vt[t][1]};
+        bf16x8 vf;
+        __builtin_memcpy(&vf, both, 16);
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[t], 0, 0, 0);
+      }
+    }
+  });
+
+  // merge of the compute waves (rows 0..7: lanes n < 8 of both halves), then the partial
+  const float2 l_pair = pair32(l_run);
+  const float l_tot = l_pair.x + l_pair.y;
+  const int ml = (lane & 7) + 8 * h;  // merge slot of lane (n, h), n < 8
+  if (wave > 0) {
+    if (n < kDecRows) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          mo[wave - 1][4 * t + jj][ml] = f32x4{o[t][4 * jj], o[t][4 * jj + 1], o[t][4 * jj + 2], o[t][4 * jj + 3]};
+      if (h == 0) {
+        mml[wave - 1][0][n] = m_run;
+        mml[wave - 1][1][n] = l_tot;
+      }
+    }
+    arrive(&cnt[kDcMerge], lane);
+    return;
+  }
+  await(&cnt[kDcMerge], kDecCompute - 1);
+  if (n >= kDecRows) return;
+  float m_all = m_run, l_all = l_tot;  // block 0 holds a visible key: m_run is finite
+#pragma unroll
+  for (int w = 0; w < kDecCompute - 1; ++w) {
+    const float m_o = mml[w][0][n];
+    const float l_o = mml[w][1][n];
+    const float m_new = fmaxf(m_all, m_o);
+    const float ae = __builtin_amdgcn_exp2f(m_all - m_new);
+    const float ao = __builtin_amdgcn_exp2f(m_o - m_new);  // 0 for a wave without blocks (m = -inf)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 x = mo[w][4 * t + jj][ml];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[t][4 * jj + e] = ae * o[t][4 * jj + e] + ao * x[e];
+      }
+    l_all = ae * l_all + ao * l_o;
+    m_all = m_new;
+  }
+  const long long prow = ((long long)g * a.n_split + split) * kDecRows + n;
+  // lane (n, h) holds columns 32 t + 8 jj + 4 h .. +3 of row n
+  f32x4* po = reinterpret_cast<f32x4*>(a.po + prow * kD);
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      po[(32 * t + 8 * jj + 4 * h) / 4] = f32x4{o[t][4 * jj], o[t][4 * jj + 1], o[t][4 * jj + 2], o[t][4 * jj + 3]};
+  if (h == 0) {
+    a.pm[prow] = m_all;
+    a.pl[prow] = l_all;
+  }
+}
+
+// Combine of the splits: workgroup (head g, row r) = output row 8 g + r (query head 8 g + r), one
+// column per thread; the loads of up to 8 splits are issued before any is used. Fixed order.
+__global__ __launch_bounds__(kD) void k_decode_combine(const float* po, const float* pm, const float* pl,
+                                                       uint16_t* out, int n_split) {
+  const int g = blockIdx.x / kDecRows;
+  const int r = blockIdx.x % kDecRows;
+  const int d = threadIdx.x;
+  const long long base = (long long)g * n_split * kDecRows + r;  // row of split c: base + c * 8
+  float M = -INFINITY;
+  for (int c = 0; c < n_split; ++c) M = fmaxf(M, pm[base + (long long)c * kDecRows]);
+  float L = 0.f, acc = 0.f;
+  for (int c0 = 0; c0 < n_split; c0 += 8) {
+    float w[8], x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int c = min(c0 + k, n_split - 1);
+      const long long row = base + (long long)c * kDecRows;
+      w[k] = (c0 + k < n_split) ? __builtin_amdgcn_exp2f(pm[row] - M) : 0.f;
+      x[k] = po[row * kD + d];
+      if (d == 0) L += w[k] * pl[row];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc += w[k] * x[k];
+  }
+  __shared__ float sL;
+  if (d == 0) sL = L;
+  __syncthreads();
+  const float v = acc / sL;
+  out[(long long)blockIdx.x * kD + d] = (uint16_t)f32_to_bf16(v);
+}
+
+AttnPlan decode_plan(int pos) {
+  AttnPlan p;
+  p.n_keys = pos + 1;
+  const int target = 32;  // splits per head: 8 x 32 = 256 workgroups
+  int kps = (p.n_keys + target - 1) / target;
+  if (kps < kBlk) kps = kBlk;
+  if (kps > kBlk * kDecMaxNB) kps = kBlk * kDecMaxNB;
+  p.keys_per_split = kps;
+  p.n_split = (p.n_keys + kps - 1) / kps;
+  p.n_cache_split = p.n_split;
+  p.blocks = (kps + kBlk - 1) / kBlk;
+  return p;
+}
+
+static size_t align256d(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t decode_partials_bytes(const AttnPlan& p) {
+  const size_t rows = (size_t)kHkv * p.n_split * kDecRows;
+  return align256d(rows * kD * 4) + 2 * align256d(rows * 4);
+}
+
+template <int NB>
+static hipError_t launch_dec_nb(const DecArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((k_decode_attn<NB>), dim3(kHkv * a.n_split), dim3(kDecThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const AttnPlan& plan, const DecodeLaunch& p, hipStream_t st) {
+  const size_t rows = (size_t)kHkv * plan.n_split * kDecRows;
+  char* w = static_cast<char*>(p.ws);
+  DecArgs a;
+  a.q = p.q; a.k = p.k; a.v = p.v; a.gq = p.gq; a.gk = p.gk; a.cos_t = p.cos_t; a.sin_t = p.sin_t; a.eps = p.eps;
+  a.Kc = p.Kc; a.Vc = p.Vc;
+  a.po = reinterpret_cast<float*>(w);
+  a.pm = reinterpret_cast<float*>(w + align256d(rows * kD * 4));
+  a.pl = reinterpret_cast<float*>(w + align256d(rows * kD * 4) + align256d(rows * 4));
+  a.pos = p.pos; a.Smax = p.Smax; a.n_split = plan.n_split; a.kps = plan.keys_per_split;
+  hipError_t e;
+  switch (plan.blocks) {
+    case 1: e = launch_dec_nb<1>(a, st); break;
+    case 2: e = launch_dec_nb<2>(a, st); break;
+    case 3: e = launch_dec_nb<3>(a, st); break;
+    case 4: e = launch_dec_nb<4>(a, st); break;
+    case 5: e = launch_dec_nb<5>(a, st); break;
+    case 6: e = launch_dec_nb<6>(a, st); break;
+    case 7: e = launch_dec_nb<7>(a, st); break;
+    default: e = launch_dec_nb<8>(a, st); break;
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_decode_combine, dim3(kHkv * kDecRows), dim3(kD), 0, st, a.po, a.pm, a.pl, p.out, plan.n_split);
+  return hipGetLastError();
+}
+
+}  // namespace ax

@@ -92,6 +92,26 @@ hipError_t launch_attn(const AttnPlan& plan, const AttnLaunch& p, hipStream_t st
 hipError_t launch_attn_split(const AttnPlan& plan, const AttnLaunch& p, hipStream_t st);  // partials
 hipError_t launch_attn_combine(const AttnPlan& plan, const void* ws, uint16_t* out, hipStream_t st);
 
+// Text-model decode step: one token at cache row pos, 64 query heads, 8 kv heads.
+struct DecodeLaunch {
+  const uint16_t* q;      // [64][128] raw
+  const uint16_t* k;      // [8][128] raw
+  const uint16_t* v;      // [8][128]
+  const uint16_t* gq;
+  const uint16_t* gk;
+  const float* cos_t;     // [64] for position pos + rope_delta
+  const float* sin_t;
+  float eps;
+  uint16_t* Kc;
+  uint16_t* Vc;
+  uint16_t* out;          // [64][128]
+  void* ws;
+  int pos, Smax;
+};
+AttnPlan decode_plan(int pos);
+size_t decode_partials_bytes(const AttnPlan& p);
+hipError_t launch_decode(const AttnPlan& plan, const DecodeLaunch& p, hipStream_t st);
+
 hipError_t launch_copy_words(const void* src, void* dst, size_t n, hipStream_t st);
 
 }  // namespace ax

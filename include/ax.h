@@ -236,6 +236,30 @@ int ax_expert_attn_fp8_combine(const void* ws, size_t ws_bytes, int S, int Smax,
                                void* stream);
 
 /*
+ * Text-model decode step (page code/alpamayo_tt/text.py,
+ * TTTextModel._layer_decode from the q/k norms to the attention output): the
+ * VLM's text layers have 64 query heads and 8 kv heads of width 128. One new
+ * token at cache position pos:
+ *   q_in [64][128], k_in and v_in [8][128] bf16 (raw, after the qkv
+ *   projection); gamma_q, gamma_k [128]; rope_cos, rope_sin float32 [64]:
+ *   cos / sin of (pos + rope_delta) * theta^(-2j/128), j = 0..63 (the one-token
+ *   table of ax_rope_tables(pos + rope_delta, 1, 128, theta, ...)).
+ * q and k are RMSNormed per head (eps) and roped in float32; the roped k
+ * (rounded to bf16) and v_in are written into row pos of Kc and Vc
+ * [8][Smax][128]; query head h attends to rows [0, pos] of kv head h / 8 with
+ * scale 1/sqrt(128); out [64][128] bf16. Rows after pos are never read; every
+ * row except pos is left untouched. 0 <= pos < Smax <= AX_SMAX_LIMIT.
+ * ws: at least ax_text_decode_workspace_bytes(pos, Smax) bytes, 256-byte
+ * aligned, contents on entry irrelevant. Two launches (split attention,
+ * combine).
+ */
+size_t ax_text_decode_workspace_bytes(int pos, int Smax);
+int ax_text_decode_attn(const uint16_t* q_in, const uint16_t* k_in, const uint16_t* v_in,
+                        const uint16_t* gamma_q, const uint16_t* gamma_k, const float* rope_cos,
+                        const float* rope_sin, float eps, uint16_t* Kc, uint16_t* Vc, int pos,
+                        int Smax, uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Measurement helper: dst[i] = src[i] for n 16-byte words, one plain
  * streaming copy kernel. Used to calibrate hardware byte counters against a
  * transfer of known size. Pointers 16-byte aligned.

@@ -173,3 +173,24 @@ def test_fp8_validation_codes():
     cb = ax.lib.ax_expert_attn_fp8_combine
     assert cb(FAKE, 8, 128, 256, FAKE, None) == ax.AX_E_WORKSPACE
     assert cb(FAKE, 1 << 30, 128, 256, None, None) == ax.AX_E_NULL
+
+
+def test_text_decode_validation_codes():
+    assert ax.text_decode_workspace_bytes(0, 1) > 0
+    assert ax.text_decode_workspace_bytes(4700, 8192) > 0
+    assert ax.text_decode_workspace_bytes(8192, 8192) == 0      # pos must be < Smax
+    assert ax.text_decode_workspace_bytes(-1, 64) == 0
+    f = ax.lib.ax_text_decode_attn
+
+    def call(q=FAKE, Kc=FAKE, pos=100, Smax=256, eps=1e-6, ws=FAKE, ws_bytes=1 << 30, c=FAKE):
+        return f(q, FAKE, FAKE, FAKE, FAKE, c, FAKE, eps, Kc, FAKE, pos, Smax, FAKE, ws, ws_bytes, None)
+
+    assert call(q=None) == ax.AX_E_NULL
+    assert call(c=None) == ax.AX_E_NULL
+    assert call(Kc=MIS) == ax.AX_E_ALIGN
+    assert call(pos=256) == ax.AX_E_SHAPE
+    assert call(pos=-1) == ax.AX_E_SHAPE
+    assert call(Smax=(1 << 20) + 1, pos=0) == ax.AX_E_SHAPE
+    assert call(eps=float("inf")) == ax.AX_E_ARG
+    assert call(ws_bytes=8) == ax.AX_E_WORKSPACE
+    assert call(ws=FAKE + 16) == ax.AX_E_WORKSPACE

@@ -1,0 +1,123 @@
+"""Parity of the text-model decode step (64 query heads, 8 kv heads, one token at pos) with the
+fp64 oracle, through the C ABI.
+
+Bars: every output element within 1e-2 + 2^-8 |ref| of the oracle and PCC >= 0.9999; cache row pos:
+V bit-exact (the given v), K within one bf16 ulp of the oracle's float64 roped k; every other
+cache row unchanged; rows after pos never read.
+
+The output bar: with few visible keys an output row is close to a single value row (magnitude
+up to ~4 for N(0,1) values), where one rounding of the output to bf16 alone is up to 2^-9 |ref|
+and the bf16 softmax weights of the value sum add up to 2^-9 max |v|; 2^-8 |ref| on top of the
+absolute 1e-2 covers both. With many keys the outputs are averages far below 1 and the
+absolute term governs, as in the expert step.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from flow_matching_action_amd import synth
+
+from gpu_util import DEV, bf16_to_f64, down, metrics, say, up
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ax():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from flow_matching_action_amd import ax as lib
+    return lib
+
+
+def run_decode(ax, d, eps=1e-6):
+    pos, Smax = d["pos"], d["Smax"]
+    q, k, v, gq, gk = (up(d[n]) for n in ("q", "k", "v", "gq", "gk"))
+    Kc, Vc = up(d["Kc"]), up(d["Vc"])
+    cos, sin = ax.rope_tables(pos + d["rope_delta"], 1)
+    cos, sin = torch.from_numpy(cos).to(DEV), torch.from_numpy(sin).to(DEV)
+    out = torch.zeros((64, 128), dtype=torch.int16, device=DEV)
+    ws = torch.empty(ax.text_decode_workspace_bytes(pos, Smax), dtype=torch.uint8, device=DEV)
+    assert q.shape == (64, 128) and k.shape == (8, 128) and Kc.shape == (8, Smax, 128) and cos.shape == (1, 64)
+    ax.text_decode_attn(q, k, v, gq, gk, cos, sin, eps, Kc, Vc, pos, Smax, out, ws)
+    torch.cuda.synchronize()
+    return down(out), down(Kc), down(Vc)
+
+
+def ref_decode(d):
+    return oracle.text_decode_attn(d["q"], d["k"], d["v"], d["gq"], d["gk"], d["Kc"], d["Vc"], d["pos"],
+                                   d["rope_delta"])
+
+
+def check(d, got, Kn, Vn, ref, label):
+    gotf = bf16_to_f64(got)
+    m = metrics(gotf, ref["out"])
+    excess = float(np.max(np.abs(gotf - ref["out"]) - (1e-2 + 2.0 ** -8 * np.abs(ref["out"]))))
+    print(f"{label}: max_abs={m['max_abs']:.3e} pcc={m['pcc']:.7f} rel_l2={m['rel_l2']:.3e} "
+          f"max(err - bar)={excess:.3e}", flush=True)
+    assert excess <= 0, m
+    assert m["pcc"] >= 0.9999, m
+    pos = d["pos"]
+    assert np.array_equal(Vn[:, pos], d["v"])
+    kr = bf16_to_f64(Kn[:, pos])
+    ulp = np.abs(bf16_to_f64(oracle.f64_to_bf16_bits(ref["k_roped"]))) * 2.0 ** -7 + 1e-30
+    assert np.all(np.abs(kr - ref["k_roped"]) <= ulp)
+    other = np.ones(d["Smax"], bool)
+    other[pos] = False
+    assert np.array_equal(Kn[:, other], d["Kc"][:, other]) and np.array_equal(Vn[:, other], d["Vc"][:, other])
+
+
+@pytest.mark.parametrize("pos,Smax", [(0, 64), (1, 64), (31, 64), (32, 64), (100, 256), (1023, 2048), (1024, 2048),
+                                      (1285, 2048), (4700, 8192), (8191, 8192), (12345, 16384)])
+def test_decode_matches_oracle(ax, pos, Smax):
+    d = synth.decode_inputs(Smax, pos, seed=3000 + pos)
+    say(f"text_decode_attn pos={pos} Smax={Smax}")
+    got, Kn, Vn = run_decode(ax, d)
+    check(d, got, Kn, Vn, ref_decode(d), f"decode pos={pos} Smax={Smax}")
+
+
+def test_decode_rope_delta(ax):
+    d = synth.decode_inputs(1024, 700, seed=41, rope_delta=-123)
+    say("text_decode_attn rope_delta=-123")
+    got, Kn, Vn = run_decode(ax, d)
+    check(d, got, Kn, Vn, ref_decode(d), "decode rope_delta=-123")
+
+
+def test_decode_rows_after_pos_never_read(ax):
+    d = synth.decode_inputs(2048, 900, seed=42)
+    say("text_decode_attn rows after pos: 7.0 vs NaN, old row pos NaN")
+    a, _, _ = run_decode(ax, d)
+    bad = dict(d)
+    for n in ("Kc", "Vc"):
+        bad[n] = d[n].copy()
+        bad[n][:, 900:] = 0x7FC0
+    b, _, _ = run_decode(ax, bad)
+    assert np.array_equal(a, b)
+
+
+def test_decode_repeat_is_bitwise_deterministic(ax):
+    d = synth.decode_inputs(8192, 4700, seed=43)
+    say("text_decode_attn determinism x3")
+    outs = [run_decode(ax, d)[0] for _ in range(3)]
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("step,layer", [(0, 0), (9, 63)])
+def test_decode_benchmark_inputs_match_oracle(ax, step, layer):
+    # the decode benchmark's own inputs: layer l's device-generated cache, fresh q/k/v per (step, layer)
+    pos, Smax = 4700, 8192
+    say(f"decode benchmark inputs, step {step}, layer {layer}")
+    Kc, Vc = (t.contiguous() for t in synth.device_cache(Smax, pos, layer, DEV))
+    q, k, v = (t.contiguous() for t in synth.device_decode_qkv(step, layer, DEV))
+    gq, gk = (t.contiguous() for t in synth.device_gammas(layer, DEV))
+    bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)  # noqa: E731
+    d = {"q": bits(q), "k": bits(k), "v": bits(v), "gq": bits(gq), "gk": bits(gk), "Kc": bits(Kc), "Vc": bits(Vc),
+         "pos": pos, "Smax": Smax, "rope_delta": 0}
+    ref = ref_decode(d)
+    cos, sin = (torch.from_numpy(t).to(DEV) for t in ax.rope_tables(pos, 1))
+    out = torch.empty((64, 128), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(ax.text_decode_workspace_bytes(pos, Smax), dtype=torch.uint8, device=DEV)
+    ax.text_decode_attn(q, k, v, gq, gk, cos, sin, 1e-6, Kc, Vc, pos, Smax, out, ws)
+    torch.cuda.synchronize()
+    check(d, bits(out), bits(Kc), bits(Vc), ref, f"decode sequence s={step} l={layer}")
