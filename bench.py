@@ -17,7 +17,11 @@ The fp8-cache variant (e4m3 codes + float32 row scales) is measured the same way
 workload, Smax = 8192, S = 8128 (the full cache), over 64 rotating fp8 caches (1.1 GB), and
 reported under "fp8" in the same line.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-fp8]
+The text model's single-token decode attention step (64 query heads, 8 kv heads, one token at
+pos = 4700 of the same 64 caches, fresh q/k/v per step) is measured the same way and reported
+under "decode".
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-fp8] [--no-decode]
        python bench.py --calibrate-copy BYTES   (a plain copy of known size, for counter runs)
 Prints one JSON line.
 """
@@ -118,6 +122,44 @@ class RotatingWorkload:
         j = i % self.n_sets
         self.ax.expert_layer_attn_split(self.q[j], self.k[j], self.v[j], self.gq[l], self.gk[l], self.cos, self.sin,
                                         EPS, self.K[l], self.V[l], self.S, self.Smax, self.ws, stream=stream)
+
+
+POS_DECODE = 4700
+
+
+def algorithmic_bytes_decode(pos: int) -> int:
+    """One decode step: cache rows [0, pos) of K and V, q (64 heads) and the new k/v in, the new rows of K
+    and V written, the output (64 heads) out."""
+    row = 128 * 2
+    return 2 * 8 * pos * row + 64 * row + 2 * 8 * row + 2 * 8 * row + 64 * row
+
+
+class RotatingDecode:
+    """The decode step over the bf16 workload's 64 layer caches, with fresh q/k/v per (step, layer)."""
+
+    def __init__(self, ax, torch, wl: RotatingWorkload, pos: int = POS_DECODE):
+        from flow_matching_action_amd import synth
+        dev = "cuda:0"
+        self.ax, self.wl, self.pos = ax, wl, pos
+        self.q, self.k, self.v = [], [], []
+        for i in range(wl.n_sets):
+            s, l = divmod(i, wl.n_layers)
+            q, k, v = synth.device_decode_qkv(s, l, dev)
+            self.q.append(q.contiguous())
+            self.k.append(k.contiguous())
+            self.v.append(v.contiguous())
+        cos, sin = ax.rope_tables(pos + ROPE_DELTA, 1)
+        self.cos = torch.from_numpy(cos).to(dev)
+        self.sin = torch.from_numpy(sin).to(dev)
+        self.out = [torch.empty((64, 128), dtype=torch.bfloat16, device=dev) for _ in range(wl.n_layers)]
+        self.ws = torch.empty(ax.text_decode_workspace_bytes(pos, wl.Smax), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def step(self, i: int, stream=None):
+        wl = self.wl
+        l, j = i % wl.n_layers, i % wl.n_sets
+        self.ax.text_decode_attn(self.q[j], self.k[j], self.v[j], wl.gq[l], wl.gk[l], self.cos, self.sin, EPS,
+                                 wl.K[l], wl.V[l], self.pos, wl.Smax, self.out[l], self.ws, stream=stream)
 
 
 class RotatingWorkloadF8:
@@ -276,6 +318,7 @@ def main() -> int:
     ap.add_argument("--replays", type=int, default=5, help="timed replays of the K-step graph (median reported)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache workload")
+    ap.add_argument("--no-decode", action="store_true", help="skip the text-model decode workload")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run the plain copy kernel on BYTES (for rocprofv3 --pmc calibration)")
     args = ap.parse_args()
@@ -380,6 +423,32 @@ def main() -> int:
                          "matrix_peak_tflops_bf16": 2500.0},
             "replays_ms": [round(t, 4) for t in t8],
             "outputs_finite": ok8,
+        }
+    if not args.no_decode:
+        dec = RotatingDecode(ax, torch, wl)
+        with torch.cuda.stream(stream):
+            for i in range(W):
+                dec.step(i, stream)
+        torch.cuda.synchronize()
+        td = timed_graph(torch, stream, dec.step, W, K, args.replays)
+        usd = statistics.median(td) * 1e3 / K
+        bd = algorithmic_bytes_decode(POS_DECODE)
+        okd = all(bool(torch.isfinite(o.float()).all()) for o in dec.out)
+        out_ok = out_ok and okd
+        result["outputs_finite"] = out_ok
+        result["decode"] = {
+            "workload": "text-model decode attention step, 64 q heads / 8 kv heads, one token at pos=4700 of "
+                        "Smax=8192 bf16 caches, 64 rotating layer caches (2.1 GB, cold), fresh q/k/v per "
+                        "(step, layer), hipGraph of K steps",
+            "value": round(usd, 3), "unit": "us/step",
+            "achieved_hbm_gbs": round(bd / (usd * 1e-6) / 1e9, 1),
+            "roofline": {"bound": "hbm", "achieved": round(bd / (usd * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(bd / (usd * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "traffic": None,
+                         "kernel": "k_decode_attn + k_decode_combine (the whole step, two launches)",
+                         "algorithmic_bytes_per_step": bd},
+            "replays_ms": [round(t, 4) for t in td],
+            "outputs_finite": okd,
         }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()

@@ -331,35 +331,67 @@ __global__ __launch_bounds__(kDecThreads, 1) void k_decode_attn(DecArgs a) {
   }
 }
 
-// Combine of the splits: workgroup (head g, row r) = output row 8 g + r (query head 8 g + r), one
-// column per thread; the loads of up to 8 splits are issued before any is used. Fixed order.
-__global__ __launch_bounds__(kD) void k_decode_combine(const float* po, const float* pm, const float* pl,
-                                                       uint16_t* out, int n_split) {
+// Combine of the splits: workgroup (head g, row r) = output row 8 g + r (query head 8 g + r):
+// 512 threads in 4 split groups of 128 columns; group k reduces splits k, k + 4, ..., issuing the
+// loads of 8 splits before using any of them, so 32 splits are in flight at once. The groups
+// meet in LDS. Fixed order.
+constexpr int kDecCombGroups = 4;
+constexpr int kDecCombBatch = 8;
+__global__ __launch_bounds__(kDecCombGroups * kD) void k_decode_combine(const float* po, const float* pm,
+                                                                        const float* pl, uint16_t* out,
+                                                                        int n_split) {
+  __shared__ float sM[kDecCombGroups], sL[kDecCombGroups];
+  __shared__ float sA[kDecCombGroups][kD];
   const int g = blockIdx.x / kDecRows;
   const int r = blockIdx.x % kDecRows;
-  const int d = threadIdx.x;
+  const int grp = threadIdx.x / kD;
+  const int d = threadIdx.x % kD;
   const long long base = (long long)g * n_split * kDecRows + r;  // row of split c: base + c * 8
-  float M = -INFINITY;
-  for (int c = 0; c < n_split; ++c) M = fmaxf(M, pm[base + (long long)c * kDecRows]);
-  float L = 0.f, acc = 0.f;
-  for (int c0 = 0; c0 < n_split; c0 += 8) {
-    float w[8], x[8];
+  float M = -INFINITY, L = 0.f, acc = 0.f;
+  for (int c0 = grp; c0 < n_split; c0 += kDecCombGroups * kDecCombBatch) {
+    float mv[kDecCombBatch], lv[kDecCombBatch], xv[kDecCombBatch];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int c = min(c0 + k, n_split - 1);
+    for (int k = 0; k < kDecCombBatch; ++k) {
+      const int c = min(c0 + kDecCombGroups * k, n_split - 1);  // past the end: a repeat, weighted 0 below
       const long long row = base + (long long)c * kDecRows;
-      w[k] = (c0 + k < n_split) ? __builtin_amdgcn_exp2f(pm[row] - M) : 0.f;
-      x[k] = po[row * kD + d];
-      if (d == 0) L += w[k] * pl[row];
+      mv[k] = pm[row];
+      lv[k] = pl[row];
+      xv[k] = po[row * kD + d];
     }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the batch is issued before any is used
+    float Mb = M;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc += w[k] * x[k];
+    for (int k = 0; k < kDecCombBatch; ++k)
+      if (c0 + kDecCombGroups * k < n_split) Mb = fmaxf(Mb, mv[k]);
+    const float rs = __builtin_amdgcn_exp2f(M - Mb);  // 0 while M is -inf
+    L *= rs;
+    acc *= rs;
+    M = Mb;
+#pragma unroll
+    for (int k = 0; k < kDecCombBatch; ++k) {
+      const float w = (c0 + kDecCombGroups * k < n_split) ? __builtin_amdgcn_exp2f(mv[k] - M) : 0.f;
+      L += w * lv[k];
+      acc += w * xv[k];
+    }
   }
-  __shared__ float sL;
-  if (d == 0) sL = L;
+  if (d == 0) {
+    sM[grp] = M;
+    sL[grp] = L;
+  }
+  sA[grp][d] = acc;
   __syncthreads();
-  const float v = acc / sL;
-  out[(long long)blockIdx.x * kD + d] = (uint16_t)f32_to_bf16(v);
+  if (grp != 0) return;
+  float Mt = sM[0];  // group 0 holds split 0, so Mt is finite
+#pragma unroll
+  for (int k = 1; k < kDecCombGroups; ++k) Mt = fmaxf(Mt, sM[k]);
+  float Lt = 0.f, At = 0.f;
+#pragma unroll
+  for (int k = 0; k < kDecCombGroups; ++k) {
+    const float w = __builtin_amdgcn_exp2f(sM[k] - Mt);  // 0 for a group without splits
+    Lt += w * sL[k];
+    At += w * sA[k][d];
+  }
+  out[(long long)blockIdx.x * kD + d] = (uint16_t)f32_to_bf16(At / Lt);
 }
 
 AttnPlan decode_plan(int pos) {
@@ -411,7 +443,8 @@ hipError_t launch_decode(const AttnPlan& plan, const DecodeLaunch& p, hipStream_
     default: e = launch_dec_nb<8>(a, st); break;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_decode_combine, dim3(kHkv * kDecRows), dim3(kD), 0, st, a.po, a.pm, a.pl, p.out, plan.n_split);
+  hipLaunchKernelGGL(k_decode_combine, dim3(kHkv * kDecRows), dim3(kDecCombGroups * kD), 0, st, a.po, a.pm, a.pl,
+                     p.out, plan.n_split);
   return hipGetLastError();
 }
 
