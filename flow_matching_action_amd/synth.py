@@ -201,6 +201,31 @@ def device_decode_qkv(step: int, layer: int, device):
     return t[:64], t[64:64 + N_KV_HEADS], t[64 + N_KV_HEADS:]
 
 
+def layer_weights(seed: int, hidden: int = 1536, qkv: int = 4096, attn: int = 2048, mlp: int = 6144) -> dict:
+    """Random weights of one expert decoder layer as bf16 bits, stored input-major ([in, out]):
+    ln1, ln2 [hidden] = 1 + 0.1 N(0,1); wqkv [hidden, qkv], wo [attn, hidden], w1 and w3 [hidden, mlp],
+    w2 [mlp, hidden] = N(0,1) / sqrt(in), so that every product keeps unit scale; qn, kn [128] as the
+    other gammas. Draw order: ln1, wqkv, qn, kn, wo, ln2, w1, w3, w2."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+
+    def draw(*shape):
+        return rng.standard_normal(shape, dtype=np.float32)
+
+    def mat(i, o):
+        return f32_to_bf16_bits(draw(i, o) / np.float32(np.sqrt(i)))
+
+    return {"ln1": f32_to_bf16_bits(1.0 + 0.1 * draw(hidden)), "wqkv": mat(hidden, qkv),
+            "qn": f32_to_bf16_bits(1.0 + 0.1 * draw(128)), "kn": f32_to_bf16_bits(1.0 + 0.1 * draw(128)),
+            "wo": mat(attn, hidden), "ln2": f32_to_bf16_bits(1.0 + 0.1 * draw(hidden)),
+            "w1": mat(hidden, mlp), "w3": mat(hidden, mlp), "w2": mat(mlp, hidden)}
+
+
+def residual_inputs(seed: int, n_tok: int = N_TOK, hidden: int = 1536) -> np.ndarray:
+    """The residual stream entering a layer, [n_tok, hidden] bf16 bits of N(0,1) draws."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return f32_to_bf16_bits(rng.standard_normal((n_tok, hidden), dtype=np.float32))
+
+
 def device_qkv(step: int, layer: int, device):
     """q [16,64,128], own k and v [8,64,128] (bf16 tensors) of one (step, layer)."""
     t = _dev_normal_bf16((N_Q_HEADS + 2 * N_KV_HEADS, N_TOK, HEAD_DIM), 5000 + 64 * step + layer, device)

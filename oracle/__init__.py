@@ -18,6 +18,7 @@ from .expert_attn import (
     quantize_rows_e4m3, dequantize_rows_e4m3, expert_attn_layer_fp8,
 )
 from .text_decode import N_KV_HEADS_TEXT, N_Q_HEADS_TEXT, decode_attention, text_decode_attn
+from .expert_layer import HIDDEN, MLP, QKV, expert_layer, silu
 
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "e4m3_bits_to_f64", "f64_to_e4m3_bits", "E4M3_MAX",
@@ -26,4 +27,5 @@ __all__ = [
     "attention", "attention_partial", "lse_combine", "expert_attn_layer",
     "quantize_rows_e4m3", "dequantize_rows_e4m3", "expert_attn_layer_fp8",
     "N_Q_HEADS_TEXT", "N_KV_HEADS_TEXT", "decode_attention", "text_decode_attn",
+    "HIDDEN", "QKV", "MLP", "expert_layer", "silu",
 ]

@@ -1,0 +1,71 @@
+"""fp64 oracle of one whole action-expert decoder layer with given weights (test infrastructure).
+
+Test infrastructure only: imported by ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py``; the product path never touches it.
+
+The op sequence is the one page ``code/alpamayo_tt/EXPERT_NOTES.md`` lists per layer (section
+"Layouts": rms_norm -> linear(wqkv) -> nlp_create_qkv_heads -> q/k norms -> RoPE -> fill_cache ->
+attention -> nlp_concat_heads -> linear(wo) -> add -> rms_norm -> linear(w1, silu), linear(w3) ->
+mul -> linear(w2) -> add), with the shapes of its table: residual [64, 1536]; wqkv [1536, 4096]
+holding q heads 0..15, then k heads 0..7, then v heads 0..7 in its columns; wo [2048, 1536];
+w1 and w3 [1536, 6144]; w2 [6144, 1536]; all weights stored input-major ([in, out], the
+transpose of the HF layout, as the table says). Page ``code/alpamayo_tt/expert.py``,
+``TTExpert.layer``, is the same sequence in code.
+
+Reading (also in the design notes): every op hands a bf16 tensor to the next, as ttnn ops do
+(the pages' activations are bf16 throughout), so the oracle rounds to bf16 at each op boundary
+of the list above and computes inside each op in float64: the residual inputs of the adds, the
+normed activations, qkv, the attention output, o, g = silu(n2 w1), u = n2 w3, m = g u, d.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .codecs import bf16_bits_to_f64, f64_to_bf16_bits
+from .expert_attn import EPS, N_KV_HEADS, N_Q_HEADS, expert_attn_layer, rms_norm
+
+HIDDEN = 1536
+QKV = 4096
+ATTN_OUT = N_Q_HEADS * 128
+MLP = 6144
+
+
+def _bf(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to bf16 and return them as float64 (an op's bf16 output)."""
+    return bf16_bits_to_f64(f64_to_bf16_bits(x))
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    return x / (1.0 + np.exp(-x))
+
+
+def expert_layer(x, ln1, wqkv, qn, kn, wo, ln2, w1, w3, w2, Kc, Vc, S: int, Smax: int, rope_delta: int = 0,
+                 eps: float = EPS) -> dict:
+    """One decoder layer: x [64, 1536] and every weight as bf16 bits; caches [8, Smax, 128] bits.
+    The residual RMSNorms are ``rms_norm`` over the 1536 columns (eps as for the heads).
+
+    Returns ``x_out`` [64, 1536] float64 (bf16 values), the intermediate bf16 tensors (as float64)
+    ``n1``, ``qkv``, ``attn`` ([64, 2048], heads concatenated), ``x2``, ``n2``, ``m``, and the
+    updated caches ``Kc_new``/``Vc_new`` (bits).
+    """
+    x = bf16_bits_to_f64(x)
+    w = {k: bf16_bits_to_f64(v) for k, v in dict(ln1=ln1, wqkv=wqkv, wo=wo, ln2=ln2, w1=w1, w3=w3, w2=w2).items()}
+    n1 = _bf(rms_norm(x, w["ln1"], eps))
+    qkv = _bf(n1 @ w["wqkv"])                                   # [64, 4096]
+    t = x.shape[0]
+    q = qkv[:, :N_Q_HEADS * 128].reshape(t, N_Q_HEADS, 128).transpose(1, 0, 2)             # [16, 64, 128]
+    k = qkv[:, N_Q_HEADS * 128:(N_Q_HEADS + N_KV_HEADS) * 128].reshape(t, N_KV_HEADS, 128).transpose(1, 0, 2)
+    v = qkv[:, (N_Q_HEADS + N_KV_HEADS) * 128:].reshape(t, N_KV_HEADS, 128).transpose(1, 0, 2)
+    att = expert_attn_layer(f64_to_bf16_bits(q), f64_to_bf16_bits(k), f64_to_bf16_bits(v), qn, kn, Kc, Vc, S, Smax,
+                            rope_delta, eps)
+    a = _bf(att["out"]).transpose(1, 0, 2).reshape(t, N_Q_HEADS * 128)                      # concat heads
+    o = _bf(a @ w["wo"])
+    x2 = _bf(x + o)
+    n2 = _bf(rms_norm(x2, w["ln2"], eps))
+    g = _bf(silu(n2 @ w["w1"]))
+    u = _bf(n2 @ w["w3"])
+    m = _bf(g * u)
+    d = _bf(m @ w["w2"])
+    x3 = _bf(x2 + d)
+    return {"x_out": x3, "n1": n1, "qkv": qkv, "attn": a, "x2": x2, "n2": n2, "m": m,
+            "Kc_new": att["Kc_new"], "Vc_new": att["Vc_new"]}
