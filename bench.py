@@ -21,7 +21,12 @@ The text model's single-token decode attention step (64 query heads, 8 kv heads,
 pos = 4700 of the same 64 caches, fresh q/k/v per step) is measured the same way and reported
 under "decode".
 
+The whole expert decoder layer (residual norms, the qkv / o / SwiGLU projections with 64 layers of
+seeded bf16 weights, and the attention step on the same caches), chained so that each step's output
+residual is the next step's input, is measured the same way and reported under "layer".
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-fp8] [--no-decode]
+                       [--no-layer]
        python bench.py --calibrate-copy BYTES   (a plain copy of known size, for counter runs)
 Prints one JSON line.
 """
@@ -160,6 +165,51 @@ class RotatingDecode:
         l, j = i % wl.n_layers, i % wl.n_sets
         self.ax.text_decode_attn(self.q[j], self.k[j], self.v[j], wl.gq[l], wl.gk[l], self.cos, self.sin, EPS,
                                  wl.K[l], wl.V[l], self.pos, wl.Smax, self.out[l], self.ws, stream=stream)
+
+
+LAYER_WEIGHT_ELEMS = 1536 * 4096 + 2048 * 1536 + 2 * 1536 * 6144 + 6144 * 1536
+
+
+def algorithmic_bytes_layer(S: int) -> int:
+    """One whole expert layer: the five weight matrices and four gammas, the residual in and out, the
+    attention step's cache rows [0, S) read and tail rows written, the RoPE tables. Intermediates
+    between the layer's kernels are not counted (an ideal layer keeps them on chip)."""
+    row = 128 * 2
+    weights = 2 * LAYER_WEIGHT_ELEMS + 2 * (2 * 1536 + 2 * 128)
+    resid = 2 * 64 * 1536 * 2
+    cache = 2 * 8 * S * row + 2 * 8 * 64 * row
+    return weights + resid + cache + 2 * 64 * 64 * 4
+
+
+def algorithmic_flops_layer(S: int) -> int:
+    """Matrix flops of one whole layer: the four projections (2 x 64 x in x out each) plus the
+    attention's."""
+    return 2 * 64 * LAYER_WEIGHT_ELEMS + algorithmic_flops(S)
+
+
+class RotatingLayer:
+    """The whole expert layer over the bf16 workload's 64 layer caches with 64 layers of seeded
+    weights (4.8 GB, cold), chained: the output residual of step i is the input of step i + 1."""
+
+    def __init__(self, ax, torch, wl: RotatingWorkload):
+        from flow_matching_action_amd import synth
+        dev = "cuda:0"
+        self.ax, self.wl = ax, wl
+        self.w = [synth.device_layer_weights(l, dev) for l in range(wl.n_layers)]
+        g = torch.Generator(device=dev)
+        g.manual_seed(11000)
+        x0 = torch.randn((64, 1536), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        self.x = [x0.contiguous(), torch.empty_like(x0)]
+        self.ws = torch.zeros(ax.expert_layer_workspace_bytes(wl.S, wl.Smax), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def step(self, i: int, stream=None):
+        wl = self.wl
+        l = i % wl.n_layers
+        w = self.w[l]
+        self.ax.expert_layer(self.x[i & 1], w["ln1"], w["wqkv"], w["qn"], w["kn"], w["wo"], w["ln2"], w["w1"],
+                             w["w3"], w["w2"], wl.cos, wl.sin, EPS, wl.K[l], wl.V[l], wl.S, wl.Smax,
+                             self.x[(i + 1) & 1], self.ws, stream=stream)
 
 
 class RotatingWorkloadF8:
@@ -319,6 +369,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache workload")
     ap.add_argument("--no-decode", action="store_true", help="skip the text-model decode workload")
+    ap.add_argument("--no-layer", action="store_true", help="skip the whole-layer workload")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run the plain copy kernel on BYTES (for rocprofv3 --pmc calibration)")
     args = ap.parse_args()
@@ -449,6 +500,33 @@ def main() -> int:
                          "algorithmic_bytes_per_step": bd},
             "replays_ms": [round(t, 4) for t in td],
             "outputs_finite": okd,
+        }
+    if not args.no_layer:
+        lay = RotatingLayer(ax, torch, wl)
+        with torch.cuda.stream(stream):
+            for i in range(W):
+                lay.step(i, stream)
+        torch.cuda.synchronize()
+        tl = timed_graph(torch, stream, lay.step, W, K, args.replays)
+        usl = statistics.median(tl) * 1e3 / K
+        bl = algorithmic_bytes_layer(S)
+        okl = all(bool(torch.isfinite(x.float()).all()) for x in lay.x)
+        out_ok = out_ok and okl
+        result["outputs_finite"] = out_ok
+        result["layer"] = {
+            "workload": "whole expert decoder layer (residual norms, qkv / o / SwiGLU projections, the attention "
+                        "step), 64 tokens, Smax=8192 S=4700 bf16 caches, 64 rotating layers of seeded bf16 "
+                        "weights (4.8 GB) and caches (2.1 GB), cold, chained residual, hipGraph of K steps",
+            "value": round(usl, 3), "unit": "us/layer",
+            "achieved_hbm_gbs": round(bl / (usl * 1e-6) / 1e9, 1),
+            "roofline": {"bound": "hbm", "achieved": round(bl / (usl * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(bl / (usl * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "traffic": None,
+                         "kernel": "the whole layer (eleven launches)",
+                         "algorithmic_bytes_per_layer": bl,
+                         "algorithmic_flops_per_layer": algorithmic_flops_layer(S)},
+            "replays_ms": [round(t, 4) for t in tl],
+            "outputs_finite": okl,
         }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()

@@ -86,6 +86,14 @@ lib.ax_text_decode_workspace_bytes.argtypes = [_I, _I]
 lib.ax_text_decode_attn.restype = _I
 lib.ax_text_decode_attn.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _I, _I, _P, _P,
                                     ctypes.c_size_t, _P]
+lib.ax_expert_layer_workspace_bytes.restype = ctypes.c_size_t
+lib.ax_expert_layer_workspace_bytes.argtypes = [_I, _I]
+lib.ax_expert_layer.restype = _I
+lib.ax_expert_layer.argtypes = [_P] * 12 + [ctypes.c_float, _P, _P, _I, _I, _P, _P, ctypes.c_size_t, _P]
+lib.ax_linear_m64_workspace_bytes.restype = ctypes.c_size_t
+lib.ax_linear_m64_workspace_bytes.argtypes = [_I, _I]
+lib.ax_linear_m64.restype = _I
+lib.ax_linear_m64.argtypes = [_P, _P, _I, _I, _P, _P, ctypes.c_size_t, _P]
 lib.ax_copy_words.restype = _I
 lib.ax_copy_words.argtypes = [_P, _P, ctypes.c_size_t, _P]
 
@@ -94,7 +102,8 @@ EXPORTS = ("ax_abi_version", "ax_strerror", "ax_rope_tables", "ax_qk_norm_rope",
            "ax_expert_layer_attn", "ax_expert_layer_attn_split", "ax_expert_attn_combine",
            "ax_expert_attn_fp8_workspace_bytes", "ax_cache_tail_write_fp8", "ax_expert_attn_fp8",
            "ax_expert_layer_attn_fp8", "ax_expert_layer_attn_fp8_split", "ax_expert_attn_fp8_combine",
-           "ax_text_decode_workspace_bytes", "ax_text_decode_attn", "ax_copy_words")
+           "ax_text_decode_workspace_bytes", "ax_text_decode_attn", "ax_expert_layer_workspace_bytes",
+           "ax_expert_layer", "ax_linear_m64_workspace_bytes", "ax_linear_m64", "ax_copy_words")
 
 
 def _check(fn: str, code: int) -> None:
@@ -235,6 +244,27 @@ def text_decode_attn(q_in, k_in, v_in, gamma_q, gamma_k, rope_cos, rope_sin, eps
     _check("ax_text_decode_attn", lib.ax_text_decode_attn(
         _ptr(q_in), _ptr(k_in), _ptr(v_in), _ptr(gamma_q), _ptr(gamma_k), _ptr(rope_cos), _ptr(rope_sin),
         float(eps), _ptr(Kc), _ptr(Vc), int(pos), int(Smax), _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def expert_layer_workspace_bytes(S: int, Smax: int) -> int:
+    return int(lib.ax_expert_layer_workspace_bytes(int(S), int(Smax)))
+
+
+def expert_layer(x_in, ln1, wqkv, q_norm_w, k_norm_w, wo, ln2, w1, w3, w2, rope_cos, rope_sin, eps, Kc, Vc, S: int,
+                 Smax: int, x_out, ws, stream=None):
+    _check("ax_expert_layer", lib.ax_expert_layer(
+        _ptr(x_in), _ptr(ln1), _ptr(wqkv), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(wo), _ptr(ln2), _ptr(w1), _ptr(w3),
+        _ptr(w2), _ptr(rope_cos), _ptr(rope_sin), float(eps), _ptr(Kc), _ptr(Vc), int(S), int(Smax), _ptr(x_out),
+        _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def linear_m64_workspace_bytes(K: int, N: int) -> int:
+    return int(lib.ax_linear_m64_workspace_bytes(int(K), int(N)))
+
+
+def linear_m64(A, W, K: int, N: int, C, ws, stream=None):
+    _check("ax_linear_m64", lib.ax_linear_m64(_ptr(A), _ptr(W), int(K), int(N), _ptr(C), _ptr(ws), _nbytes(ws),
+                                              _stream(stream)))
 
 
 def copy_words(src, dst, n_words16: int, stream=None):

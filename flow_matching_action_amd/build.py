@@ -14,7 +14,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libax.so")
-SOURCES = ["ax_api.hip", "ax_qknorm.hip", "ax_attn.hip", "ax_attn_f8.hip", "ax_decode.hip"]
+SOURCES = ["ax_api.hip", "ax_qknorm.hip", "ax_attn.hip", "ax_attn_f8.hip", "ax_decode.hip", "ax_layer.hip"]
 
 # Packed-fp32 instructions are switched off for all device code; hipcc's host pass warns that
 # it does not know the feature, which is harmless.

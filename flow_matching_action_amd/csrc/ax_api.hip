@@ -287,6 +287,45 @@ int ax_text_decode_attn(const uint16_t* q_in, const uint16_t* k_in, const uint16
   return status(ax::launch_decode(ax::decode_plan(pos), p, as_stream(stream)));
 }
 
+// ---- the whole expert layer ------------------------------------------------------------------------
+
+size_t ax_linear_m64_workspace_bytes(int K, int N) {
+  return ax::gemm64_shape_ok(K, N) ? ax::gemm64_partials_bytes(K, N) : 0;
+}
+
+int ax_linear_m64(const uint16_t* A, const uint16_t* W, int K, int N, uint16_t* C, void* ws, size_t ws_bytes,
+                  void* stream) {
+  int r = check_ptrs({A, W, C, ws});
+  if (r == AX_OK && (!ax::gemm64_shape_ok(K, N) || K > (1 << 20) || N > (1 << 20))) r = AX_E_SHAPE;
+  if (r == AX_OK && ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || ws_bytes < ax_linear_m64_workspace_bytes(K, N)))
+    r = AX_E_WORKSPACE;
+  if (r == AX_OK) r = check_device();
+  if (r != AX_OK) return r;
+  return status(ax::launch_linear64(A, W, K, N, C, ws, as_stream(stream)));
+}
+
+size_t ax_expert_layer_workspace_bytes(int S, int Smax) {
+  if (check_shape(S, Smax) != AX_OK) return 0;
+  return ax::layer_workspace_bytes(S, Smax);
+}
+
+int ax_expert_layer(const uint16_t* x_in, const uint16_t* ln1, const uint16_t* wqkv, const uint16_t* q_norm_w,
+                    const uint16_t* k_norm_w, const uint16_t* wo, const uint16_t* ln2, const uint16_t* w1,
+                    const uint16_t* w3, const uint16_t* w2, const float* rope_cos, const float* rope_sin, float eps,
+                    uint16_t* Kc, uint16_t* Vc, int S, int Smax, uint16_t* x_out, void* ws, size_t ws_bytes,
+                    void* stream) {
+  int r = check_ptrs({x_in, ln1, wqkv, q_norm_w, k_norm_w, wo, ln2, w1, w3, w2, rope_cos, rope_sin, Kc, Vc, x_out, ws});
+  if (r == AX_OK) r = check_shape(S, Smax);
+  if (r == AX_OK) r = check_eps(eps);
+  if (r == AX_OK && ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || ws_bytes < ax_expert_layer_workspace_bytes(S, Smax)))
+    r = AX_E_WORKSPACE;
+  if (r == AX_OK) r = check_device();
+  if (r != AX_OK) return r;
+  ax::LayerLaunch p{x_in, ln1, wqkv, q_norm_w, k_norm_w, wo, ln2, w1, w3, w2, rope_cos, rope_sin, eps, Kc, Vc, S, Smax,
+                    x_out, ws};
+  return status(ax::launch_layer(p, as_stream(stream)));
+}
+
 int ax_copy_words(const void* src, void* dst, size_t n_words16, void* stream) {
   int r = check_ptrs({src, dst});
   if (r == AX_OK) r = check_device();

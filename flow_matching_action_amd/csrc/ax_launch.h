@@ -112,6 +112,39 @@ AttnPlan decode_plan(int pos);
 size_t decode_partials_bytes(const AttnPlan& p);
 hipError_t launch_decode(const AttnPlan& plan, const DecodeLaunch& p, hipStream_t st);
 
+// One whole expert decoder layer (residual norms, projections, SwiGLU MLP around the attention
+// step). Widths of the expert's layer: residual 1536, qkv 4096 (16 + 8 + 8 heads of 128), MLP 6144.
+constexpr int kLayerHidden = 1536;
+constexpr int kLayerQkv = 4096;
+constexpr int kLayerMlp = 6144;
+struct LayerLaunch {
+  const uint16_t* x;      // [64][1536]
+  const uint16_t* ln1;    // [1536]
+  const uint16_t* wqkv;   // [1536][4096]
+  const uint16_t* qn;     // [128]
+  const uint16_t* kn;
+  const uint16_t* wo;     // [2048][1536]
+  const uint16_t* ln2;
+  const uint16_t* w1;     // [1536][6144]
+  const uint16_t* w3;
+  const uint16_t* w2;     // [6144][1536]
+  const float* cos_t;     // [64][64]
+  const float* sin_t;
+  float eps;
+  uint16_t* Kc;
+  uint16_t* Vc;
+  int S, Smax;
+  uint16_t* x_out;        // [64][1536]
+  void* ws;
+};
+size_t layer_workspace_bytes(int S, int Smax);
+hipError_t launch_layer(const LayerLaunch& p, hipStream_t st);
+// C[64][N] = bf16(A[64][K] W[K][N]) (W input-major); ws: gemm64_partials_bytes(K, N) bytes.
+bool gemm64_shape_ok(int K, int N);
+size_t gemm64_partials_bytes(int K, int N);
+hipError_t launch_linear64(const uint16_t* A, const uint16_t* W, int K, int N, uint16_t* C, void* ws,
+                           hipStream_t st);
+
 hipError_t launch_copy_words(const void* src, void* dst, size_t n, hipStream_t st);
 
 }  // namespace ax

@@ -201,6 +201,27 @@ def device_decode_qkv(step: int, layer: int, device):
     return t[:64], t[64:64 + N_KV_HEADS], t[64 + N_KV_HEADS:]
 
 
+def device_layer_weights(layer: int, device, hidden: int = 1536, qkv: int = 4096, attn: int = 2048,
+                         mlp: int = 6144) -> dict:
+    """Weights of one expert decoder layer on the device (bf16 tensors, input-major), the recipe of
+    ``layer_weights`` drawn with torch's device generator (seed 10000 + layer); qn and kn are the
+    gammas of ``device_gammas(layer)``."""
+    g = torch.Generator(device=device)
+    g.manual_seed(10000 + layer)
+
+    def draw(*shape):
+        return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+
+    def mat(i, o):
+        return (draw(i, o) / float(np.sqrt(i))).to(torch.bfloat16).contiguous()
+
+    qn, kn = device_gammas(layer, device)
+    return {"ln1": (1.0 + 0.1 * draw(hidden)).to(torch.bfloat16), "wqkv": mat(hidden, qkv),
+            "qn": qn.contiguous(), "kn": kn.contiguous(), "wo": mat(attn, hidden),
+            "ln2": (1.0 + 0.1 * draw(hidden)).to(torch.bfloat16), "w1": mat(hidden, mlp), "w3": mat(hidden, mlp),
+            "w2": mat(mlp, hidden)}
+
+
 def layer_weights(seed: int, hidden: int = 1536, qkv: int = 4096, attn: int = 2048, mlp: int = 6144) -> dict:
     """Random weights of one expert decoder layer as bf16 bits, stored input-major ([in, out]):
     ln1, ln2 [hidden] = 1 + 0.1 N(0,1); wqkv [hidden, qkv], wo [attn, hidden], w1 and w3 [hidden, mlp],

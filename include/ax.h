@@ -260,6 +260,41 @@ int ax_text_decode_attn(const uint16_t* q_in, const uint16_t* k_in, const uint16
                         int Smax, uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * One whole action-expert decoder layer, the pages' layer_fn(i, x, K, V) -> x
+ * (page code/alpamayo_tt/EXPERT_NOTES.md, section "Layouts": the per-layer op
+ * list and the weight shapes; page code/alpamayo_tt/expert.py, TTExpert.layer):
+ *   n1 = RMSNorm(x; ln1), qkv = n1 wqkv split into q heads 0..15, k heads 0..7,
+ *   v heads 0..7 (columns 128 h .. 128 h + 127 of each block), the attention
+ *   step of ax_expert_layer_attn on them (q_norm_w / k_norm_w are its gammas),
+ *   heads concatenated, x2 = x + attn wo, n2 = RMSNorm(x2; ln2),
+ *   x_out = x2 + (silu(n2 w1) * (n2 w3)) w2.
+ * x_in, x_out [64][1536]; ln1, ln2 [1536]; weights input-major (the transpose
+ * of the HF layout, as the pages store them): wqkv [1536][4096], wo
+ * [2048][1536], w1 and w3 [1536][6144], w2 [6144][1536]; all bf16. Every op
+ * hands a bf16 tensor to the next (rounded to nearest even); inside an op the
+ * arithmetic is float32 (products of bf16 on the matrix cores). Updates the
+ * cache tail like ax_expert_layer_attn. x_out must not alias x_in. ws: at least
+ * ax_expert_layer_workspace_bytes(S, Smax) bytes, 256-byte aligned. Eleven
+ * launches.
+ */
+size_t ax_expert_layer_workspace_bytes(int S, int Smax);
+int ax_expert_layer(const uint16_t* x_in, const uint16_t* ln1, const uint16_t* wqkv,
+                    const uint16_t* q_norm_w, const uint16_t* k_norm_w, const uint16_t* wo,
+                    const uint16_t* ln2, const uint16_t* w1, const uint16_t* w3, const uint16_t* w2,
+                    const float* rope_cos, const float* rope_sin, float eps, uint16_t* Kc, uint16_t* Vc,
+                    int S, int Smax, uint16_t* x_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The layer's projection on its own: C[64][N] = bf16(A[64][K] W[K][N]) for 64
+ * rows (bf16 A and W, W input-major, float32 accumulation). K a multiple of
+ * 128, N of 64. ws: ax_linear_m64_workspace_bytes(K, N) bytes (float32 split
+ * partials), 256-byte aligned.
+ */
+size_t ax_linear_m64_workspace_bytes(int K, int N);
+int ax_linear_m64(const uint16_t* A, const uint16_t* W, int K, int N, uint16_t* C, void* ws,
+                  size_t ws_bytes, void* stream);
+
+/*
  * Measurement helper: dst[i] = src[i] for n 16-byte words, one plain
  * streaming copy kernel. Used to calibrate hardware byte counters against a
  * transfer of known size. Pointers 16-byte aligned.

@@ -194,3 +194,33 @@ def test_text_decode_validation_codes():
     assert call(eps=float("inf")) == ax.AX_E_ARG
     assert call(ws_bytes=8) == ax.AX_E_WORKSPACE
     assert call(ws=FAKE + 16) == ax.AX_E_WORKSPACE
+
+
+def test_expert_layer_workspace_and_validation_codes():
+    assert ax.expert_layer_workspace_bytes(4700, 8192) > ax.expert_attn_workspace_bytes(4700, 8192)
+    assert ax.expert_layer_workspace_bytes(193, 256) == 0
+    assert ax.linear_m64_workspace_bytes(1536, 4096) == 6 * 64 * 4096 * 4
+    assert ax.linear_m64_workspace_bytes(100, 64) == 0
+    assert ax.linear_m64_workspace_bytes(128, 96) == 0
+    f = ax.lib.ax_expert_layer
+    big = 1 << 30
+
+    def layer(**kw):
+        a = dict(x=FAKE, ln1=FAKE, wqkv=FAKE, qn=FAKE, kn=FAKE, wo=FAKE, ln2=FAKE, w1=FAKE, w3=FAKE, w2=FAKE,
+                 cos=FAKE, sin=FAKE, eps=1e-6, Kc=FAKE, Vc=FAKE, S=128, Smax=256, out=FAKE, ws=FAKE, ws_bytes=big)
+        a.update(kw)
+        return f(*a.values(), None)
+
+    assert layer(w2=None) == ax.AX_E_NULL
+    assert layer(out=None) == ax.AX_E_NULL
+    assert layer(S=193) == ax.AX_E_SHAPE
+    assert layer(eps=float("nan")) == ax.AX_E_ARG
+    assert layer(ws_bytes=16) == ax.AX_E_WORKSPACE
+    assert layer(ws=FAKE + 16) == ax.AX_E_WORKSPACE
+    assert layer() == ax.AX_E_UNSUPPORTED                      # valid arguments, no device here
+    g = ax.lib.ax_linear_m64
+    assert g(None, FAKE, 128, 64, FAKE, FAKE, big, None) == ax.AX_E_NULL
+    assert g(FAKE, FAKE, 100, 64, FAKE, FAKE, big, None) == ax.AX_E_SHAPE
+    assert g(FAKE, FAKE, 128, 96, FAKE, FAKE, big, None) == ax.AX_E_SHAPE
+    assert g(FAKE, FAKE, 128, 64, FAKE, FAKE, 16, None) == ax.AX_E_WORKSPACE
+    assert g(FAKE, FAKE, 128, 64, FAKE, FAKE, big, None) == ax.AX_E_UNSUPPORTED

@@ -1,0 +1,183 @@
+"""Parity of the whole expert decoder layer and of its M = 64 projection with the fp64 oracle,
+through the C ABI, on seeded inputs.
+
+Bars. A projection output is one bf16 rounding of a float32 sum of exact bf16 products, the
+oracle's one rounding of the float64 sum: within the float32 summation bound plus one rounding,
+and nearly all equal. The layer: PCC >= 0.9999 on x_out, the level the pages report for their
+device expert layer against their torch oracle (page code/alpamayo_tt/EXPERT_NOTES.md, section
+"Accuracy": 0.99993 to 0.999998 over the layers), relative L2 <= 1e-2, and elementwise |got - ref| <= 0.05 +
+2^-6 |ref| as a guard against a gross error in one element: the attention output already differs
+from the oracle's by up to 1e-2 (its bf16 probabilities), and each of the bf16 roundings
+after it (o, x2, n2, m, d, x_out; six in all) can fall the other way, moving an element by an ulp of up to
+2^-7 |value|. Cache rows outside the tail unchanged; the tail within two bf16 ulps of the
+oracle's plus the projection's float32 summation bound (its rows come through the projection's
+rounding), and nearly all bits equal.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from flow_matching_action_amd import synth
+
+from gpu_util import DEV, bf16_to_f64, down, metrics, say, up
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ax():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from flow_matching_action_amd import ax as lib
+    return lib
+
+
+def _bits_normal(rng, shape, scale=1.0):
+    return oracle.f64_to_bf16_bits(rng.standard_normal(shape) * scale)
+
+
+def _linear(ax, a_bits, w_bits):
+    K, N = w_bits.shape
+    A, W = up(a_bits), up(w_bits)
+    C = torch.zeros((64, N), dtype=torch.int16, device=DEV)
+    nb = ax.linear_m64_workspace_bytes(K, N)
+    assert nb > 0
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    ax.linear_m64(A, W, K, N, C, ws)
+    torch.cuda.synchronize()
+    return down(C)
+
+
+def _check_linear(got_bits, a_bits, w_bits, label):
+    a, w = bf16_to_f64(a_bits), bf16_to_f64(w_bits)
+    ref = a @ w
+    got = bf16_to_f64(got_bits)
+    ref_r = bf16_to_f64(oracle.f64_to_bf16_bits(ref))
+    # float32 sums of exact bf16 products: error at most K 2^-24 sum |a w| (a deterministic bound);
+    # then one bf16 rounding, at most 2^-8 of the value
+    acc = w.shape[0] * 2.0 ** -24 * (np.abs(a) @ np.abs(w))
+    bound = 2.0 ** -8 * (np.abs(ref) + acc) + acc
+    ratio = np.abs(got - ref) / bound
+    i = np.unravel_index(np.argmax(ratio), ratio.shape)
+    same = float(np.mean(got == ref_r))
+    print(f"{label}: equal to the rounded float64 product {same:.5f}, max_abs {np.abs(got - ref).max():.3e}, "
+          f"worst/bound {ratio[i]:.3f} at {i} (got {got[i]!r}, ref {ref[i]!r})", flush=True)
+    assert ratio.max() <= 1.0
+    assert same > 0.99
+
+
+@pytest.mark.parametrize("K,N", [(128, 64), (1536, 4096), (2048, 1536), (1536, 6144), (6144, 1536), (384, 192)])
+def test_linear_m64_matches_float64_product(ax, K, N):
+    rng = np.random.default_rng(K * 7 + N)
+    a = _bits_normal(rng, (64, K))
+    w = _bits_normal(rng, (K, N), 1.0 / np.sqrt(K))
+    say(f"linear_m64 K={K} N={N}")
+    _check_linear(_linear(ax, a, w), a, w, f"linear K={K} N={N}")
+
+
+def test_linear_m64_structure(ax):
+    # identity weights copy A (every column of the tile maps to its own output column), a single
+    # nonzero weight row picks one A column: a transposed operand or a swizzle slip fails these
+    rng = np.random.default_rng(3)
+    K = N = 256
+    a = _bits_normal(rng, (64, K))
+    eye = oracle.f64_to_bf16_bits(np.eye(K))
+    say("linear_m64 identity")
+    assert np.array_equal(_linear(ax, a, eye), a)
+    w = np.zeros((K, N))
+    w[37, :] = np.arange(N) + 1.0
+    got = bf16_to_f64(_linear(ax, a, oracle.f64_to_bf16_bits(w)))
+    ref = bf16_to_f64(oracle.f64_to_bf16_bits(bf16_to_f64(a)[:, 37:38] * (np.arange(N) + 1.0)[None, :]))
+    assert np.array_equal(got, ref)
+
+
+def test_linear_m64_rejects_bad_shapes(ax):
+    x = torch.zeros(64 * 256, dtype=torch.int16, device=DEV)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=DEV)
+    for K, N in ((100, 64), (128, 96), (0, 64)):
+        with pytest.raises(RuntimeError):
+            ax.linear_m64(x, x, K, N, x, ws)
+
+
+class LayerBufs:
+    def __init__(self, ax, w, x, cache, S, Smax):
+        self.S, self.Smax = S, Smax
+        self.w = {k: up(v) for k, v in w.items()}
+        self.x = up(x)
+        self.Kc, self.Vc = up(cache["Kc"]), up(cache["Vc"])
+        cos, sin = ax.rope_tables(S)
+        self.cos = torch.from_numpy(cos).to(DEV)
+        self.sin = torch.from_numpy(sin).to(DEV)
+        self.out = torch.zeros((64, 1536), dtype=torch.int16, device=DEV)
+        nb = ax.expert_layer_workspace_bytes(S, Smax)
+        assert nb > 0
+        self.ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+        assert self.ws.data_ptr() % 256 == 0
+
+    def run(self, ax):
+        w = self.w
+        ax.expert_layer(self.x, w["ln1"], w["wqkv"], w["qn"], w["kn"], w["wo"], w["ln2"], w["w1"], w["w3"], w["w2"],
+                        self.cos, self.sin, 1e-6, self.Kc, self.Vc, self.S, self.Smax, self.out, self.ws)
+
+
+def _ref(w, x, cache, S, Smax):
+    return oracle.expert_layer(x, w["ln1"], w["wqkv"], w["qn"], w["kn"], w["wo"], w["ln2"], w["w1"], w["w3"],
+                               w["w2"], cache["Kc"], cache["Vc"], S, Smax)
+
+
+def _check_layer(b, ref, cache, label):
+    got = bf16_to_f64(down(b.out))
+    r = ref["x_out"]
+    m = metrics(got, r)
+    ratio = np.abs(got - r) / (0.05 + 2.0 ** -6 * np.abs(r))
+    i = np.unravel_index(np.argmax(ratio), ratio.shape)
+    print(f"{label}: max_abs={m['max_abs']:.3e} pcc={m['pcc']:.7f} rel_l2={m['rel_l2']:.3e} "
+          f"equal={np.mean(got == r):.4f} worst/bound={ratio[i]:.3f} (got {got[i]!r}, ref {r[i]!r})", flush=True)
+    assert ratio.max() <= 1.0, m
+    assert m["pcc"] >= 0.9999, m
+    assert m["rel_l2"] <= 1e-2, m
+    Smax = b.Smax
+    for name, t in (("Kc", b.Kc), ("Vc", b.Vc)):
+        c = down(t)
+        assert np.array_equal(c[:, :Smax - 64], cache[name][:, :Smax - 64]), name
+        tail, rt = bf16_to_f64(c[:, Smax - 64:]), ref[name + "_new"][:, Smax - 64:]
+        rtf = bf16_to_f64(rt)
+        # the float32 sum over the 1536 qkv inputs may be off by up to 1536 2^-24 sum |n1 w| (~2e-3
+        # here) before its rounding, which matters for values near zero; a k element whose rounding
+        # fell the other way reaches its rotate_half partner (d +- 64) through RoPE
+        part = np.roll(rtf, 64, axis=-1) if name == "Kc" else 0.0
+        assert (np.abs(tail - rtf) <= 2.0 ** -6 * (np.abs(rtf) + np.abs(part)) + 2e-3).all(), name
+        same = float(np.mean(c[:, Smax - 64:] == rt))
+        print(f"  {name} tail bits equal: {same:.5f}", flush=True)
+        assert same > 0.98, name
+
+
+@pytest.mark.parametrize("S,Smax,seed", [(128, 256, 1), (0, 64, 2), (1000, 1100, 3)])
+def test_expert_layer_matches_oracle(ax, S, Smax, seed):
+    w = synth.layer_weights(100 + seed)
+    x = synth.residual_inputs(200 + seed)
+    cache = synth.layer_inputs(Smax, S, 300 + seed)
+    say(f"expert_layer S={S} Smax={Smax} seed={seed}")
+    b = LayerBufs(ax, w, x, cache, S, Smax)
+    b.run(ax)
+    torch.cuda.synchronize()
+    _check_layer(b, _ref(w, x, cache, S, Smax), cache, f"layer S={S} Smax={Smax}")
+
+
+def test_expert_layer_headline_shape(ax):
+    S, Smax = 4700, 8192
+    w = synth.layer_weights(11)
+    x = synth.residual_inputs(12)
+    cache = synth.layer_inputs(Smax, S, 13)
+    say(f"expert_layer S={S} Smax={Smax}")
+    b = LayerBufs(ax, w, x, cache, S, Smax)
+    b.run(ax)
+    torch.cuda.synchronize()
+    _check_layer(b, _ref(w, x, cache, S, Smax), cache, "layer headline")
+    # a second call on the updated cache and the same input: the tail is rewritten with the
+    # same rows, so the output repeats bit for bit
+    first = down(b.out).copy()
+    b.run(ax)
+    torch.cuda.synchronize()
+    assert np.array_equal(down(b.out), first)
