@@ -195,7 +195,14 @@ class RotatingLayer:
         from flow_matching_action_amd import synth
         dev = "cuda:0"
         self.ax, self.wl = ax, wl
-        self.w = [synth.device_layer_weights(l, dev) for l in range(wl.n_layers)]
+        self.w = []
+        for l in range(wl.n_layers):
+            w = synth.device_layer_weights(l, dev)
+            for name in ("wqkv", "wo", "w1", "w3", "w2"):    # the projections' packed layout, once
+                p = torch.empty_like(w[name])
+                ax.pack_weight_m64(w[name], w[name].shape[0], w[name].shape[1], p)
+                w[name] = p
+            self.w.append(w)
         g = torch.Generator(device=dev)
         g.manual_seed(11000)
         x0 = torch.randn((64, 1536), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)

@@ -90,6 +90,8 @@ lib.ax_expert_layer_workspace_bytes.restype = ctypes.c_size_t
 lib.ax_expert_layer_workspace_bytes.argtypes = [_I, _I]
 lib.ax_expert_layer.restype = _I
 lib.ax_expert_layer.argtypes = [_P] * 12 + [ctypes.c_float, _P, _P, _I, _I, _P, _P, ctypes.c_size_t, _P]
+lib.ax_pack_weight_m64.restype = _I
+lib.ax_pack_weight_m64.argtypes = [_P, _I, _I, _P, _P]
 lib.ax_linear_m64_workspace_bytes.restype = ctypes.c_size_t
 lib.ax_linear_m64_workspace_bytes.argtypes = [_I, _I]
 lib.ax_linear_m64.restype = _I
@@ -103,7 +105,8 @@ EXPORTS = ("ax_abi_version", "ax_strerror", "ax_rope_tables", "ax_qk_norm_rope",
            "ax_expert_attn_fp8_workspace_bytes", "ax_cache_tail_write_fp8", "ax_expert_attn_fp8",
            "ax_expert_layer_attn_fp8", "ax_expert_layer_attn_fp8_split", "ax_expert_attn_fp8_combine",
            "ax_text_decode_workspace_bytes", "ax_text_decode_attn", "ax_expert_layer_workspace_bytes",
-           "ax_expert_layer", "ax_linear_m64_workspace_bytes", "ax_linear_m64", "ax_copy_words")
+           "ax_expert_layer", "ax_pack_weight_m64", "ax_linear_m64_workspace_bytes", "ax_linear_m64",
+           "ax_copy_words")
 
 
 def _check(fn: str, code: int) -> None:
@@ -256,6 +259,10 @@ def expert_layer(x_in, ln1, wqkv, q_norm_w, k_norm_w, wo, ln2, w1, w3, w2, rope_
         _ptr(x_in), _ptr(ln1), _ptr(wqkv), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(wo), _ptr(ln2), _ptr(w1), _ptr(w3),
         _ptr(w2), _ptr(rope_cos), _ptr(rope_sin), float(eps), _ptr(Kc), _ptr(Vc), int(S), int(Smax), _ptr(x_out),
         _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def pack_weight_m64(W, K: int, N: int, W_packed, stream=None):
+    _check("ax_pack_weight_m64", lib.ax_pack_weight_m64(_ptr(W), int(K), int(N), _ptr(W_packed), _stream(stream)))
 
 
 def linear_m64_workspace_bytes(K: int, N: int) -> int:

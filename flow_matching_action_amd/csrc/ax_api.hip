@@ -289,6 +289,14 @@ int ax_text_decode_attn(const uint16_t* q_in, const uint16_t* k_in, const uint16
 
 // ---- the whole expert layer ------------------------------------------------------------------------
 
+int ax_pack_weight_m64(const uint16_t* W, int K, int N, uint16_t* W_packed, void* stream) {
+  int r = check_ptrs({W, W_packed});
+  if (r == AX_OK && (!ax::gemm64_shape_ok(K, N) || K > (1 << 20) || N > (1 << 20))) r = AX_E_SHAPE;
+  if (r == AX_OK) r = check_device();
+  if (r != AX_OK) return r;
+  return status(ax::launch_pack_w64(W, K, N, W_packed, as_stream(stream)));
+}
+
 size_t ax_linear_m64_workspace_bytes(int K, int N) {
   return ax::gemm64_shape_ok(K, N) ? ax::gemm64_partials_bytes(K, N) : 0;
 }

@@ -120,7 +120,7 @@ constexpr int kLayerMlp = 6144;
 struct LayerLaunch {
   const uint16_t* x;      // [64][1536]
   const uint16_t* ln1;    // [1536]
-  const uint16_t* wqkv;   // [1536][4096]
+  const uint16_t* wqkv;   // [1536][4096], packed (launch_pack_w64) like the other four matrices
   const uint16_t* qn;     // [128]
   const uint16_t* kn;
   const uint16_t* wo;     // [2048][1536]
@@ -139,8 +139,10 @@ struct LayerLaunch {
 };
 size_t layer_workspace_bytes(int S, int Smax);
 hipError_t launch_layer(const LayerLaunch& p, hipStream_t st);
-// C[64][N] = bf16(A[64][K] W[K][N]) (W input-major); ws: gemm64_partials_bytes(K, N) bytes.
+// C[64][N] = bf16(A[64][K] W[K][N]) (W input-major, packed); ws: gemm64_partials_bytes(K, N) bytes.
 bool gemm64_shape_ok(int K, int N);
+// Weights into the packed layout the projection kernel streams (K x N elements, same size).
+hipError_t launch_pack_w64(const uint16_t* W, int K, int N, uint16_t* Wp, hipStream_t st);
 size_t gemm64_partials_bytes(int K, int N);
 hipError_t launch_linear64(const uint16_t* A, const uint16_t* W, int K, int N, uint16_t* C, void* ws,
                            hipStream_t st);

@@ -16,22 +16,39 @@
 //   float32 partial goes to the workspace.
 // - k_gemm_reduce: sums the splits in a fixed order and applies the op's epilogue: the head
 //   split of qkv into q/k/v [heads][64][128], the residual add (o + x, d + x2), or SiLU(g) * u.
-// - k_rmsnorm_rows: one workgroup per token row.
+// - k_rmsnorm_rows: one workgroup per token row; k_reduce_residual_norm: the o projection's
+//   split sum and residual add followed by the second norm, in one pass per row.
 #include "ax_attn_common.h"
 #include "ax_launch.h"
 
 namespace ax {
 
 constexpr int kGemmM = 64;      // token rows
-constexpr int kGemmNT = 64;     // output columns per workgroup
-constexpr int kGemmThreads = 256;
+constexpr int kNBlk = 32;       // columns of one weight block (the matrix-core tile's n)
+constexpr int kMaxSplit = 256;
 
-// W tile rows are 128 bytes (64 columns): chunk c of row k holds columns 8c' .. 8c'+7 with
-// c' = c ^ wswz(k); the transpose read of a 16-lane group takes rows r .. r+3 at one chunk pair.
-__device__ __forceinline__ int wswz(int k) { return 2 * (k & 3); }
-// A tile rows are KC x 2 bytes: within each aligned group of 8 chunks, chunk c holds chunk
-// c ^ (m & 7), so the 32 rows a k-step reads at one column spread over 8 bank groups.
-__device__ __forceinline__ int aswz(int c, int m) { return (c & ~7) | ((c & 7) ^ (m & 7)); }
+// Packed weight layout. W [K][N] (input-major) is stored as 1 KB blocks, one per (32-column block
+// j, 16-row step s), at block index j * (K / 16) + s: a column block's steps are consecutive. In a
+// block, the 16 bytes of lane l are W[16 s + 8 (l / 32) + e][32 j + l % 32], e = 0..7: exactly
+// the W^T operand lane l hands v_mfma_f32_32x32x16_bf16, so one plain 16-byte load per lane
+// fetches an operand, with no transpose and no LDS.
+__global__ __launch_bounds__(256) void k_pack_w64(const uint16_t* W, int K, int N, uint16_t* Wp) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;  // 16-byte chunk of the packed layout
+  const long long b = i >> 6;
+  const int l = (int)(i & 63);
+  const int steps = K / 16;
+  const int j = (int)(b / steps), s = (int)(b % steps);
+  const uint16_t* src = W + (long long)(16 * s + 8 * (l >> 5)) * N + kNBlk * j + (l & 31);
+  uint16_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = src[(long long)e * N];
+  u32x4 o;
+  o[0] = v[0] | (uint32_t)v[1] << 16;
+  o[1] = v[2] | (uint32_t)v[3] << 16;
+  o[2] = v[4] | (uint32_t)v[5] << 16;
+  o[3] = v[6] | (uint32_t)v[7] << 16;
+  *reinterpret_cast<u32x4*>(Wp + i * 8) = o;
+}
 
 // A element (m, k): row-major [64][lda], or (heads = true) the attention output [16][64][128]
 // read as its heads concatenated ([64][2048]: column 128 h + d of row m is head h, token m,
@@ -40,122 +57,199 @@ __device__ __forceinline__ const uint16_t* a_elem(const uint16_t* A, int lda, in
   return heads ? A + ((long long)(k >> 7) * kGemmM + m) * 128 + (k & 127) : A + (long long)m * lda + k;
 }
 
-template <int KC, bool HEADS>
-__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm64(const uint16_t* A, int lda, const uint16_t* W, int N,
-                                                          float* part) {
-  static_assert(KC % 64 == 0 && KC <= 512, "k chunk");
-  __shared__ __attribute__((aligned(16))) uint8_t wt[KC * kGemmNT * 2];
-  __shared__ __attribute__((aligned(16))) uint8_t at[kGemmM * KC * 2];
+// A slice rows in LDS are KC x 2 bytes; chunk c of row m sits at position c ^ (m & 15) (within its
+// aligned group of 16 chunks), so the 16 rows a 16-lane group reads at one chunk hit 16 distinct
+// 16-byte bank groups.
+__device__ __forceinline__ int aswz(int c, int m) { return c ^ (m & 15); }
+
+// One split of C = A W over NB column blocks of 32. The workgroup has NB x KW waves: wave (nb, kq)
+// streams column block nb over its KW-th share of the split's KC = KW x STEPS x 16 rows, straight
+// into registers (STEPS 1 KB loads per wave, all issued at the start and consumed in order), while
+// the split's 64 x KC slice of A sits in LDS (loaded first, from L2, through registers: a
+// direct-to-LDS load would make the compiler drain the whole weight stream before the first LDS
+// read). Each wave makes
+// C^T[32 n][64 m] with two matrix-core products per step (m halves); the KW waves of a column block
+// then add their tiles in LDS in kq order and the first stores the float32 partial. W0 holds
+// blocks [0, nblk0), W1 (if not null) the next nblk0, written to partial columns N .. 2N - 1.
+template <int NB, int KW, int STEPS, bool HEADS>
+__global__ __launch_bounds__(64 * NB * KW) void k_gemm64(const uint16_t* A, int lda, const uint16_t* W0,
+                                                       const uint16_t* W1, int K, int N, int n_tiles,
+                                                       float* part) {
+  constexpr int kThreads = 64 * NB * KW;
+  constexpr int KC = KW * STEPS * 16;
+  constexpr int kCpr = KC / 8;                     // 16-byte chunks per A row
+  static_assert(kCpr % 16 == 0, "A rows of at least 16 chunks");
+  constexpr int kALoads = kGemmM * kCpr / 64;      // 1 KB loads of the A slice
+  static_assert(kALoads % (NB * KW) == 0, "A slice split evenly over the waves");
+  constexpr int kRedBytes = (KW - 1) * NB * 64 * 32 * 4;
+  constexpr int kLds = kGemmM * KC * 2 > kRedBytes ? kGemmM * KC * 2 : kRedBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int n_tiles = N / kGemmNT;
+  const int nb = wave % NB;
+  const int kq = wave / NB;
   const int tile = blockIdx.x % n_tiles;
   const int split = blockIdx.x / n_tiles;
-  const int n0 = tile * kGemmNT;
   const int k0 = split * KC;
 
-  // weight tile: KC rows of 128 bytes, 8 rows per 1 KB load (lane l: row 8i + l / 8, chunk l % 8)
-  constexpr int kWLoads = KC / 8;
-  static_for<kWLoads / 4>([&](auto ic) {
-    constexpr int i0 = decltype(ic)::value;
-    const int i = 4 * i0 + wave;
-    const int k = 8 * i + (lane >> 3);
-    const int c = (lane & 7) ^ wswz(k);
-    __builtin_amdgcn_global_load_lds(W + (long long)(k0 + k) * N + n0 + 8 * c, (lds_void*)(wt + i * 1024), 16, 0,
-                                     kNonTemporal);
-  });
-  // A slice: 64 rows of KC x 2 bytes (KC / 8 chunks per row), 1 KB per load
-  constexpr int kCpr = KC / 8;
-  constexpr int kALoads = kGemmM * kCpr / 64;
-  static_for<kALoads / 4>([&](auto ic) {
-    constexpr int i0 = decltype(ic)::value;
-    const int i = 4 * i0 + wave;
-    const int e = 64 * i + lane;      // chunk index in the tile
+  // the A slice first (plain loads into registers; stored to LDS once the weight loads are out):
+  // chunk e of the slice, row m = e / kCpr, position e % kCpr, holds chunk aswz(e % kCpr, m)
+  constexpr int kAPer = kALoads / (NB * KW);
+  u32x4 av[kAPer];
+#pragma unroll
+  for (int j = 0; j < kAPer; ++j) {
+    const int e = 64 * (j * (NB * KW) + wave) + lane;
     const int m = e / kCpr;
-    const int c = aswz(e % kCpr, m);  // the A chunk that lands at this position
-    __builtin_amdgcn_global_load_lds(a_elem(A, lda, m, k0 + 8 * c, HEADS), (lds_void*)(at + i * 1024), 16, 0, 0);
-  });
-  wait_vmcnt<0>();
-  lds_barrier();
-
-  // wave w: C^T tile (n-sub t = w & 1: columns 32t .. 32t+31) x (m-sub = w >> 1: rows 32ms .. +31)
-  const int t = wave & 1;
-  const int ms = wave >> 1;
-  const int G = lane >> 4, li = lane & 15;
-  const int wrow0 = 8 * (G >> 1) + (li >> 2);                  // + 4 hf + 16 kstep
-  const int wx = 4 * t + 2 * (G & 1) + ((li & 3) >> 1);        // chunk before the swizzle
-  const int woff = wrow0 * 128 + 16 * (wx ^ wswz(wrow0)) + 8 * (li & 1);
-  const int am = 32 * ms + (lane & 31);                         // A row of this lane's B operand
-  const int ah = lane >> 5;
-  f32x16 acc;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-#pragma unroll 4
-  for (int ks = 0; ks < KC / 16; ++ks) {
-    // A operand: W^T rows n = 32t + lane % 32, k = 16 ks + 8 (lane / 32) .. +7 (swizzle depends on k & 3 only)
-    const v4i16 w0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(wt + (16 * ks) * 128 + woff));
-    const v4i16 w1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(wt + (16 * ks + 4) * 128 + woff));
-    const v4i16 both[2] = {w0, w1};
-    bf16x8 wf;
-    __builtin_memcpy(&wf, both, 16);
-    // B operand: A^T, row am, k = 16 ks + 8 ah .. +7
-    const int c = 2 * ks + ah;
-    const bf16x8 af = *reinterpret_cast<const bf16x8*>(at + am * (KC * 2) + 16 * aswz(c, am));
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, af, acc, 0, 0, 0);
+    const int c = aswz(e % kCpr, m);
+    av[j] = *reinterpret_cast<const u32x4*>(a_elem(A, lda, m, k0 + 8 * c, HEADS));
   }
-  // lane (m = lane % 32, h) holds C rows 32 ms + m, columns 32t + 8a + 4h + (0..3), a = 0..3
-  float* dst = part + ((long long)split * kGemmM + am) * N + n0 + 32 * t + 4 * ah;
+  __builtin_amdgcn_sched_barrier(0);
+  // then every weight operand of this wave, from a wave-uniform base
+  const int nblk0 = W1 ? n_tiles * NB / 2 : n_tiles * NB;
+  const int jb = tile * NB + nb;  // column block over W0 then W1
+  const uint16_t* W = jb < nblk0 ? W0 : W1;
+  const int jl = jb < nblk0 ? jb : jb - nblk0;
+  const u32x4* wsrc = reinterpret_cast<const u32x4*>(W) + ((long long)jl * (K / 16) + k0 / 16 + kq * STEPS) * 64;
+  u32x4 wv[STEPS];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-    __builtin_nontemporal_store(f32x4{acc[4 * a], acc[4 * a + 1], acc[4 * a + 2], acc[4 * a + 3]},
-                                reinterpret_cast<f32x4*>(dst + 8 * a));
+  for (int s = 0; s < STEPS; ++s) wv[s] = __builtin_nontemporal_load(wsrc + s * 64 + lane);
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4* alds = reinterpret_cast<u32x4*>(lds);
+#pragma unroll
+  for (int j = 0; j < kAPer; ++j) alds[64 * (j * (NB * KW) + wave) + lane] = av[j];
+  __syncthreads();
+
+  f32x16 acc[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[h][i] = 0.f;
+  const int am0 = lane & 31;
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+    const int c = 2 * (kq * STEPS + s) + (lane >> 5);
+    bf16x8 wf;
+    __builtin_memcpy(&wf, &wv[s], 16);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int m = 32 * h + am0;
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(lds + m * (KC * 2) + 16 * aswz(c, m));
+      acc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, af, acc[h], 0, 0, 0);
+    }
+  }
+
+  // the KW waves of column block nb add their tiles in kq order
+  if constexpr (KW > 1) {
+    __syncthreads();  // every wave is done with the A slice; its LDS now holds the tiles
+    f32x4* red = reinterpret_cast<f32x4*>(lds);
+    if (kq > 0) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          red[(((kq - 1) * NB + nb) * 8 + 4 * h + a) * 64 + lane] =
+              f32x4{acc[h][4 * a], acc[h][4 * a + 1], acc[h][4 * a + 2], acc[h][4 * a + 3]};
+    }
+    __syncthreads();
+    if (kq > 0) return;
+#pragma unroll
+    for (int q = 1; q < KW; ++q)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 v = red[(((q - 1) * NB + nb) * 8 + 4 * h + a) * 64 + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[h][4 * a + e] += v[e];
+        }
+  }
+  // lane (m = lane % 32, g = lane / 32) holds C rows 32 h + m, columns 32 jb + 8a + 4g + (0..3)
+  const int pld = W1 ? 2 * N : N;
+  const int pcol = kNBlk * jb + 4 * (lane >> 5);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float* dst = part + ((long long)split * kGemmM + 32 * h + am0) * pld + pcol;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      __builtin_nontemporal_store(f32x4{acc[h][4 * a], acc[h][4 * a + 1], acc[h][4 * a + 2], acc[h][4 * a + 3]},
+                                  reinterpret_cast<f32x4*>(dst + 8 * a));
+  }
 }
 
 enum GemmEpilogue { kEpiStore = 0, kEpiQkvSplit = 1, kEpiResidual = 2, kEpiSwiGlu = 3 };
 
-// Sum of the splits of C[64, N] in split order, then the epilogue; thread = 4 consecutive columns.
-// kEpiStore: out[m][n] = bf16(C); kEpiQkvSplit: bf16(C) into q / k / v [heads][64][128] (columns
-// 0..2047 q heads, 2048..3071 k heads, 3072..4095 v heads); kEpiResidual: out = bf16(res +
-// bf16(C)); kEpiSwiGlu: C and C2 are x w1 and x w3, out = bf16(bf16(silu(C)) * bf16(C2)).
-template <int EPI>
-__global__ __launch_bounds__(256) void k_gemm_reduce(const float* part, const float* part2, int n_split, int N,
-                                                     const uint16_t* res, uint16_t* out, uint16_t* out_k,
-                                                     uint16_t* out_v) {
-  const int i = blockIdx.x * 256 + threadIdx.x;  // quad index
-  if (i >= kGemmM * N / 4) return;
-  const int m = (4 * i) / N;
-  const int n = (4 * i) % N;
-  const long long stride = (long long)kGemmM * N / 4;
-  const f32x4* p = reinterpret_cast<const f32x4*>(part) + i;
-  f32x4 s = p[0];
-  for (int c = 1; c < n_split; ++c) {
-    const f32x4 v = p[c * stride];
-    s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
-  }
-  float r[4];
-  if constexpr (EPI == kEpiSwiGlu) {
-    const f32x4* p2 = reinterpret_cast<const f32x4*>(part2) + i;
-    f32x4 s2 = p2[0];
-    for (int c = 1; c < n_split; ++c) {
-      const f32x4 v = p2[c * stride];
-      s2[0] += v[0]; s2[1] += v[1]; s2[2] += v[2]; s2[3] += v[3];
+// Sum of the splits of C[64, N], then the epilogue. A workgroup covers one row and 256 columns: thread (g, q) sums splits g, g + 4, ... of columns 4q .. 4q + 3 (eight loads in
+// flight), and group 0 adds the four group sums in group order, so the result does not depend on
+// timing. kEpiStore: out[m][n] = bf16(C); kEpiQkvSplit: bf16(C) into q / k / v [heads][64][128]
+// (columns 0..2047 q heads, 2048..3071 k heads, 3072..4095 v heads); kEpiResidual: out =
+// bf16(res + bf16(C)); kEpiSwiGlu: partial columns n and N + n are x w1 and x w3, out =
+// bf16(bf16(silu(C1)) * bf16(C3)).
+constexpr int kRedGroups = 4, kRedBatch = 8;
+
+__device__ __forceinline__ f32x4 split_sum(const f32x4* p, long long stride, int g, int n_split) {
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = g; c0 < n_split; c0 += kRedGroups * kRedBatch) {
+    f32x4 v[kRedBatch];
+#pragma unroll
+    for (int b = 0; b < kRedBatch; ++b) {
+      const int c = c0 + kRedGroups * b;
+      v[b] = c < n_split ? p[c * stride] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
+    for (int b = 0; b < kRedBatch; ++b) {
+      s[0] += v[b][0]; s[1] += v[b][1]; s[2] += v[b][2]; s[3] += v[b][3];
+    }
+  }
+  return s;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_reduce(const float* part, int n_split, int N, const uint16_t* res,
+                                                     uint16_t* out, uint16_t* out_k, uint16_t* out_v) {
+  constexpr int kSets = EPI == kEpiSwiGlu ? 2 : 1;
+  __shared__ f32x4 red[kSets][kRedGroups - 1][64];
+  const int g = threadIdx.x >> 6;
+  const int q = threadIdx.x & 63;
+  const int m = blockIdx.x % kGemmM;
+  const int n = (blockIdx.x / kGemmM) * 256 + 4 * q;
+  const int pld = kSets * N;
+  const long long stride = (long long)kGemmM * pld / 4;  // float4s per split
+  const bool live = n < N;  // the last block of a width that is not a multiple of 256
+  const f32x4* p = reinterpret_cast<const f32x4*>(part + (long long)m * pld + (live ? n : 0));
+  f32x4 s[kSets];
+  s[0] = split_sum(p, stride, g, live ? n_split : 0);
+  if constexpr (kSets == 2) s[1] = split_sum(p + N / 4, stride, g, live ? n_split : 0);
+  if (g > 0) {
+#pragma unroll
+    for (int j = 0; j < kSets; ++j) red[j][g - 1][q] = s[j];
+  }
+  __syncthreads();
+  if (g > 0 || !live) return;
+#pragma unroll
+  for (int j = 0; j < kSets; ++j)
+#pragma unroll
+    for (int k = 0; k < kRedGroups - 1; ++k) {
+      const f32x4 v = red[j][k][q];
+      s[j][0] += v[0]; s[j][1] += v[1]; s[j][2] += v[2]; s[j][3] += v[3];
+    }
+  float r[4];
+  if constexpr (EPI == kEpiSwiGlu) {
+#pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float g = bf16_to_f32(f32_to_bf16(s[e] / (1.0f + __expf(-s[e]))));
-      const float u = bf16_to_f32(f32_to_bf16(s2[e]));
-      r[e] = g * u;
+      const float gv = bf16_to_f32(f32_to_bf16(s[0][e] / (1.0f + __expf(-s[0][e]))));
+      const float uv = bf16_to_f32(f32_to_bf16(s[1][e]));
+      r[e] = gv * uv;
     }
   } else if constexpr (EPI == kEpiResidual) {
     const uint2 rr = *reinterpret_cast<const uint2*>(res + (long long)m * N + n);
     const float x[4] = {bf16_to_f32(rr.x & 0xffffu), bf16_to_f32(rr.x >> 16), bf16_to_f32(rr.y & 0xffffu),
                         bf16_to_f32(rr.y >> 16)};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] = x[e] + bf16_to_f32(f32_to_bf16(s[e]));
+    for (int e = 0; e < 4; ++e) r[e] = x[e] + bf16_to_f32(f32_to_bf16(s[0][e]));
   } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] = s[e];
+    for (int e = 0; e < 4; ++e) r[e] = s[0][e];
   }
   const uint2 o2 = make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
   uint16_t* dst;
@@ -203,55 +297,128 @@ __global__ __launch_bounds__(256) void k_rmsnorm_rows(const uint16_t* x, const u
   *reinterpret_cast<u32x4*>(out + (long long)m * width + 8 * t) = pack8v(o);
 }
 
+// The o projection's epilogue and the second residual norm in one pass, one workgroup per row:
+// x2[m] = bf16(x[m] + bf16(sum of the splits of C[m])) and n2[m] = bf16(gamma * x2[m] /
+// sqrt(mean(x2[m]^2) + eps)) (the same arithmetic as k_gemm_reduce's residual epilogue followed by
+// k_rmsnorm_rows). 8 columns per thread, width = 8 x blockDim; all split loads of a thread are
+// issued before any is added.
+template <int NSPLIT>
+__global__ __launch_bounds__(256) void k_reduce_residual_norm(const float* part, const uint16_t* x,
+                                                              const uint16_t* gamma, float eps, int width,
+                                                              uint16_t* x2, uint16_t* n2) {
+  __shared__ float red[8];
+  const int m = blockIdx.x;
+  const int t = threadIdx.x;
+  const long long row = (long long)m * width + 8 * t;
+  const f32x4* p = reinterpret_cast<const f32x4*>(part + row);
+  const long long stride = (long long)kGemmM * width / 4;
+  f32x4 v[NSPLIT][2];
+#pragma unroll
+  for (int c = 0; c < NSPLIT; ++c) {
+    v[c][0] = p[c * stride];
+    v[c][1] = p[c * stride + 1];
+  }
+  float xr[8], g[8], o[8];
+  unpack8v(*reinterpret_cast<const u32x4*>(x + row), xr);
+  unpack8v(*reinterpret_cast<const u32x4*>(gamma + 8 * t), g);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float sum = v[0][e >> 2][e & 3];
+#pragma unroll
+    for (int c = 1; c < NSPLIT; ++c) sum += v[c][e >> 2][e & 3];
+    o[e] = bf16_to_f32(f32_to_bf16(xr[e] + bf16_to_f32(f32_to_bf16(sum))));  // x2, as stored
+    ss += o[e] * o[e];
+  }
+  *reinterpret_cast<u32x4*>(x2 + row) = pack8v(o);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  if ((t & 63) == 0) red[t >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += red[w];
+  const float inv = 1.0f / sqrtf(tot / (float)width + eps);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = o[e] * inv * g[e];
+  *reinterpret_cast<u32x4*>(n2 + row) = pack8v(o);
+}
+
 // ---- host side -----------------------------------------------------------------------------------
 
-// K chunk per workgroup: the largest of 512, 256, 128 that divides K and leaves at least 256
-// workgroups, else the one with the most workgroups.
-static int gemm_kc(int K, int N) {
-  const int tiles = N / kGemmNT;
-  int best = 0;
-  for (int kc : {512, 256, 128})
-    if (K % kc == 0 && tiles * (K / kc) >= 256) return kc;
-  for (int kc : {128, 256, 512})
-    if (K % kc == 0) { best = kc; break; }
-  return best;
+// Projection shapes. A configuration is (NB column blocks, KW waves along k, STEPS 16-row steps per
+// wave); a split then covers KC = 16 KW STEPS rows and the grid is (N / (32 NB)) x (K / KC).
+struct GemmCfg {
+  int nb, kw, steps;
+};
+// the layer's four projections, each the fastest of a sweep over configurations on the cold-weight
+// workload: qkv 64 x 4 = 256 workgroups of 2 waves, o 48 x 4 = 192 of 4, gate/up 96 x 2 = 192 of 8,
+// down 24 x 8 = 192 of 4
+constexpr GemmCfg kCfgQkv{2, 1, 24}, kCfgO{1, 4, 8}, kCfgGateUp{4, 2, 24}, kCfgDown{2, 2, 24};
+// any other shape: 4 waves along k over one column block, the most rows per wave that still gives
+// 256 workgroups (else the fewest)
+static GemmCfg gemm_cfg_generic(int K, int N) {
+  for (int st : {12, 8, 6, 4, 2}) {
+    const int kc = 64 * st;
+    if (K % kc == 0 && K / kc <= kMaxSplit && (N / kNBlk) * (K / kc) >= 256) return {1, 4, st};
+  }
+  return (K % 128 == 0 && K / 128 <= kMaxSplit) ? GemmCfg{1, 4, 2} : GemmCfg{0, 0, 0};
+}
+static int gemm_splits(const GemmCfg& c, int K) { return K / (16 * c.kw * c.steps); }
+
+bool gemm64_shape_ok(int K, int N) {
+  return K > 0 && N > 0 && N % 64 == 0 && K % 128 == 0 && gemm_cfg_generic(K, N).nb > 0;
 }
 
 size_t gemm64_partials_bytes(int K, int N) {
-  const int kc = gemm_kc(K, N);
-  if (kc == 0) return 0;
-  return (size_t)(K / kc) * kGemmM * N * 4;
+  const GemmCfg c = gemm_cfg_generic(K, N);
+  if (c.nb == 0) return 0;
+  return (size_t)gemm_splits(c, K) * kGemmM * N * 4;
 }
 
-bool gemm64_shape_ok(int K, int N) { return K > 0 && N > 0 && N % kGemmNT == 0 && K % 128 == 0; }
+template <int NB, int KW, int STEPS, bool HEADS>
+static void launch_gemm_cfg(const uint16_t* A, int lda, const uint16_t* W0, const uint16_t* W1, int K, int N,
+                            float* part, hipStream_t st) {
+  const int tiles = (W1 ? 2 : 1) * (N / kNBlk) / NB;
+  const int splits = K / (16 * KW * STEPS);
+  hipLaunchKernelGGL((k_gemm64<NB, KW, STEPS, HEADS>), dim3(tiles * splits), dim3(64 * NB * KW), 0, st, A, lda, W0,
+                     W1, K, N, tiles, part);
+}
 
-template <bool HEADS>
-static hipError_t launch_gemm(const uint16_t* A, int lda, const uint16_t* W, int K, int N, float* part,
-                              hipStream_t st, int* n_split) {
-  const int kc = gemm_kc(K, N);
-  *n_split = K / kc;
-  const dim3 grid((N / kGemmNT) * (K / kc));
-  if (kc == 512) hipLaunchKernelGGL((k_gemm64<512, HEADS>), grid, dim3(kGemmThreads), 0, st, A, lda, W, N, part);
-  else if (kc == 256) hipLaunchKernelGGL((k_gemm64<256, HEADS>), grid, dim3(kGemmThreads), 0, st, A, lda, W, N, part);
-  else hipLaunchKernelGGL((k_gemm64<128, HEADS>), grid, dim3(kGemmThreads), 0, st, A, lda, W, N, part);
+static hipError_t launch_gemm_generic(const uint16_t* A, const uint16_t* W, int K, int N, float* part,
+                                      hipStream_t st, int* n_split) {
+  const GemmCfg c = gemm_cfg_generic(K, N);
+  *n_split = gemm_splits(c, K);
+  switch (c.steps) {
+    case 12: launch_gemm_cfg<1, 4, 12, false>(A, K, W, nullptr, K, N, part, st); break;
+    case 8: launch_gemm_cfg<1, 4, 8, false>(A, K, W, nullptr, K, N, part, st); break;
+    case 6: launch_gemm_cfg<1, 4, 6, false>(A, K, W, nullptr, K, N, part, st); break;
+    case 4: launch_gemm_cfg<1, 4, 4, false>(A, K, W, nullptr, K, N, part, st); break;
+    case 2: launch_gemm_cfg<1, 4, 2, false>(A, K, W, nullptr, K, N, part, st); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 template <int EPI>
-static hipError_t launch_reduce(const float* part, const float* part2, int n_split, int N, const uint16_t* res,
-                                uint16_t* out, uint16_t* out_k, uint16_t* out_v, hipStream_t st) {
-  const int quads = kGemmM * N / 4;
-  hipLaunchKernelGGL((k_gemm_reduce<EPI>), dim3((quads + 255) / 256), dim3(256), 0, st, part, part2, n_split, N, res,
-                     out, out_k, out_v);
+static hipError_t launch_reduce(const float* part, int n_split, int N, const uint16_t* res, uint16_t* out,
+                                uint16_t* out_k, uint16_t* out_v, hipStream_t st) {
+  hipLaunchKernelGGL((k_gemm_reduce<EPI>), dim3(kGemmM * ((N + 255) / 256)), dim3(256), 0, st, part, n_split, N, res, out,
+                     out_k, out_v);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_w64(const uint16_t* W, int K, int N, uint16_t* Wp, hipStream_t st) {
+  const long long chunks = (long long)K * N / 8;
+  hipLaunchKernelGGL(k_pack_w64, dim3((unsigned)(chunks / 256)), dim3(256), 0, st, W, K, N, Wp);
   return hipGetLastError();
 }
 
 hipError_t launch_linear64(const uint16_t* A, const uint16_t* W, int K, int N, uint16_t* C, void* ws,
                            hipStream_t st) {
   int ns = 0;
-  hipError_t e = launch_gemm<false>(A, K, W, K, N, static_cast<float*>(ws), st, &ns);
+  hipError_t e = launch_gemm_generic(A, W, K, N, static_cast<float*>(ws), st, &ns);
   if (e != hipSuccess) return e;
-  return launch_reduce<kEpiStore>(static_cast<float*>(ws), nullptr, ns, N, nullptr, C, nullptr, nullptr, st);
+  return launch_reduce<kEpiStore>(static_cast<float*>(ws), ns, N, nullptr, C, nullptr, nullptr, st);
 }
 
 // Layer workspace: activations, then the attention workspace, then the GEMM partials (the
@@ -259,7 +426,7 @@ hipError_t launch_linear64(const uint16_t* A, const uint16_t* W, int K, int N, u
 struct LayerWs {
   uint16_t *n1, *q, *k, *v, *attn, *x2, *n2, *mlp;
   void* attn_ws;
-  float *part, *part2;
+  float* part;
 };
 static size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 static size_t layer_ws_layout(const AttnPlan& plan, void* ws, LayerWs* l) {
@@ -280,14 +447,15 @@ static size_t layer_ws_layout(const AttnPlan& plan, void* ws, LayerWs* l) {
   uint16_t* n2 = reinterpret_cast<uint16_t*>(take(act));
   uint16_t* mlp = reinterpret_cast<uint16_t*>(take((size_t)kGemmM * kLayerMlp * 2));
   void* attn_ws = take(attn_partials_bytes(plan));
-  const size_t p1 = gemm64_partials_bytes(kLayerHidden, kLayerMlp);
-  size_t pmax = p1;
-  for (size_t b : {gemm64_partials_bytes(kLayerHidden, kLayerQkv), gemm64_partials_bytes(kHq * 128, kLayerHidden),
-                   gemm64_partials_bytes(kLayerMlp, kLayerHidden)})
+  // float32 partials of the largest projection (gate and up share one launch: rows of 2 x 6144)
+  size_t pmax = 0;
+  for (size_t b : {(size_t)gemm_splits(kCfgQkv, kLayerHidden) * kGemmM * kLayerQkv * 4,
+                   (size_t)gemm_splits(kCfgO, kHq * 128) * kGemmM * kLayerHidden * 4,
+                   (size_t)gemm_splits(kCfgGateUp, kLayerHidden) * kGemmM * 2 * kLayerMlp * 4,
+                   (size_t)gemm_splits(kCfgDown, kLayerMlp) * kGemmM * kLayerHidden * 4})
     pmax = b > pmax ? b : pmax;
   float* part = reinterpret_cast<float*>(take(pmax));
-  float* part2 = reinterpret_cast<float*>(take(p1));
-  if (l) *l = LayerWs{n1, q, k, v, attn, x2, n2, mlp, attn_ws, part, part2};
+  if (l) *l = LayerWs{n1, q, k, v, attn, x2, n2, mlp, attn_ws, part};
   return off;
 }
 
@@ -307,21 +475,31 @@ hipError_t launch_layer(const LayerLaunch& p, hipStream_t st) {
   hipLaunchKernelGGL(k_rmsnorm_rows, dim3(kGemmM), dim3(kLayerHidden / 8), 0, st, p.x, p.ln1, p.eps, kLayerHidden,
                      l.n1);
   AX_TRY(hipGetLastError());
-  AX_TRY(launch_gemm<false>(l.n1, kLayerHidden, p.wqkv, kLayerHidden, kLayerQkv, l.part, st, &ns));
-  AX_TRY(launch_reduce<kEpiQkvSplit>(l.part, nullptr, ns, kLayerQkv, nullptr, l.q, l.k, l.v, st));
+  launch_gemm_cfg<kCfgQkv.nb, kCfgQkv.kw, kCfgQkv.steps, false>(l.n1, kLayerHidden, p.wqkv, nullptr, kLayerHidden,
+                                                                kLayerQkv, l.part, st);
+  AX_TRY(hipGetLastError());
+  AX_TRY(launch_reduce<kEpiQkvSplit>(l.part, gemm_splits(kCfgQkv, kLayerHidden), kLayerQkv, nullptr, l.q, l.k, l.v,
+                                     st));
   AttnLaunch a{l.q, p.qn, p.kn, p.cos_t, p.sin_t, p.eps, l.k, l.v, p.Kc, p.Vc, l.attn, l.attn_ws, p.S, p.Smax,
                /*q_norm=*/1, /*tail_norm=*/1};
   AX_TRY(launch_attn(plan, a, st));
-  AX_TRY(launch_gemm<true>(l.attn, 0, p.wo, kHq * 128, kLayerHidden, l.part, st, &ns));
-  AX_TRY(launch_reduce<kEpiResidual>(l.part, nullptr, ns, kLayerHidden, p.x, l.x2, nullptr, nullptr, st));
-  hipLaunchKernelGGL(k_rmsnorm_rows, dim3(kGemmM), dim3(kLayerHidden / 8), 0, st, l.x2, p.ln2, p.eps, kLayerHidden,
-                     l.n2);
+  launch_gemm_cfg<kCfgO.nb, kCfgO.kw, kCfgO.steps, true>(l.attn, 0, p.wo, nullptr, kHq * 128, kLayerHidden, l.part,
+                                                         st);
   AX_TRY(hipGetLastError());
-  AX_TRY(launch_gemm<false>(l.n2, kLayerHidden, p.w1, kLayerHidden, kLayerMlp, l.part, st, &ns));
-  AX_TRY(launch_gemm<false>(l.n2, kLayerHidden, p.w3, kLayerHidden, kLayerMlp, l.part2, st, &ns));
-  AX_TRY(launch_reduce<kEpiSwiGlu>(l.part, l.part2, ns, kLayerMlp, nullptr, l.mlp, nullptr, nullptr, st));
-  AX_TRY(launch_gemm<false>(l.mlp, kLayerMlp, p.w2, kLayerMlp, kLayerHidden, l.part, st, &ns));
-  AX_TRY(launch_reduce<kEpiResidual>(l.part, nullptr, ns, kLayerHidden, l.x2, p.x_out, nullptr, nullptr, st));
+  static_assert(kHq * 128 / (16 * kCfgO.kw * kCfgO.steps) == 4, "o projection splits");
+  hipLaunchKernelGGL(k_reduce_residual_norm<4>, dim3(kGemmM), dim3(kLayerHidden / 8), 0, st, l.part, p.x, p.ln2,
+                     p.eps, kLayerHidden, l.x2, l.n2);
+  AX_TRY(hipGetLastError());
+  launch_gemm_cfg<kCfgGateUp.nb, kCfgGateUp.kw, kCfgGateUp.steps, false>(l.n2, kLayerHidden, p.w1, p.w3,
+                                                                         kLayerHidden, kLayerMlp, l.part, st);
+  AX_TRY(hipGetLastError());
+  AX_TRY(launch_reduce<kEpiSwiGlu>(l.part, gemm_splits(kCfgGateUp, kLayerHidden), kLayerMlp, nullptr, l.mlp, nullptr,
+                                   nullptr, st));
+  launch_gemm_cfg<kCfgDown.nb, kCfgDown.kw, kCfgDown.steps, false>(l.mlp, kLayerMlp, p.w2, nullptr, kLayerMlp,
+                                                                   kLayerHidden, l.part, st);
+  AX_TRY(hipGetLastError());
+  AX_TRY(launch_reduce<kEpiResidual>(l.part, gemm_splits(kCfgDown, kLayerMlp), kLayerHidden, l.x2, p.x_out, nullptr,
+                                     nullptr, st));
 #undef AX_TRY
   return hipSuccess;
 }

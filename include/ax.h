@@ -270,7 +270,8 @@ int ax_text_decode_attn(const uint16_t* q_in, const uint16_t* k_in, const uint16
  *   x_out = x2 + (silu(n2 w1) * (n2 w3)) w2.
  * x_in, x_out [64][1536]; ln1, ln2 [1536]; weights input-major (the transpose
  * of the HF layout, as the pages store them): wqkv [1536][4096], wo
- * [2048][1536], w1 and w3 [1536][6144], w2 [6144][1536]; all bf16. Every op
+ * [2048][1536], w1 and w3 [1536][6144], w2 [6144][1536]; all bf16, each passed
+ * through ax_pack_weight_m64 once beforehand. Every op
  * hands a bf16 tensor to the next (rounded to nearest even); inside an op the
  * arithmetic is float32 (products of bf16 on the matrix cores). Updates the
  * cache tail like ax_expert_layer_attn. x_out must not alias x_in. ws: at least
@@ -285,10 +286,20 @@ int ax_expert_layer(const uint16_t* x_in, const uint16_t* ln1, const uint16_t* w
                     int S, int Smax, uint16_t* x_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Weight packing for the projections: W [K][N] bf16, input-major, into W_packed
+ * (same size, a separate buffer) in the layout the projection kernel streams:
+ * 4 KB blocks of 32 rows x 64 columns, the blocks of one 64-column tile
+ * consecutive, so that each workgroup reads one contiguous range. A one-time
+ * step when weights are loaded. K a multiple of 128, N of 64.
+ */
+int ax_pack_weight_m64(const uint16_t* W, int K, int N, uint16_t* W_packed, void* stream);
+
+/*
  * The layer's projection on its own: C[64][N] = bf16(A[64][K] W[K][N]) for 64
- * rows (bf16 A and W, W input-major, float32 accumulation). K a multiple of
- * 128, N of 64. ws: ax_linear_m64_workspace_bytes(K, N) bytes (float32 split
- * partials), 256-byte aligned.
+ * rows (bf16 A and W, W input-major and packed by ax_pack_weight_m64, float32
+ * accumulation). K a multiple of 128, N of 64. ws:
+ * ax_linear_m64_workspace_bytes(K, N) bytes (float32 split partials), 256-byte
+ * aligned.
  */
 size_t ax_linear_m64_workspace_bytes(int K, int N);
 int ax_linear_m64(const uint16_t* A, const uint16_t* W, int K, int N, uint16_t* C, void* ws,

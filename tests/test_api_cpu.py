@@ -199,7 +199,7 @@ def test_text_decode_validation_codes():
 def test_expert_layer_workspace_and_validation_codes():
     assert ax.expert_layer_workspace_bytes(4700, 8192) > ax.expert_attn_workspace_bytes(4700, 8192)
     assert ax.expert_layer_workspace_bytes(193, 256) == 0
-    assert ax.linear_m64_workspace_bytes(1536, 4096) == 6 * 64 * 4096 * 4
+    assert ax.linear_m64_workspace_bytes(1536, 4096) == 2 * 64 * 4096 * 4     # 2 splits of 768 rows
     assert ax.linear_m64_workspace_bytes(100, 64) == 0
     assert ax.linear_m64_workspace_bytes(128, 96) == 0
     f = ax.lib.ax_expert_layer
@@ -218,6 +218,10 @@ def test_expert_layer_workspace_and_validation_codes():
     assert layer(ws_bytes=16) == ax.AX_E_WORKSPACE
     assert layer(ws=FAKE + 16) == ax.AX_E_WORKSPACE
     assert layer() == ax.AX_E_UNSUPPORTED                      # valid arguments, no device here
+    pk = ax.lib.ax_pack_weight_m64
+    assert pk(None, 128, 64, FAKE, None) == ax.AX_E_NULL
+    assert pk(FAKE, 100, 64, FAKE, None) == ax.AX_E_SHAPE
+    assert pk(FAKE, 128, 64, FAKE, None) == ax.AX_E_UNSUPPORTED
     g = ax.lib.ax_linear_m64
     assert g(None, FAKE, 128, 64, FAKE, FAKE, big, None) == ax.AX_E_NULL
     assert g(FAKE, FAKE, 100, 64, FAKE, FAKE, big, None) == ax.AX_E_SHAPE

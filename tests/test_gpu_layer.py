@@ -37,9 +37,17 @@ def _bits_normal(rng, shape, scale=1.0):
     return oracle.f64_to_bf16_bits(rng.standard_normal(shape) * scale)
 
 
+def _packed(ax, w):
+    """A device weight [K, N] in the projections' packed layout."""
+    K, N = w.shape
+    wp = torch.empty_like(w)
+    ax.pack_weight_m64(w, K, N, wp)
+    return wp
+
+
 def _linear(ax, a_bits, w_bits):
     K, N = w_bits.shape
-    A, W = up(a_bits), up(w_bits)
+    A, W = up(a_bits), _packed(ax, up(w_bits))
     C = torch.zeros((64, N), dtype=torch.int16, device=DEV)
     nb = ax.linear_m64_workspace_bytes(K, N)
     assert nb > 0
@@ -92,6 +100,19 @@ def test_linear_m64_structure(ax):
     assert np.array_equal(got, ref)
 
 
+def test_pack_weight_m64_layout(ax):
+    # packed block (32-column block j, 16-row step s), lane l, element e holds weight row
+    # 16 s + 8 (l // 32) + e, column 32 j + l % 32: the matrix-core operand of lane l, checked
+    # element by element against that definition
+    K, N = 256, 192
+    w = np.arange(K * N, dtype=np.uint32).reshape(K, N).astype(np.uint16)
+    say("pack_weight_m64 layout")
+    got = down(_packed(ax, up(w))).reshape(N // 32, K // 16, 64, 8)
+    j, s, l, e = np.meshgrid(*(np.arange(n) for n in got.shape), indexing="ij")
+    ref = w[16 * s + 8 * (l // 32) + e, 32 * j + l % 32]
+    assert np.array_equal(got, ref)
+
+
 def test_linear_m64_rejects_bad_shapes(ax):
     x = torch.zeros(64 * 256, dtype=torch.int16, device=DEV)
     ws = torch.empty(1 << 20, dtype=torch.uint8, device=DEV)
@@ -103,7 +124,7 @@ def test_linear_m64_rejects_bad_shapes(ax):
 class LayerBufs:
     def __init__(self, ax, w, x, cache, S, Smax):
         self.S, self.Smax = S, Smax
-        self.w = {k: up(v) for k, v in w.items()}
+        self.w = {k: (_packed(ax, up(v)) if v.ndim == 2 else up(v)) for k, v in w.items()}
         self.x = up(x)
         self.Kc, self.Vc = up(cache["Kc"]), up(cache["Vc"])
         cos, sin = ax.rope_tables(S)
