@@ -202,3 +202,67 @@ def test_expert_layer_headline_shape(ax):
     b.run(ax)
     torch.cuda.synchronize()
     assert np.array_equal(down(b.out), first)
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("layer", [0, 63])
+def test_layer_benchmark_inputs_match_oracle(ax, layer):
+    # the benchmark's own inputs: device-seeded weights of this layer (packed as the benchmark
+    # packs them), the layer's cache, the first residual; copied back and checked against the oracle
+    S, Smax = 4700, 8192
+    say(f"layer benchmark inputs, layer {layer}")
+    w = synth.device_layer_weights(layer, DEV)
+    Kc, Vc = (t.contiguous() for t in synth.device_cache(Smax, S, layer, DEV))
+    g = torch.Generator(device=DEV)
+    g.manual_seed(11000)
+    x = torch.randn((64, 1536), generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+    host = {k: _bits(v) for k, v in w.items()}
+    cache = {"Kc": _bits(Kc), "Vc": _bits(Vc)}
+    xb = _bits(x)
+    packed = {k: (_packed(ax, v) if v.dim() == 2 else v) for k, v in w.items()}
+    cos, sin = (torch.from_numpy(t).to(DEV) for t in ax.rope_tables(S))
+    out = torch.zeros((64, 1536), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(ax.expert_layer_workspace_bytes(S, Smax), dtype=torch.uint8, device=DEV)
+    ax.expert_layer(x, packed["ln1"], packed["wqkv"], packed["qn"], packed["kn"], packed["wo"], packed["ln2"],
+                    packed["w1"], packed["w3"], packed["w2"], cos, sin, 1e-6, Kc, Vc, S, Smax, out, ws)
+    torch.cuda.synchronize()
+    ref = _ref(host, xb, cache, S, Smax)
+    got = bf16_to_f64(_bits(out))
+    m = metrics(got, ref["x_out"])
+    print(f"layer {layer}: max_abs={m['max_abs']:.3e} pcc={m['pcc']:.7f} rel_l2={m['rel_l2']:.3e}", flush=True)
+    assert m["pcc"] >= 0.9999 and m["rel_l2"] <= 1e-2, m
+    assert (np.abs(got - ref["x_out"]) <= 0.05 + 2.0 ** -6 * np.abs(ref["x_out"])).all()
+
+
+def test_layer_graph_replay_equals_eager(ax):
+    # the layer's eleven launches captured in one graph, replayed three times with eager work in
+    # between: every replay equals the eager result bit for bit
+    S, Smax = 1000, 2048
+    w = synth.layer_weights(41)
+    x = synth.residual_inputs(42)
+    cache = synth.layer_inputs(Smax, S, 43)
+    say("layer graph capture / replay x3")
+    b = LayerBufs(ax, w, x, cache, S, Smax)
+    b.run(ax)
+    torch.cuda.synchronize()
+    eager = down(b.out).copy()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    wt = b.w
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            ax.expert_layer(b.x, wt["ln1"], wt["wqkv"], wt["qn"], wt["kn"], wt["wo"], wt["ln2"], wt["w1"], wt["w3"],
+                            wt["w2"], b.cos, b.sin, 1e-6, b.Kc, b.Vc, S, Smax, b.out, b.ws, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        b.out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(down(b.out), eager), f"replay {rep}"
+        torch.randn(1 << 20, device=DEV).sum().item()   # eager work between replays
