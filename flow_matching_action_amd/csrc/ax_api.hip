@@ -3,24 +3,30 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/ax.h"
 #include "ax_launch.h"
 
 namespace {
 
 constexpr int kMaxDev = 64;
-int g_arch[kMaxDev];  // 0 = unknown, 1 = gfx950, -1 = other
+// 0 = unknown, 1 = gfx950, -1 = other; atomic because callers on several host threads may fill
+// the same entry (all with the same value)
+std::atomic<int> g_arch[kMaxDev];
 
 // Is the current device a gfx950? Cached per device (the query is not a stream operation).
 int check_device() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return AX_E_UNSUPPORTED;
-  if (g_arch[dev] == 0) {
+  int arch = g_arch[dev].load(std::memory_order_relaxed);
+  if (arch == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return AX_E_UNSUPPORTED;
-    g_arch[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    arch = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_arch[dev].store(arch, std::memory_order_relaxed);
   }
-  return g_arch[dev] == 1 ? AX_OK : AX_E_UNSUPPORTED;
+  return arch == 1 ? AX_OK : AX_E_UNSUPPORTED;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
