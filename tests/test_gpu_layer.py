@@ -122,12 +122,12 @@ def test_linear_m64_rejects_bad_shapes(ax):
 
 
 class LayerBufs:
-    def __init__(self, ax, w, x, cache, S, Smax):
+    def __init__(self, ax, w, x, cache, S, Smax, rope_delta=0):
         self.S, self.Smax = S, Smax
         self.w = {k: (_packed(ax, up(v)) if v.ndim == 2 else up(v)) for k, v in w.items()}
         self.x = up(x)
         self.Kc, self.Vc = up(cache["Kc"]), up(cache["Vc"])
-        cos, sin = ax.rope_tables(S)
+        cos, sin = ax.rope_tables(S + rope_delta)
         self.cos = torch.from_numpy(cos).to(DEV)
         self.sin = torch.from_numpy(sin).to(DEV)
         self.out = torch.zeros((64, 1536), dtype=torch.int16, device=DEV)
@@ -142,9 +142,9 @@ class LayerBufs:
                         self.cos, self.sin, 1e-6, self.Kc, self.Vc, self.S, self.Smax, self.out, self.ws)
 
 
-def _ref(w, x, cache, S, Smax):
+def _ref(w, x, cache, S, Smax, rope_delta=0):
     return oracle.expert_layer(x, w["ln1"], w["wqkv"], w["qn"], w["kn"], w["wo"], w["ln2"], w["w1"], w["w3"],
-                               w["w2"], cache["Kc"], cache["Vc"], S, Smax)
+                               w["w2"], cache["Kc"], cache["Vc"], S, Smax, rope_delta)
 
 
 def _check_layer(b, ref, cache, label):
@@ -184,6 +184,40 @@ def test_expert_layer_matches_oracle(ax, S, Smax, seed):
     b.run(ax)
     torch.cuda.synchronize()
     _check_layer(b, _ref(w, x, cache, S, Smax), cache, f"layer S={S} Smax={Smax}")
+
+
+def test_expert_layer_rope_delta_and_full_cache(ax):
+    # the tables passed in decide the positions (S + rope_delta + i); a cache with no hidden rows
+    S, Smax, delta = 448, 512, 7
+    w = synth.layer_weights(51)
+    x = synth.residual_inputs(52)
+    cache = synth.layer_inputs(Smax, S, 53)
+    say(f"expert_layer S={S} Smax={Smax} rope_delta={delta}")
+    b = LayerBufs(ax, w, x, cache, S, Smax, rope_delta=delta)
+    b.run(ax)
+    torch.cuda.synchronize()
+    ref = _ref(w, x, cache, S, Smax, delta)
+    _check_layer(b, ref, cache, f"layer S={S} Smax={Smax} delta={delta}")
+    # the same call with the tables of rope_delta 0 is measurably different (the offset is used)
+    ref0 = _ref(w, x, cache, S, Smax, 0)
+    assert np.abs(ref0["x_out"] - ref["x_out"]).max() > 0.05
+
+
+def test_expert_layer_workspace_reuse(ax):
+    # one workspace sized for the larger shape serves a smaller one next (no state is kept in it)
+    w = synth.layer_weights(61)
+    x = synth.residual_inputs(62)
+    big = synth.layer_inputs(2048, 1900, 63)
+    small = synth.layer_inputs(256, 64, 64)
+    say("expert_layer workspace reuse 1900/2048 then 64/256")
+    b1 = LayerBufs(ax, w, x, big, 1900, 2048)
+    b1.run(ax)
+    b2 = LayerBufs(ax, w, x, small, 64, 256)
+    b2.ws = b1.ws
+    b2.run(ax)
+    torch.cuda.synchronize()
+    _check_layer(b1, _ref(w, x, big, 1900, 2048), big, "layer reuse, big")
+    _check_layer(b2, _ref(w, x, small, 64, 256), small, "layer reuse, small")
 
 
 def test_expert_layer_headline_shape(ax):
