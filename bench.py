@@ -263,10 +263,12 @@ class RotatingWorkloadF8:
 KERNEL_SOURCES = {
     "bf16": ("ax_attn.hip", "ax_attn_common.h", "ax_dev.h"),
     "fp8": ("ax_attn_f8.hip", "ax_attn_common.h", "ax_dev.h"),
+    "decode": ("ax_decode.hip", "ax_attn_common.h", "ax_dev.h"),
 }
 TRAFFIC_FILES = {
     "bf16": "traffic_expert_layer_attn_smax8192_s4700.txt",
     "fp8": "traffic_expert_layer_attn_fp8_smax8192_s8128.txt",
+    "decode": "traffic_text_decode_pos4700_smax8192.txt",
 }
 
 
@@ -502,7 +504,7 @@ def main() -> int:
             "achieved_hbm_gbs": round(bd / (usd * 1e-6) / 1e9, 1),
             "roofline": {"bound": "hbm", "achieved": round(bd / (usd * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(bd / (usd * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                         "traffic": None,
+                         "traffic": load_traffic("decode"),
                          "kernel": "k_decode_attn + k_decode_combine (the whole step, two launches)",
                          "algorithmic_bytes_per_step": bd},
             "replays_ms": [round(t, 4) for t in td],
