@@ -264,11 +264,13 @@ KERNEL_SOURCES = {
     "bf16": ("ax_attn.hip", "ax_attn_common.h", "ax_dev.h"),
     "fp8": ("ax_attn_f8.hip", "ax_attn_common.h", "ax_dev.h"),
     "decode": ("ax_decode.hip", "ax_attn_common.h", "ax_dev.h"),
+    "layer": ("ax_layer.hip", "ax_attn.hip", "ax_attn_common.h", "ax_dev.h"),
 }
 TRAFFIC_FILES = {
     "bf16": "traffic_expert_layer_attn_smax8192_s4700.txt",
     "fp8": "traffic_expert_layer_attn_fp8_smax8192_s8128.txt",
     "decode": "traffic_text_decode_pos4700_smax8192.txt",
+    "layer": "traffic_expert_layer_smax8192_s4700.txt",
 }
 
 
@@ -530,7 +532,7 @@ def main() -> int:
             "achieved_hbm_gbs": round(bl / (usl * 1e-6) / 1e9, 1),
             "roofline": {"bound": "hbm", "achieved": round(bl / (usl * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(bl / (usl * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                         "traffic": None,
+                         "traffic": load_traffic("layer"),
                          "kernel": "the whole layer (eleven launches)",
                          "algorithmic_bytes_per_layer": bl,
                          "algorithmic_flops_per_layer": algorithmic_flops_layer(S)},
