@@ -15,24 +15,25 @@
 // give the same softmax).
 //
 // gfx950 mapping
-// - One workgroup of 12 waves per (kv head, key split); workgroup id w -> head w % 8,
-//   which the dispatcher places on XCD w % 8, so a head's splits share one L2. The cache
-//   keys [0, S) are cut into splits of at most 6 blocks of 32 keys; the 64 own tokens
-//   form one more split of their own.
-// - Waves 8..11 (loaders) stream the split's K/V rows into per-block LDS tiles with
+// - One workgroup of 8 waves (one compute and one loader wave per SIMD) per (kv head, key
+//   split); workgroup id w -> head w % 8, which the dispatcher places on XCD w % 8, so a
+//   head's splits share one L2. The cache keys [0, S) are cut into splits of at most 6
+//   blocks of 32 keys; the 64 own tokens form one more split of their own.
+// - Waves 4..7 (loaders) stream the split's K/V rows into per-block LDS tiles with
 //   direct-to-LDS loads (global_load_lds, 16 bytes per lane), a few blocks ahead, and
 //   count each landed block in LDS; rows are 256 bytes with the 16-byte chunks
 //   XOR-swizzled by row.
-// - Waves 0..7 (compute) fetch and norm/rope the 128 query rows in place in LDS (16
+// - Waves 0..3 (compute) fetch and norm/rope the 128 query rows in place in LDS (16
 //   lanes per row, the same arithmetic as the stand-alone norm/RoPE kernel); in the own
 //   split they also norm/rope the own k rows and write the cache tail. Then wave w takes
-//   query rows 32 (w & 3) .. +31 over the blocks of parity w >> 2: S^T = K Q^T on
+//   query rows 32w .. +31 over every block of the split: S^T = K Q^T on
 //   v_mfma_f32_32x32x16_bf16 (A = K rows, B = Q^T), so each lane holds one query row's
 //   scores; O^T = V^T P^T with V^T read straight from row-major V by ds_read_tr16_b64
 //   and P^T taken from the S^T accumulator. Inside a block MFMA row m reads key pi(m)
 //   (bits 2 and 3 swapped), which makes the 8 keys a lane supplies to one PV step
-//   consecutive. The two parity waves of a query group merge through LDS and the even
-//   one stores the split's partial.
+//   consecutive. The loop is software-pipelined one block deep (scores of block b+1
+//   with the softmax of block b, and the PV of block b with the row max of block b+1),
+//   and each wave stores its own rows' partial.
 #include "ax_attn_common.h"
 #include "ax_launch.h"
 
@@ -42,6 +43,11 @@ constexpr int kMaxNB = 6;                     // blocks per split, upper bound (
 static_assert(kMaxNB <= kMaxBlocks, "counter layout");
 constexpr int kTileBytes = 2 * kBlk * kD * 2; // K 8 KB + V 8 KB
 constexpr int kDmaDepth = 3;                  // blocks of a split in flight per loader wave
+// Wave roles of the split kernel: one compute wave and one loader wave per SIMD, so that a
+// compute wave has 256 registers for its software pipeline.
+constexpr int kFCompute = 4;
+constexpr int kFLoad = 4;
+constexpr int kFThreads = 64 * (kFCompute + kFLoad);
 
 struct FusedArgs {
   const uint16_t* q;       // [16][64][128]: raw q (q_norm) or already roped q
@@ -80,27 +86,52 @@ __device__ __forceinline__ uint8_t* pick(uint8_t* t0, uint8_t* t1, uint8_t* t2, 
   else return t5;
 }
 
+// RMSNorm + RoPE in place in LDS of the 8 query rows 32p + 16s + r16 (p = 0..3, s = 0..1) that
+// this lane's 16-lane group holds (columns 8 j16 .. +7); row 32p + 16s + r16 is token
+// 32(p & 1) + 16s + r16, whose RoPE coefficients are A/B[2(p & 1) + s]. All rows are read
+// before any is written back. Per row the arithmetic is that of the stand-alone kernel.
+__device__ __forceinline__ void norm_rope_query_rows8(uint8_t* qlds, const float (&A)[4][8], const float (&B)[4][8],
+                                                      int j16, int r16, float eps) {
+  u32x4 qv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 32 * (i >> 1) + 16 * (i & 1) + r16;
+    qv[i] = *reinterpret_cast<const u32x4*>(qlds + r * 256 + 16 * (j16 ^ qswz(r)));
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int t = 2 * ((i >> 1) & 1) + (i & 1);
+    float x[8];
+    unpack8v(qv[i], x);
+    norm_rope_row16(x, A[t], B[t], eps);
+    qv[i] = pack8v(x);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 32 * (i >> 1) + 16 * (i & 1) + r16;
+    *reinterpret_cast<u32x4*>(qlds + r * 256 + 16 * (j16 ^ qswz(r))) = qv[i];
+  }
+}
+
 // NORM: q and the own k arrive raw and are normed + roped here (the layer step); otherwise
 // both arrive roped (attention only).
 //
-// Wave roles (12 waves, 3 per SIMD).
-// - Waves 8..11 (loaders) only issue direct-to-LDS loads - the 128 query rows of the head,
-//   then the cache blocks of the split - and count each landed block in LDS. Keeping
-//   ordinary loads and LDS-DMA loads in different waves keeps each wave's vmcnt in order,
-//   so no wave ever has to drain its queue early; the counters (not barriers) let the loads
-//   run ahead of the arithmetic.
-// - Waves 0..7 (compute) norm/rope the queries in place in LDS and handle the own-token
-//   rows, then wave w takes query rows 32 (w & 3) .. +31 over the blocks of parity w >> 2.
-//   The two waves of a query group share a SIMD, so one's matrix-core work overlaps the
-//   other's softmax. At the end the odd-parity wave hands its (m, l, O) to the even one
-//   through LDS, which merges them and writes the split's partial.
+// Wave roles (8 waves, 2 per SIMD).
+// - Waves 4..7 (loaders) only issue direct-to-LDS loads of the split's cache blocks and count
+//   each landed block in LDS. Keeping ordinary loads and LDS-DMA loads in different waves
+//   keeps each wave's vmcnt in order, so no wave ever has to drain its queue early; the
+//   counters (not barriers) let the loads run ahead of the arithmetic.
+// - Waves 0..3 (compute) fetch, norm and rope the 128 query rows in place in LDS and handle
+//   the own-token rows; then wave w takes query rows 32w .. +31 over every block of the
+//   split, software-pipelined: the QK^T of block b+1 runs on the matrix cores while the
+//   exponentials of block b run on the vector ALU, and the PV of block b while the max of
+//   block b+1. Each wave stores its rows' partial itself.
 template <int NB, bool NORM>
-__global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
+__global__ __launch_bounds__(kFThreads, 1) void k_attn_fused(FusedArgs a) {
   AX_TILE(0); AX_TILE(1); AX_TILE(2); AX_TILE(3); AX_TILE(4); AX_TILE(5);
   __shared__ __attribute__((aligned(16))) uint8_t qlds[kQBytes];
   // roped own-token K rows (row tok, chunks swizzled like the tile row they stand in for)
   __shared__ __attribute__((aligned(16))) uint8_t kown[kT * 256];
-  __shared__ float mlx[4][2][32];  // merge hand-off: (m, l) of the odd-parity waves per query row
   // hand-off counters
   __shared__ int cnt[kNCnt];
   const int tid = threadIdx.x;
@@ -115,28 +146,53 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
   const int k_begin = own_split ? a.S : split * a.kps;
   const int k_end = own_split ? n_keys : min(k_begin + a.kps, a.S);
   const long long head_off = (long long)g * a.Smax * kD;
-  // blocks holding own-token rows that need the tail step (norm of k and/or cache tail write)
+  // own rows come from the k/v tensors (normed here if NORM) and go to the cache tail
   const bool own_tail = a.own_tail != 0;
 
   if (tid < kNCnt) cnt[tid] = 0;
-  if (wave < kComputeWaves) {
-    // Each compute wave fetches the 16 query rows it norms (rows 32p + 4 wave .. +3, p = 0..3)
-    // ahead of the cache stream; lane l lands at 16 l of the 1 KB, so it fetches the chunk
-    // that the row's swizzle puts there.
+  // Compute-wave lanes: lane group r16 (0..15) norms query rows 32p + 16s + r16 (token
+  // 32(p & 1) + 16s + r16) and own-token rows 16u + r16 (u = 0..3): tokens 16u + r16 in both.
+  const int j16 = tid & 15;
+  const int r16 = tid >> 4;
+  const bool has_own = own_tail && own_split;  // this split holds the own-token rows
+  u32x4 graw, gkraw, kraw[4], vraw[4];
+  f32x4 cs_h[4][2];
+  if (wave < kFCompute) {
+    // 1. Prologue loads, all issued before the start barrier and so ahead of the cache stream
+    //    in the CU's memory queue: the 32 query rows this wave norms (rows 32p + 16s + 4 wave
+    //    .. +3; lane l lands at 16 l of the 1 KB, so it fetches the chunk that the row's
+    //    swizzle puts there), the gammas, the RoPE table rows and the own-token rows.
     const uint16_t* qh = a.q + (long long)(2 * g) * kT * kD;  // q heads 2g, 2g+1: 128 rows, contiguous
-    static_for<4>([&](auto pc) {
-      constexpr int p = decltype(pc)::value;
-      const int row = 32 * p + 4 * wave + (lane >> 4);
+    static_for<8>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const int row0 = 32 * (i >> 1) + 16 * (i & 1) + 4 * wave;
+      const int row = row0 + (lane >> 4);
       const uint16_t* src = qh + row * kD + 8 * ((lane & 15) ^ qswz(row));
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(qlds + (32 * p + 4 * wave) * 256), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(qlds + row0 * 256), 16, 0, 0);
     });
+    if constexpr (NORM) {
+      graw = *reinterpret_cast<const u32x4*>(a.gq + 8 * j16);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load_cos_sin_half(a.cos_t, a.sin_t, 16 * u + r16, j16, cs_h[u][0], cs_h[u][1]);
+    }
+    if (has_own) {
+      const uint16_t* kt = a.kt_base + g * a.tail_stride;
+      const uint16_t* vt = a.vt_base + g * a.tail_stride;
+      if constexpr (NORM) gkraw = *reinterpret_cast<const u32x4*>(a.gk + 8 * j16);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int tok = 16 * u + r16;
+        kraw[u] = *reinterpret_cast<const u32x4*>(kt + (long long)tok * kD + 8 * j16);
+        vraw[u] = *reinterpret_cast<const u32x4*>(vt + (long long)tok * kD + 8 * j16);
+      }
+    }
   }
   lds_barrier();  // start: counters cleared (the only workgroup barrier)
 
-  if (wave >= kComputeWaves) {
+  if (wave >= kFCompute) {
     // ---------------- loader waves: of each block the K row groups w and w+4 and the V row
     // groups w and w+4 (4 rows each)
-    const int w = wave - kComputeWaves;
+    const int w = wave - kFCompute;
     const uint16_t* kc = a.Kc + head_off;
     const uint16_t* vc = a.Vc + head_off;
     const uint16_t* kt = a.kt_base + g * a.tail_stride;
@@ -177,86 +233,61 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
     return;
   }
 
-  // ---------------- compute waves (512 threads)
-  const int j16 = tid & 15;
-  const int r16 = tid >> 4;  // 0..31
-  // 1. Prologue loads. Query pass p (0..3) covers folded row 32p + r16 (q head 2g + row/64,
-  //    token row % 64), so token set p & 1: token r16 or 32 + r16; own-token row set p (0..1)
-  //    is token 32p + r16 and uses the same cos/sin. Wave w's rows are the ones it fetched.
-  u32x4 graw, gkraw, kraw[2], vraw[2];
-  f32x4 cs_h[2][2];
-  if constexpr (NORM) {
-    graw = *reinterpret_cast<const u32x4*>(a.gq + 8 * j16);
-#pragma unroll
-    for (int p = 0; p < 2; ++p) load_cos_sin_half(a.cos_t, a.sin_t, 32 * p + r16, j16, cs_h[p][0], cs_h[p][1]);
-  }
-  const bool has_own = own_tail && k_end > a.S;  // this split holds own-token rows
-  if (has_own) {
-    const uint16_t* kt = a.kt_base + g * a.tail_stride;
-    const uint16_t* vt = a.vt_base + g * a.tail_stride;
-    if constexpr (NORM) gkraw = *reinterpret_cast<const u32x4*>(a.gk + 8 * j16);
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int tok = 32 * p + r16;
-      kraw[p] = *reinterpret_cast<const u32x4*>(kt + (long long)tok * kD + 8 * j16);
-      vraw[p] = *reinterpret_cast<const u32x4*>(vt + (long long)tok * kD + 8 * j16);
-    }
-  }
-  float qc[2][8], qs[2][8];
+  // ---------------- compute waves (256 threads)
+  float qc[4][8], qs[4][8];
   if constexpr (NORM) {
 #pragma unroll
-    for (int p = 0; p < 2; ++p) split_cos_sin(cs_h[p][0], cs_h[p][1], j16, qc[p], qs[p]);
+    for (int u = 0; u < 4; ++u) split_cos_sin(cs_h[u][0], cs_h[u][1], j16, qc[u], qs[u]);
   }
-  // 2. this wave's query rows, normed and roped in place in LDS (unless they came roped)
-  wait_vmcnt<0>();  // its query rows and every prologue load have landed
-  if constexpr (NORM) norm_rope_query_rows(qlds, graw, qc, qs, j16, r16, a.eps);
-  // 3. own-token rows of this split: K normed + roped (or taken roped) into kown and the cache
-  //    tail, V copied to the cache tail (the stores come after every load has been waited
-  //    for, so no later wait includes them)
+  // 2. the query rows, normed and roped in place in LDS (unless they came roped)
+  wait_vmcnt<0>();  // this wave's query rows and every prologue load have landed
+  if constexpr (NORM) {
+    float qg[8], A[4][8], B[4][8];
+    unpack8v(graw, qg);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) rope_coef(qg, qc[u], qs[u], j16, A[u], B[u]);
+    norm_rope_query_rows8(qlds, A, B, j16, r16, a.eps);
+  }
+  // 3. own-token rows (own split only): K normed + roped (or taken roped) into kown and the
+  //    cache tail, V copied to the cache tail (the stores come after every load has been
+  //    waited for, so no later wait includes them)
   if (has_own) {
     float gk[8];
     if constexpr (NORM) unpack8v(gkraw, gk);
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int tok = 32 * p + r16;
-      const int vk = a.S + tok;
-      if (vk >= k_begin && vk < k_end) {
-        u32x4 kv = kraw[p];
-        if constexpr (NORM) {
-          float x[8], A[8], B[8];
-          unpack8v(kv, x);
-          rope_coef(gk, qc[p], qs[p], j16, A, B);
-          norm_rope_row16(x, A, B, a.eps);
-          kv = pack8v(x);
-        }
-        const int rr = (vk - k_begin) & (kBlk - 1);
-        *reinterpret_cast<u32x4*>(kown + tok * 256 + 16 * (j16 ^ kswz(rr))) = kv;
-        const long long dst = head_off + (long long)(a.Smax - kT + tok) * kD + 8 * j16;
-        *reinterpret_cast<u32x4*>(a.Kc + dst) = kv;
-        *reinterpret_cast<u32x4*>(a.Vc + dst) = vraw[p];
+    for (int u = 0; u < 4; ++u) {
+      const int tok = 16 * u + r16;
+      u32x4 kv = kraw[u];
+      if constexpr (NORM) {
+        float x[8], A[8], B[8];
+        unpack8v(kv, x);
+        rope_coef(gk, qc[u], qs[u], j16, A, B);
+        norm_rope_row16(x, A, B, a.eps);
+        kv = pack8v(x);
       }
+      *reinterpret_cast<u32x4*>(kown + tok * 256 + 16 * (j16 ^ kswz(tok & (kBlk - 1)))) = kv;
+      const long long dst = head_off + (long long)(a.Smax - kT + tok) * kD + 8 * j16;
+      *reinterpret_cast<u32x4*>(a.Kc + dst) = kv;
+      *reinterpret_cast<u32x4*>(a.Vc + dst) = vraw[u];
     }
   }
   arrive(&cnt[kCntQNormed], lane);
-  await(&cnt[kCntQNormed], kComputeWaves);  // all 128 query rows and the own-token K rows are in LDS
+  await(&cnt[kCntQNormed], kFCompute);  // all 128 query rows and the own-token K rows are in LDS
 
-  const int qgrp = wave & 3;  // query rows 32 qgrp .. +31
-  const int par = wave >> 2;  // blocks b with b % 2 == par
   const int n = lane & 31;
   const int h = lane >> 5;
-  const int qrow = 32 * qgrp + n;
+  const int qrow = 32 * wave + n;
   bf16x8 qf[8];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk)
     qf[kk] = *reinterpret_cast<const bf16x8*>(qlds + qrow * 256 + 16 * ((dcol(kk, h) >> 3) ^ qswz(qrow)));
-  arrive(&cnt[kCntQRead], lane);  // this wave no longer reads qlds
 
   f32x16 o[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;  // running max in log2 units of the scaled score, row sum
+  float l_run = 0.f;  // row sum (this lane's half of the keys)
   const float sc = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
   const int krow = perm_key(n);
   // Per-lane LDS offsets, fixed for the loop: a block only adds its tile's (constant) base.
@@ -276,131 +307,163 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_fused(FusedArgs a) {
   const int voff[2] = {vrow0 * 256 + 16 * (vx ^ vswz(vrow0)) + 8 * (li & 1),
                        vrow0 * 256 + 16 * ((4 + vx) ^ vswz(vrow0)) + 8 * (li & 1)};
 
-  // Blocks of this wave's parity. A block past the split end (only in a short split) is
-  // skipped, but still awaited and counted as consumed, so that a consumed tile is never
-  // written by a load still in flight; the first block a wave processes holds at least one
-  // visible key, so m_run is finite after it.
+  // Blocks 0 .. nb-1 hold visible keys (only the last can be partial). K of an own-token block
+  // (own split with own_tail) is read from kown, swizzled like the tile. The pipeline reads K
+  // and forms scores ahead of the softmax; past nb it reads a tile without waiting for it
+  // (LDS, in bounds), and nothing computed from such a tile is used: its max takes no part in
+  // the rescale test and the loop ends before its exponentials.
+  const int nb = (k_end - k_begin + kBlk - 1) / kBlk;
+  const bool k_from_own = has_own;
+  auto kbase = [&](auto bc) -> const uint8_t* {
+    constexpr int b = decltype(bc)::value;
+    if constexpr (b * kBlk < kT)
+      if (k_from_own) return kown + b * kBlk * 256;
+    return pick<b>(t0, t1, t2, t3, t4, t5);
+  };
+  auto read_k = [&](const uint8_t* base, bf16x8 (&kf)[8]) {
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(base + koff[kk & 3] + 128 * (kk >> 2));
+  };
+  auto qk = [&](const bf16x8 (&kf)[8]) {
+    f32x16 s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+    return s;
+  };
+  // Row max of a block's scores over both lane halves, in log2 units. Rows past the split end
+  // hold a copy of the split's first key (see the loaders), a visible key, so the max of a
+  // partial block needs no mask.
+  auto blk_max = [&](const f32x16& s) {
+    float m0 = fmaxf(fmaxf(s[0], s[1]), s[2]);
+    float m1 = fmaxf(fmaxf(s[3], s[4]), s[5]);
+    float m2 = fmaxf(fmaxf(s[6], s[7]), s[8]);
+    float m3 = fmaxf(fmaxf(s[9], s[10]), s[11]);
+    float m4 = fmaxf(fmaxf(s[12], s[13]), s[14]);
+    const float m = fmaxf(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)), fmaxf(m4, s[15]));
+    const float2 pr = pair32(m);
+    return fmaxf(pr.x, pr.y) * sc;
+  };
+
+  bf16x8 kf[8];
+  // block 0: scores, max; the exponent reference m_run starts at its max (finite: block 0 holds
+  // a visible key)
+  await(&cnt[kCntBlock + 0], kFLoad);
+  read_k(kbase(std::integral_constant<int, 0>{}), kf);
+  f32x16 s_cur = qk(kf);
+  float m_run = blk_max(s_cur);
+  if constexpr (NB > 1) {
+    if (nb > 1) {
+      await(&cnt[kCntBlock + 1], kFLoad);
+      read_k(kbase(std::integral_constant<int, 1>{}), kf);
+    }
+  }
+  const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+
   static_for<NB>([&](auto bc) {
     constexpr int b = decltype(bc)::value;
+    if (b >= nb) return;
+    if constexpr (b + 2 < NB) {
+      if (b + 2 < nb) await(&cnt[kCntBlock + b + 2], kFLoad);  // its K is read below
+    }
     const int kb = k_begin + b * kBlk;
-    if ((b & 1) != par) return;
-    uint8_t* tile = pick<b>(t0, t1, t2, t3, t4, t5);
-    await(&cnt[kCntBlock + b], kLoaderWaves);
-    if (kb < k_end) {
-      // S^T = K Q^T: K fragments from LDS (own-token rows from kown), then 8 MFMAs.
-      f32x16 s;
-      {
-        bf16x8 kf[8];
-        if (!own_tail || kb + kBlk <= a.S) {  // no own-token row in the block
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk)
-            kf[kk] = *reinterpret_cast<const bf16x8*>(tile + koff[kk & 3] + 128 * (kk >> 2));
-        } else {
-          // own-token row tok stands in kown at row tok, swizzled like tile row krow
-          const int kvk = kb + krow;
-          const bool own = kvk >= a.S;
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk) {
-            const int off = koff[kk & 3] + 128 * (kk >> 2);
-            kf[kk] = *reinterpret_cast<const bf16x8*>(own ? kown + (kvk - a.S) * 256 + (off - krow * 256) : tile + off);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
-        // Keep four K reads in flight ahead of the dependent MFMA chain: 4 reads, then
-        // (MFMA, read) x 4, then the last 4 MFMAs. Left to itself the scheduler waits for
-        // each read right before its MFMA, which exposes the LDS latency eight times.
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      }
-      if (kb + kBlk > k_end) {  // only a split's last block can be partial
-        // accumulator element i of lane half h is key perm_key(8(i>>2) + 4h + (i&3)) = 8h + kofs(i)
-        const int lim = k_end - kb - 8 * h;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kofs = 16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3);
-          s[i] = (kofs < lim) ? s[i] : -INFINITY;
-        }
-      }
-      float bmax = s[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) bmax = fmaxf(bmax, s[i]);
-      {
-        const float2 pr = pair32(bmax);
-        bmax = fmaxf(pr.x, pr.y);
-      }
-      // The exponent reference m_run only moves when some row's max exceeds it by more than
-      // kRescale (log2 units): p stays below 2^kRescale, exact for the final normalisation,
-      // and the O rescale (64 multiplies) runs only on such jumps.
-      const float m_blk = bmax * sc;
-      if constexpr (b < 2) {
-        m_run = m_blk;  // this wave's first block: O and l are still zero
-      } else if (__any(m_blk > m_run + kRescale)) {
-        const float m_new = fmaxf(m_run, m_blk);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
-      }
-      // v_exp_f32 directly: arguments are <= kRescale or -inf (masked)
-      float psum = 0.f;
+    if (b == nb - 1 && kb + kBlk > k_end) {
+      // the last visible block is partial: keys past the split end get p = 0. Accumulator
+      // element i of lane half h is key perm_key(8(i>>2) + 4h + (i&3)) = 8h + kofs(i).
+      const int lim = k_end - kb - 8 * h;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sc, -m_run));
-        psum += s[i];
-      }
-      l_run += psum;
-      // O^T += V^T P^T, in two halves of 16 keys (operand layout at voff above).
-      const uint8_t* tv = tile + kTileBytes / 2;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        bf16x8 pb;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pb[j] = (__bf16)s[8 * c + j];
-        v4i16 vt[4][2];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf)
-            vt[t][hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_v4i16*)(tv + (16 * c + 4 * hf) * 256 + 128 * (t >> 1) + voff[t & 1]));
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const v4i16 both[2] = {vt[t][0], vt[t][1]};
-          bf16x8 vf;
-          __builtin_memcpy(&vf, both, 16);
-          o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[t], 0, 0, 0);
-        }
+        const int kofs = 16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3);
+        s_cur[i] = (kofs < lim) ? s_cur[i] : -INFINITY;
       }
     }
-    arrive(&cnt[kCntDone + b], lane);
+    const uint8_t* tv = pick<b>(t0, t1, t2, t3, t4, t5) + kTileBytes / 2;
+    // (A) Step by step: the V^T fragment of one PV step of block b, one score MFMA of block
+    //     b+1 and two of block b's p = 2^(s sc - m_run) (v_exp_f32 directly: the
+    //     arguments are <= kRescale or -inf) with their bf16 pair and its share of l, which
+    //     the vector ALU works through while the matrix core computes. The exponent
+    //     reference m_run only moves when some row's max exceeds it by more than kRescale
+    //     (log2 units): p stays below 2^kRescale, exact for the final normalisation, and the
+    //     O rescale (64 multiplies) runs only on such jumps.
+    //     l sums the same bf16-rounded p that the PV product uses (v_dot2_f32_bf16 against
+    //     (1, 1)), so the output is an exact convex combination of V rows; with the fp32 p a
+    //     row dominated by one key would be off by that p's rounding (up to 2^-9 of its V
+    //     row), since p of a block after the first may exceed 1.
+    //     The scheduling barriers keep this order: left alone, the compiler issues the score
+    //     chain back to back with nothing to overlap it.
+    v4i16 vt[2][4][2];
+    f32x16 s_next;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s_next[i] = 0.f;
+    bf16x8 pb[2];
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      {
+        const int c = i >> 2, t = i & 3;  // the V^T fragment of PV step i, read a step at a time
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          vt[c][t][hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16*)(tv + (16 * c + 4 * hf) * 256 + 128 * (t >> 1) + voff[t & 1]));
+      }
+      if constexpr (b + 1 < NB) s_next = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i], s_next, 0, 0, 0);
+      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[2 * i], sc, -m_run));
+      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[2 * i + 1], sc, -m_run));
+      const bf16x2_t pr = {(__bf16)e0, (__bf16)e1};
+      pb[i >> 2][2 * (i & 3)] = pr[0];
+      pb[i >> 2][2 * (i & 3) + 1] = pr[1];
+      ps[i & 3] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ps[i & 3], false);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    // (B) Step by step: one K fragment of block b+2 (past the last visible block, of a tile
+    //     nobody waits for: its scores are never used), one PV MFMA of block b (O^T += V^T P^T,
+    //     two halves of 16 keys, independent accumulators) and a share of block b+1's row
+    //     max. Spreading the LDS reads over the steps keeps the wave from stalling on
+    //     a full LDS queue with nothing else issued.
+    float mx[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (b + 2 < NB) {
+        const uint8_t* kbn = kbase(std::integral_constant<int, b + 2>{});
+        kf[i] = *reinterpret_cast<const bf16x8*>(kbn + koff[i & 3] + 128 * (i >> 2));
+      }
+      const int c = i >> 2, t = i & 3;
+      const v4i16 both[2] = {vt[c][t][0], vt[c][t][1]};
+      bf16x8 vf;
+      __builtin_memcpy(&vf, both, 16);
+      o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[c], o[t], 0, 0, 0);
+      if constexpr (b + 1 < NB) {
+        if (i < 4) mx[i] = fmaxf(s_next[2 * i], s_next[2 * i + 1]);
+        else mx[i & 3] = fmaxf(fmaxf(mx[i & 3], s_next[2 * i]), s_next[2 * i + 1]);
+        asm volatile("" : "+v"(mx[i & 3]));  // computed here, not sunk to its use after the loop
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (b + 1 < NB) {
+      if (b + 1 < nb) {
+        const float2 pr = pair32(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
+        const float m_blk = fmaxf(pr.x, pr.y) * sc;
+        if (__any(m_blk > m_run + kRescale)) {
+          const float m_new = fmaxf(m_run, m_blk);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+        }
+      }
+      s_cur = s_next;
+    }
   });
 
-  // Merge of the two parities. The odd wave's O goes to a 16 KB region that nobody reads any
-  // more: the tile of block qgrp once its four readers are done with it, or for qgrp >= NB a
-  // half of the query buffer once every compute wave holds its query fragments.
-  uint8_t* region = qlds;
-  if constexpr (NB >= 2) {
-    if (qgrp < NB) region = qgrp == 0 ? t0 : qgrp == 1 ? t1 : qgrp == 2 ? t2 : t3;
-    else region = qlds + (qgrp - NB) * kTileBytes;
-  }
-  auto region_free = [&]() {
-    if (qgrp < NB) await(&cnt[kCntDone + qgrp], 4);
-    else await(&cnt[kCntQRead], kComputeWaves);
-  };
+  // The wave's partial: O (unnormalised), m and l of query rows 32w .. +31.
   const long long part = (long long)g * a.n_split + split;
-  merge_and_store_partial(o, m_run, l_run, NB >= 2, par, qgrp, lane, region, region + kTileBytes / 2,
-                          region_free, mlx, cnt, a.po, a.pm, a.pl, part);
+  merge_and_store_partial(o, m_run, l_run, false, 0, wave, lane, nullptr, nullptr, [] {}, nullptr, cnt, a.po,
+                          a.pm, a.pl, part);
 }
 
 // Combine: out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c, M = max_c m_c.
@@ -512,9 +575,9 @@ size_t attn_partials_bytes(const AttnPlan& p) {
 template <int NB>
 static hipError_t launch_nb(const FusedArgs& a, hipStream_t st) {
   if (a.q_norm)
-    hipLaunchKernelGGL((k_attn_fused<NB, true>), dim3(kHkv * a.n_split), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((k_attn_fused<NB, true>), dim3(kHkv * a.n_split), dim3(kFThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((k_attn_fused<NB, false>), dim3(kHkv * a.n_split), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((k_attn_fused<NB, false>), dim3(kHkv * a.n_split), dim3(kFThreads), 0, st, a);
   return hipGetLastError();
 }
 
