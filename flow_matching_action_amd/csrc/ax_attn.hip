@@ -86,30 +86,33 @@ __device__ __forceinline__ uint8_t* pick(uint8_t* t0, uint8_t* t1, uint8_t* t2, 
   else return t5;
 }
 
-// RMSNorm + RoPE in place in LDS of the 8 query rows 32p + 16s + r16 (p = 0..3, s = 0..1) that
-// this lane's 16-lane group holds (columns 8 j16 .. +7); row 32p + 16s + r16 is token
-// 32(p & 1) + 16s + r16, whose RoPE coefficients are A/B[2(p & 1) + s]. All rows are read
-// before any is written back. Per row the arithmetic is that of the stand-alone kernel.
+// RMSNorm + RoPE in place in LDS of the 8 query rows 32p + 16s + r16 (p = 0..3, s = 0..1)
+// that this lane's 16-lane group holds, in the pair layout (columns 4 j16 .. +3 and
+// 64 + 4 j16 .. +3); row 32p + 16s + r16 is token 32(p & 1) + 16s + r16, whose RoPE
+// coefficients are A/B[2(p & 1) + s]. All rows are read before any is written back. Per row
+// the arithmetic is that of the stand-alone kernel.
 __device__ __forceinline__ void norm_rope_query_rows8(uint8_t* qlds, const float (&A)[4][8], const float (&B)[4][8],
                                                       int j16, int r16, float eps) {
-  u32x4 qv[8];
+  uint2 lo[8], hi[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = 32 * (i >> 1) + 16 * (i & 1) + r16;
-    qv[i] = *reinterpret_cast<const u32x4*>(qlds + r * 256 + 16 * (j16 ^ qswz(r)));
+    lo[i] = *reinterpret_cast<const uint2*>(qlds + r * 256 + pair_off_lo(j16, qswz(r)));
+    hi[i] = *reinterpret_cast<const uint2*>(qlds + r * 256 + pair_off_hi(j16, qswz(r)));
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int t = 2 * ((i >> 1) & 1) + (i & 1);
     float x[8];
-    unpack8v(qv[i], x);
-    norm_rope_row16(x, A[t], B[t], eps);
-    qv[i] = pack8v(x);
+    unpack_pair(lo[i], hi[i], x);
+    norm_rope_pair(x, A[t], B[t], eps);
+    pack_pair(x, lo[i], hi[i]);
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = 32 * (i >> 1) + 16 * (i & 1) + r16;
-    *reinterpret_cast<u32x4*>(qlds + r * 256 + 16 * (j16 ^ qswz(r))) = qv[i];
+    *reinterpret_cast<uint2*>(qlds + r * 256 + pair_off_lo(j16, qswz(r))) = lo[i];
+    *reinterpret_cast<uint2*>(qlds + r * 256 + pair_off_hi(j16, qswz(r))) = hi[i];
   }
 }
 
@@ -155,8 +158,9 @@ __global__ __launch_bounds__(kFThreads, 1) void k_attn_fused(FusedArgs a) {
   const int j16 = tid & 15;
   const int r16 = tid >> 4;
   const bool has_own = own_tail && own_split;  // this split holds the own-token rows
-  u32x4 graw, gkraw, kraw[4], vraw[4];
-  f32x4 cs_h[4][2];
+  uint2 graw[2], gkraw[2], kraw[4][2];  // pair layout: columns 4 j16 .. +3, 64 + 4 j16 .. +3
+  u32x4 vraw[4];                        // 16-byte piece j16 (columns 8 j16 .. +7)
+  f32x4 cs_h[4][2];                     // cos, sin of frequencies 4 j16 .. +3
   if (wave < kFCompute) {
     // 1. Prologue loads, all issued before the start barrier and so ahead of the cache stream
     //    in the CU's memory queue: the 32 query rows this wave norms (rows 32p + 16s + 4 wave
@@ -171,19 +175,28 @@ __global__ __launch_bounds__(kFThreads, 1) void k_attn_fused(FusedArgs a) {
       __builtin_amdgcn_global_load_lds(src, (lds_void*)(qlds + row0 * 256), 16, 0, 0);
     });
     if constexpr (NORM) {
-      graw = *reinterpret_cast<const u32x4*>(a.gq + 8 * j16);
+      graw[0] = *reinterpret_cast<const uint2*>(a.gq + 4 * j16);
+      graw[1] = *reinterpret_cast<const uint2*>(a.gq + 64 + 4 * j16);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) load_cos_sin_half(a.cos_t, a.sin_t, 16 * u + r16, j16, cs_h[u][0], cs_h[u][1]);
+      for (int u = 0; u < 4; ++u) {
+        const int tok = 16 * u + r16;
+        cs_h[u][0] = *reinterpret_cast<const f32x4*>(a.cos_t + tok * 64 + 4 * j16);
+        cs_h[u][1] = *reinterpret_cast<const f32x4*>(a.sin_t + tok * 64 + 4 * j16);
+      }
     }
     if (has_own) {
       const uint16_t* kt = a.kt_base + g * a.tail_stride;
       const uint16_t* vt = a.vt_base + g * a.tail_stride;
-      if constexpr (NORM) gkraw = *reinterpret_cast<const u32x4*>(a.gk + 8 * j16);
+      if constexpr (NORM) {
+        gkraw[0] = *reinterpret_cast<const uint2*>(a.gk + 4 * j16);
+        gkraw[1] = *reinterpret_cast<const uint2*>(a.gk + 64 + 4 * j16);
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int tok = 16 * u + r16;
-        kraw[u] = *reinterpret_cast<const u32x4*>(kt + (long long)tok * kD + 8 * j16);
-        vraw[u] = *reinterpret_cast<const u32x4*>(vt + (long long)tok * kD + 8 * j16);
+        const uint16_t* krow_p = kt + (long long)(16 * u + r16) * kD;
+        kraw[u][0] = *reinterpret_cast<const uint2*>(krow_p + 4 * j16);
+        kraw[u][1] = *reinterpret_cast<const uint2*>(krow_p + 64 + 4 * j16);
+        vraw[u] = *reinterpret_cast<const u32x4*>(vt + (long long)(16 * u + r16) * kD + 8 * j16);
       }
     }
   }
@@ -234,18 +247,21 @@ __global__ __launch_bounds__(kFThreads, 1) void k_attn_fused(FusedArgs a) {
   }
 
   // ---------------- compute waves (256 threads)
-  float qc[4][8], qs[4][8];
-  if constexpr (NORM) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) split_cos_sin(cs_h[u][0], cs_h[u][1], j16, qc[u], qs[u]);
-  }
   // 2. the query rows, normed and roped in place in LDS (unless they came roped)
   wait_vmcnt<0>();  // this wave's query rows and every prologue load have landed
+  float qc[4][4], qs[4][4];
   if constexpr (NORM) {
-    float qg[8], A[4][8], B[4][8];
-    unpack8v(graw, qg);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) rope_coef(qg, qc[u], qs[u], j16, A[u], B[u]);
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qc[u][e] = cs_h[u][0][e];
+        qs[u][e] = cs_h[u][1][e];
+      }
+    float qg[8], A[4][8], B[4][8];
+    unpack_pair(graw[0], graw[1], qg);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) rope_coef_pair(qg, qc[u], qs[u], A[u], B[u]);
     norm_rope_query_rows8(qlds, A, B, j16, r16, a.eps);
   }
   // 3. own-token rows (own split only): K normed + roped (or taken roped) into kown and the
@@ -253,22 +269,25 @@ __global__ __launch_bounds__(kFThreads, 1) void k_attn_fused(FusedArgs a) {
   //    waited for, so no later wait includes them)
   if (has_own) {
     float gk[8];
-    if constexpr (NORM) unpack8v(gkraw, gk);
+    if constexpr (NORM) unpack_pair(gkraw[0], gkraw[1], gk);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int tok = 16 * u + r16;
-      u32x4 kv = kraw[u];
+      uint2 klo = kraw[u][0], khi = kraw[u][1];
       if constexpr (NORM) {
         float x[8], A[8], B[8];
-        unpack8v(kv, x);
-        rope_coef(gk, qc[u], qs[u], j16, A, B);
-        norm_rope_row16(x, A, B, a.eps);
-        kv = pack8v(x);
+        unpack_pair(klo, khi, x);
+        rope_coef_pair(gk, qc[u], qs[u], A, B);
+        norm_rope_pair(x, A, B, a.eps);
+        pack_pair(x, klo, khi);
       }
-      *reinterpret_cast<u32x4*>(kown + tok * 256 + 16 * (j16 ^ kswz(tok & (kBlk - 1)))) = kv;
-      const long long dst = head_off + (long long)(a.Smax - kT + tok) * kD + 8 * j16;
-      *reinterpret_cast<u32x4*>(a.Kc + dst) = kv;
-      *reinterpret_cast<u32x4*>(a.Vc + dst) = vraw[u];
+      uint8_t* kr = kown + tok * 256;  // swizzled like tile row tok % 32
+      *reinterpret_cast<uint2*>(kr + pair_off_lo(j16, kswz(tok & (kBlk - 1)))) = klo;
+      *reinterpret_cast<uint2*>(kr + pair_off_hi(j16, kswz(tok & (kBlk - 1)))) = khi;
+      const long long dst = head_off + (long long)(a.Smax - kT + tok) * kD;
+      *reinterpret_cast<uint2*>(a.Kc + dst + 4 * j16) = klo;
+      *reinterpret_cast<uint2*>(a.Kc + dst + 64 + 4 * j16) = khi;
+      *reinterpret_cast<u32x4*>(a.Vc + dst + 8 * j16) = vraw[u];
     }
   }
   arrive(&cnt[kCntQNormed], lane);

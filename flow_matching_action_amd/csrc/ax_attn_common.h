@@ -139,31 +139,38 @@ __device__ __forceinline__ u32x4 pack8v(const float* f) {
 
 
 // RMSNorm + RoPE in place in LDS of the query rows 32p + r16 (p = 0..3) that this lane's
-// 16-lane group holds (columns 8 j16 .. +7), rows swizzled by qswz. graw: the 8 gammas of the
-// lane; qc/qs: cos/sin of token sets p & 1. All rows are read before any is written back.
-__device__ __forceinline__ void norm_rope_query_rows(uint8_t* qlds, const u32x4& graw, const float (&qc)[2][8],
-                                                     const float (&qs)[2][8], int j16, int r16, float eps) {
+// 16-lane group holds, in the pair layout (columns 4 j16 .. +3 and 64 + 4 j16 .. +3), rows
+// swizzled by qswz. graw: the lane's 8 gammas in that layout; cs[t]: cos, sin of frequencies
+// 4 j16 .. +3 of token set t = p & 1. All rows are read before any is written back.
+__device__ __forceinline__ void norm_rope_query_rows(uint8_t* qlds, const uint2 (&graw)[2], const f32x4 (&cs)[2][2],
+                                                     int j16, int r16, float eps) {
   float qg[8], A[2][8], B[2][8];
-  unpack8v(graw, qg);
+  unpack_pair(graw[0], graw[1], qg);
 #pragma unroll
-  for (int p = 0; p < 2; ++p) rope_coef(qg, qc[p], qs[p], j16, A[p], B[p]);
-  u32x4 qv[4];
+  for (int t = 0; t < 2; ++t) {
+    const float c[4] = {cs[t][0][0], cs[t][0][1], cs[t][0][2], cs[t][0][3]};
+    const float sn[4] = {cs[t][1][0], cs[t][1][1], cs[t][1][2], cs[t][1][3]};
+    rope_coef_pair(qg, c, sn, A[t], B[t]);
+  }
+  uint2 lo[4], hi[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int r = 32 * p + r16;
-    qv[p] = *reinterpret_cast<const u32x4*>(qlds + r * 256 + 16 * (j16 ^ qswz(r)));
+    lo[p] = *reinterpret_cast<const uint2*>(qlds + r * 256 + pair_off_lo(j16, qswz(r)));
+    hi[p] = *reinterpret_cast<const uint2*>(qlds + r * 256 + pair_off_hi(j16, qswz(r)));
   }
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     float x[8];
-    unpack8v(qv[p], x);
-    norm_rope_row16(x, A[p & 1], B[p & 1], eps);
-    qv[p] = pack8v(x);
+    unpack_pair(lo[p], hi[p], x);
+    norm_rope_pair(x, A[p & 1], B[p & 1], eps);
+    pack_pair(x, lo[p], hi[p]);
   }
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int r = 32 * p + r16;
-    *reinterpret_cast<u32x4*>(qlds + r * 256 + 16 * (j16 ^ qswz(r))) = qv[p];
+    *reinterpret_cast<uint2*>(qlds + r * 256 + pair_off_lo(j16, qswz(r))) = lo[p];
+    *reinterpret_cast<uint2*>(qlds + r * 256 + pair_off_hi(j16, qswz(r))) = hi[p];
   }
 }
 

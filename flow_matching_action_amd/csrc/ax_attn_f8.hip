@@ -175,56 +175,79 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_f8(F8Args a) {
   const int j16 = tid & 15;
   const int r16 = tid >> 4;  // 0..31
   const bool has_own = own_tail && own_split;
-  u32x4 graw, gkraw, kraw[2], vraw[2];
-  f32x4 cs_h[2][2];
+  // Raw q / own k are held in the pair layout (columns 4 j16 .. +3 and 64 + 4 j16 .. +3) when
+  // normed here, the v rows (and a k that arrives roped) as 16-byte pieces j16.
+  uint2 graw[2], gkraw[2], kpair[2][2];
+  u32x4 kraw[2], vraw[2];
+  f32x4 cs_h[2][2];  // cos, sin of frequencies 4 j16 .. +3 of tokens r16 and 32 + r16
   if constexpr (NORM) {
-    graw = *reinterpret_cast<const u32x4*>(a.gq + 8 * j16);
-#pragma unroll
-    for (int p = 0; p < 2; ++p) load_cos_sin_half(a.cos_t, a.sin_t, 32 * p + r16, j16, cs_h[p][0], cs_h[p][1]);
-  }
-  if (has_own) {
-    if constexpr (NORM) gkraw = *reinterpret_cast<const u32x4*>(a.gk + 8 * j16);
+    graw[0] = *reinterpret_cast<const uint2*>(a.gq + 4 * j16);
+    graw[1] = *reinterpret_cast<const uint2*>(a.gq + 64 + 4 * j16);
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const long long tok_off = ((long long)g * kT + 32 * p + r16) * kD + 8 * j16;
-      kraw[p] = *reinterpret_cast<const u32x4*>(a.k_own + tok_off);
-      vraw[p] = *reinterpret_cast<const u32x4*>(a.v_own + tok_off);
+      const int tok = 32 * p + r16;
+      cs_h[p][0] = *reinterpret_cast<const f32x4*>(a.cos_t + tok * 64 + 4 * j16);
+      cs_h[p][1] = *reinterpret_cast<const f32x4*>(a.sin_t + tok * 64 + 4 * j16);
     }
   }
-  float qc[2][8], qs[2][8];
-  if constexpr (NORM) {
+  if (has_own) {
+    if constexpr (NORM) {
+      gkraw[0] = *reinterpret_cast<const uint2*>(a.gk + 4 * j16);
+      gkraw[1] = *reinterpret_cast<const uint2*>(a.gk + 64 + 4 * j16);
+    }
 #pragma unroll
-    for (int p = 0; p < 2; ++p) split_cos_sin(cs_h[p][0], cs_h[p][1], j16, qc[p], qs[p]);
+    for (int p = 0; p < 2; ++p) {
+      const long long tok_off = ((long long)g * kT + 32 * p + r16) * kD;
+      if constexpr (NORM) {
+        kpair[p][0] = *reinterpret_cast<const uint2*>(a.k_own + tok_off + 4 * j16);
+        kpair[p][1] = *reinterpret_cast<const uint2*>(a.k_own + tok_off + 64 + 4 * j16);
+      } else {
+        kraw[p] = *reinterpret_cast<const u32x4*>(a.k_own + tok_off + 8 * j16);
+      }
+      vraw[p] = *reinterpret_cast<const u32x4*>(a.v_own + tok_off + 8 * j16);
+    }
   }
   wait_vmcnt<0>();  // its query rows and every prologue load have landed
-  if constexpr (NORM) norm_rope_query_rows(qlds, graw, qc, qs, j16, r16, a.eps);
+  if constexpr (NORM) norm_rope_query_rows(qlds, graw, cs_h, j16, r16, a.eps);
   // own tokens (the own split only): k normed + roped (or taken roped) and rounded to bf16, v
   // as given; each row quantised into the own blocks' tiles, the scales into LDS, both into
   // the cache tail. Token tok is key tok of the split: block tok / 32, row tok % 32.
   if (has_own) {
     float gk[8];
-    if constexpr (NORM) unpack8v(gkraw, gk);
+    if constexpr (NORM) unpack_pair(gkraw[0], gkraw[1], gk);
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int tok = 32 * p + r16;
       const int r = tok & (kBlk - 1);
-      float x[8];
-      unpack8v(kraw[p], x);
+      const long long crow = head_row + a.Smax - kT + tok;
+      uint8_t* tile = &tiles[p][0];
+      float x[8], sk, sv;
       if constexpr (NORM) {
+        // normed and roped in the pair layout, rounded to bf16 (the activation format),
+        // quantised; the lane's codes are columns 4 j16 .. +3 and 64 + 4 j16 .. +3
         float A[8], B[8];
-        rope_coef(gk, qc[p], qs[p], j16, A, B);
-        norm_rope_row16(x, A, B, a.eps);
-        unpack8v(pack8v(x), x);  // the roped k in the activation format (bf16)
+        const float c[4] = {cs_h[p][0][0], cs_h[p][0][1], cs_h[p][0][2], cs_h[p][0][3]};
+        const float sn[4] = {cs_h[p][1][0], cs_h[p][1][1], cs_h[p][1][2], cs_h[p][1][3]};
+        unpack_pair(kpair[p][0], kpair[p][1], x);
+        rope_coef_pair(gk, c, sn, A, B);
+        norm_rope_pair(x, A, B, a.eps);
+        uint2 lo, hi;
+        pack_pair(x, lo, hi);
+        unpack_pair(lo, hi, x);
+        const uint2 ck = quant_row16(x, sk);
+        *reinterpret_cast<uint32_t*>(tile + r * kD + 16 * ((j16 >> 2) ^ kswz(r)) + 4 * (j16 & 3)) = ck.x;
+        *reinterpret_cast<uint32_t*>(tile + r * kD + 16 * ((4 + (j16 >> 2)) ^ kswz(r)) + 4 * (j16 & 3)) = ck.y;
+        *reinterpret_cast<uint32_t*>(a.Kc + crow * kD + 4 * j16) = ck.x;
+        *reinterpret_cast<uint32_t*>(a.Kc + crow * kD + 64 + 4 * j16) = ck.y;
+      } else {
+        unpack8v(kraw[p], x);
+        const uint2 ck = quant_row16(x, sk);
+        *reinterpret_cast<uint2*>(tile + r * kD + 16 * ((j16 >> 1) ^ kswz(r)) + 8 * (j16 & 1)) = ck;
+        *reinterpret_cast<uint2*>(a.Kc + crow * kD + 8 * j16) = ck;
       }
-      float sk, sv;
-      const uint2 ck = quant_row16(x, sk);
       unpack8v(vraw[p], x);
       const uint2 cv = quant_row16(x, sv);
-      uint8_t* tile = &tiles[p][0];
-      *reinterpret_cast<uint2*>(tile + r * kD + 16 * ((j16 >> 1) ^ kswz(r)) + 8 * (j16 & 1)) = ck;
       *reinterpret_cast<uint2*>(tile + kVOff8 + r * kD + 16 * ((j16 >> 1) ^ vswz8(r)) + 8 * (j16 & 1)) = cv;
-      const long long crow = head_row + a.Smax - kT + tok;
-      *reinterpret_cast<uint2*>(a.Kc + crow * kD + 8 * j16) = ck;
       *reinterpret_cast<uint2*>(a.Vc + crow * kD + 8 * j16) = cv;
       if (j16 == 0) {
         scl[p][r >> 3][r & 7] = sk;

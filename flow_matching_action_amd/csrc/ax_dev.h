@@ -108,4 +108,54 @@ __device__ __forceinline__ void norm_rope_row16(float* x, const float* A, const 
   for (int e = 0; e < 8; ++e) x[e] = inv * __builtin_fmaf(p[e], B[e], x[e] * A[e]);
 }
 
+// The same RMSNorm + RoPE in the pair layout: lane j16 of a row's 16-lane group holds
+// columns 4 j16 .. +3 (x[0..3]) and 64 + 4 j16 .. +3 (x[4..7]), so both members of every
+// RoPE pair (j, j + 64) sit in one lane and the rotation needs no lane moves; the RoPE rows
+// a lane needs are the 4 frequencies 4 j16 .. +3, one float4 of cosines and one of sines.
+// g: the 8 gammas in that layout; c, s: cos/sin of frequencies 4 j16 .. +3.
+__device__ __forceinline__ void rope_coef_pair(const float* g, const float* c, const float* s, float* A,
+                                               float* B) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    A[e] = g[e] * c[e];              // column j:      x_j c_j - x_{j+64} s_j
+    B[e] = (-g[4 + e]) * s[e];
+    A[4 + e] = g[4 + e] * c[e];      // column j + 64: x_{j+64} c_j + x_j s_j
+    B[4 + e] = g[e] * s[e];
+  }
+}
+
+// x: the 8 inputs in the pair layout, replaced by the outputs. The sum of squares is a
+// rotate-by-8/4/2/1 butterfly over the 16 lanes, which leaves the same bits in all of them.
+__device__ __forceinline__ void norm_rope_pair(float* x, const float* A, const float* B, float eps) {
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+  ss += row_ror<8>(ss);
+  ss += row_ror<4>(ss);
+  ss += row_ror<2>(ss);
+  ss += row_ror<1>(ss);
+  const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / kD) + eps);  // v_rsq_f32
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = inv * __builtin_fmaf(x[e ^ 4], B[e], x[e] * A[e]);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = y[e];
+}
+
+// Pair-layout row access: the lane's two 8-byte pieces (4 bf16 each) of a bf16 row.
+__device__ __forceinline__ void unpack_pair(const uint2& lo, const uint2& hi, float* x) {
+  x[0] = __uint_as_float(lo.x << 16); x[1] = __uint_as_float(lo.x & 0xffff0000u);
+  x[2] = __uint_as_float(lo.y << 16); x[3] = __uint_as_float(lo.y & 0xffff0000u);
+  x[4] = __uint_as_float(hi.x << 16); x[5] = __uint_as_float(hi.x & 0xffff0000u);
+  x[6] = __uint_as_float(hi.y << 16); x[7] = __uint_as_float(hi.y & 0xffff0000u);
+}
+__device__ __forceinline__ void pack_pair(const float* x, uint2& lo, uint2& hi) {
+  lo = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+  hi = make_uint2(pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
+}
+// Byte offsets of the two pieces in a 256-byte row whose 16-byte chunks are XOR-swizzled by
+// sw (chunk c of the row lives at chunk c ^ sw).
+__device__ __forceinline__ int pair_off_lo(int j16, int sw) { return 16 * ((j16 >> 1) ^ sw) + 8 * (j16 & 1); }
+__device__ __forceinline__ int pair_off_hi(int j16, int sw) { return 16 * ((8 + (j16 >> 1)) ^ sw) + 8 * (j16 & 1); }
+
 }  // namespace ax

@@ -5,10 +5,12 @@
 // the raw v at row Smax - 64 of the layer's cache (EXPERT_NOTES.md, "Attention
 // over the VLM cache: masking approach").
 //
-// Layout of the work: a 16-lane group owns one 128-wide row (8 bf16 per lane,
-// one 16-byte load). Rows 0..1023 are q (head h = r / 64, token r % 64), rows
-// 1024..1535 are k, rows 1536..2047 are v (copied, not normed). 256-thread
-// blocks, 16 rows each: 128 blocks for a full step.
+// Layout of the work: a 16-lane group owns one 128-wide row. Rows 0..1023 are q (head
+// h = r / 64, token r % 64), rows 1024..1535 are k, rows 1536..2047 are v (copied, not
+// normed, one 16-byte piece per lane). A q or k row is held in the pair layout (lane j16:
+// columns 4 j16 .. +3 and 64 + 4 j16 .. +3, two 8-byte pieces), the arithmetic the fused
+// attention kernels use too, so both paths give the same bits. 256-thread blocks, 16 rows
+// each: 128 blocks for a full step.
 #include "ax_dev.h"
 #include "ax_launch.h"
 
@@ -47,29 +49,30 @@ __global__ __launch_bounds__(256) void k_qk_norm_rope(QkArgs a) {
   const int tok = rr & (kT - 1);
   const int head = rr >> 6;
 
-  const uint16_t* src = is_q ? a.q_in : (is_k ? a.k_in : a.v_in);
-  const uint4 raw = *reinterpret_cast<const uint4*>(src + (long long)rr * kD + 8 * j16);
+  const uint16_t* src = (is_q ? a.q_in : (is_k ? a.k_in : a.v_in)) + (long long)rr * kD;
   if (is_q || is_k) {
-    float x[8], g[8], c[8], s[8];
-    unpack8(raw, x);
-    unpack8(*reinterpret_cast<const uint4*>((is_q ? a.gq : a.gk) + 8 * j16), g);
-    const int f0 = 8 * (j16 & 7);
-    const float4* cp = reinterpret_cast<const float4*>(a.cos_t + tok * 64 + f0);
-    const float4* sp = reinterpret_cast<const float4*>(a.sin_t + tok * 64 + f0);
-    const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
-    c[0] = c0.x; c[1] = c0.y; c[2] = c0.z; c[3] = c0.w; c[4] = c1.x; c[5] = c1.y; c[6] = c1.z; c[7] = c1.w;
-    s[0] = s0.x; s[1] = s0.y; s[2] = s0.z; s[3] = s0.w; s[4] = s1.x; s[5] = s1.y; s[6] = s1.z; s[7] = s1.w;
-    float A[8], B[8];
-    rope_coef(g, c, s, j16, A, B);
-    norm_rope_row16(x, A, B, a.eps);
+    float x[8], g[8], A[8], B[8];
+    unpack_pair(*reinterpret_cast<const uint2*>(src + 4 * j16), *reinterpret_cast<const uint2*>(src + 64 + 4 * j16),
+                x);
+    const uint16_t* gam = is_q ? a.gq : a.gk;
+    unpack_pair(*reinterpret_cast<const uint2*>(gam + 4 * j16), *reinterpret_cast<const uint2*>(gam + 64 + 4 * j16),
+                g);
+    const float4 c4 = *reinterpret_cast<const float4*>(a.cos_t + tok * 64 + 4 * j16);
+    const float4 s4 = *reinterpret_cast<const float4*>(a.sin_t + tok * 64 + 4 * j16);
+    const float c[4] = {c4.x, c4.y, c4.z, c4.w}, s[4] = {s4.x, s4.y, s4.z, s4.w};
+    rope_coef_pair(g, c, s, A, B);
+    norm_rope_pair(x, A, B, a.eps);
     if (live) {
       uint16_t* dst = is_q ? a.q_out + (long long)rr * kD
                            : a.k_dst + head * a.kv_head_stride + (a.kv_row0 + tok) * kD;
-      *reinterpret_cast<uint4*>(dst + 8 * j16) = pack8(x);
+      uint2 lo, hi;
+      pack_pair(x, lo, hi);
+      *reinterpret_cast<uint2*>(dst + 4 * j16) = lo;
+      *reinterpret_cast<uint2*>(dst + 64 + 4 * j16) = hi;
     }
   } else if (live) {
     uint16_t* dst = a.v_dst + head * a.kv_head_stride + (a.kv_row0 + tok) * kD;
-    *reinterpret_cast<uint4*>(dst + 8 * j16) = raw;
+    *reinterpret_cast<uint4*>(dst + 8 * j16) = *reinterpret_cast<const uint4*>(src + 8 * j16);
   }
 }
 
