@@ -114,7 +114,8 @@ def test_layer_matches_oracle(ax, w):
 
 
 @pytest.mark.parametrize("S,Smax", [(0, 64), (0, 256), (1, 128), (31, 160), (33, 200), (63, 4096), (191, 256),
-                                    (4095, 4160), (2050, 4000), (8128, 8192), (60000, 65536)])
+                                    (4095, 4160), (2050, 4000), (3000, 3072), (3500, 4096), (8128, 8192),
+                                    (60000, 65536)])
 def test_layer_edge_shapes(ax, S, Smax):
     inp = synth.layer_inputs(Smax, S, seed=1000 + S)
     say(f"expert_layer_attn edge S={S} Smax={Smax}")
