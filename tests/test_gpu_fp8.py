@@ -137,7 +137,8 @@ def test_fp8_layer_matches_oracle(ax, S, Smax):
 
 
 @pytest.mark.parametrize("S,Smax", [(0, 64), (0, 256), (1, 128), (31, 160), (33, 200), (191, 256), (2050, 4000),
-                                    (11904, 12288), (12000, 12288)])
+                                    (3500, 3584), (5500, 5568), (6500, 6592), (7500, 7616), (9000, 9088),
+                                    (10000, 10112), (11904, 12288), (12000, 12288)])
 def test_fp8_layer_edge_shapes(ax, S, Smax):
     # one cache split through twelve 32-key blocks and splits with a partial last block
     inp = synth.layer_inputs_fp8(Smax, S, seed=2000 + S)
