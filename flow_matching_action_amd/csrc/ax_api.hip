@@ -140,7 +140,7 @@ int ax_expert_attn(const uint16_t* q_roped, const uint16_t* k_own, const uint16_
   if (r != AX_OK) return r;
   const ax::AttnPlan plan = ax::attn_plan(S, Smax);
   ax::AttnLaunch p{q_roped, nullptr, nullptr, nullptr, nullptr, 0.f, k_own, v_own, Kc, Vc, out, ws, S, Smax,
-                   /*q_norm=*/0, /*tail_norm=*/0};
+                   /*q_norm=*/0};
   return status(ax::launch_attn(plan, p, as_stream(stream)));
 }
 
@@ -156,7 +156,7 @@ int ax_expert_layer_attn(const uint16_t* q_in, const uint16_t* k_in, const uint1
   if (r != AX_OK) return r;
   const ax::AttnPlan plan = ax::attn_plan(S, Smax);
   ax::AttnLaunch p{q_in, gamma_q, gamma_k, rope_cos, rope_sin, eps, k_in, v_in, Kc, Vc, out, ws, S, Smax,
-                   /*q_norm=*/1, /*tail_norm=*/1};
+                   /*q_norm=*/1};
   return status(ax::launch_attn(plan, p, as_stream(stream)));
 }
 
@@ -172,7 +172,7 @@ int ax_expert_layer_attn_split(const uint16_t* q_in, const uint16_t* k_in, const
   if (r != AX_OK) return r;
   const ax::AttnPlan plan = ax::attn_plan(S, Smax);
   ax::AttnLaunch p{q_in, gamma_q, gamma_k, rope_cos, rope_sin, eps, k_in, v_in, Kc, Vc, nullptr, ws, S, Smax,
-                   /*q_norm=*/1, /*tail_norm=*/1};
+                   /*q_norm=*/1};
   return status(ax::launch_attn_split(plan, p, as_stream(stream)));
 }
 

@@ -69,7 +69,7 @@ struct FusedArgs {
   float* pl;
   int S, Smax, n_split, kps;
   int n_cache_split;       // splits over cache keys [0, S); split n_cache_split holds the 64 own tokens
-  int q_norm, tail_norm;
+  int q_norm;
 };
 
 // The LDS tiles are distinct objects so that the compiler's wait counting can tell the
@@ -637,7 +637,7 @@ hipError_t launch_attn_split(const AttnPlan& plan, const AttnLaunch& p, hipStrea
   a.po = l.po; a.pm = l.pm; a.pl = l.pl;
   a.S = p.S; a.Smax = p.Smax; a.n_split = plan.n_split; a.kps = plan.keys_per_split;
   a.n_cache_split = plan.n_cache_split;
-  a.q_norm = p.q_norm; a.tail_norm = p.tail_norm;
+  a.q_norm = p.q_norm;
   hipError_t e;
   switch (plan.blocks) {
     case 1: e = launch_nb<1>(a, st); break;

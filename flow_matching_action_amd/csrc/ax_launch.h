@@ -49,19 +49,19 @@ WsLayout ws_layout(const AttnPlan& plan, const void* ws);
 
 struct AttnLaunch {
   const uint16_t* q;       // [16][64][128] (== folded [8][128][128]): raw if q_norm, else roped
-  const uint16_t* gq;      // RMSNorm gammas (used when q_norm / tail_norm)
+  const uint16_t* gq;      // RMSNorm gammas (used when q_norm)
   const uint16_t* gk;
   const float* cos_t;      // RoPE tables [64][64]
   const float* sin_t;
   float eps;
-  const uint16_t* k_tail;  // own k [8][64][128] (raw if tail_norm, else roped), or null: tail already in Kc
+  const uint16_t* k_tail;  // own k [8][64][128] (raw if q_norm, else roped), or null: tail already in Kc
   const uint16_t* v_tail;  // own v, or null
   uint16_t* Kc;
   uint16_t* Vc;
   uint16_t* out;           // [8][128][128]
   void* ws;                // partials
   int S, Smax;
-  int q_norm, tail_norm;
+  int q_norm;              // q and the own k arrive raw and are normed + roped in the kernel
 };
 
 // fp8 cache: e4m3 codes [8][Smax][128] with a float32 scale per (kv head, row) [8][Smax].

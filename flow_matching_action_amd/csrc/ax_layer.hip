@@ -481,7 +481,7 @@ hipError_t launch_layer(const LayerLaunch& p, hipStream_t st) {
   AX_TRY(launch_reduce<kEpiQkvSplit>(l.part, gemm_splits(kCfgQkv, kLayerHidden), kLayerQkv, nullptr, l.q, l.k, l.v,
                                      st));
   AttnLaunch a{l.q, p.qn, p.kn, p.cos_t, p.sin_t, p.eps, l.k, l.v, p.Kc, p.Vc, l.attn, l.attn_ws, p.S, p.Smax,
-               /*q_norm=*/1, /*tail_norm=*/1};
+               /*q_norm=*/1};
   AX_TRY(launch_attn(plan, a, st));
   launch_gemm_cfg<kCfgO.nb, kCfgO.kw, kCfgO.steps, true>(l.attn, 0, p.wo, nullptr, kHq * 128, kLayerHidden, l.part,
                                                          st);
