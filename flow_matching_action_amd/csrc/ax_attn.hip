@@ -64,7 +64,7 @@ struct FusedArgs {
   int own_tail;            // own rows come from k/v tensors: norm (if NORM) and write them to the cache tail
   uint16_t* Kc;
   uint16_t* Vc;
-  float* po;               // [8][n_split][4 query groups][16 slots][64 lanes]: 4 floats of O each
+  float* po;               // [8][n_split][4 query groups][16 slots][64 lanes]: 4 float16 of O each
   float* pm;               // [8][n_split][128]
   float* pl;
   int S, Smax, n_split, kps;
@@ -511,9 +511,9 @@ __global__ __launch_bounds__(512) void k_attn_combine(const float* po, const flo
   const int slot = 4 * tt + jj, lane = (q & 31) + 32 * h;
   const float* pmg = pm + (long long)g * n_split * kQRows + q;
   const float* plg = pl + (long long)g * n_split * kQRows + q;
-  const f32x4* pog = reinterpret_cast<const f32x4*>(po) + ((long long)g * n_split * 4 + (q >> 5)) * (16 * 64) +
+  const u32x2* pog = reinterpret_cast<const u32x2*>(po) + ((long long)g * n_split * 4 + (q >> 5)) * (16 * 64) +
                      slot * 64 + lane;
-  const long long pstride = 4 * 16 * 64;  // float4s per split partial
+  const long long pstride = 4 * 16 * 64;  // 4-float16 groups per split partial
   float M = -INFINITY, L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int c0 = grp; c0 < n_split; c0 += kCombGroups * kCombBatch) {
@@ -524,7 +524,7 @@ __global__ __launch_bounds__(512) void k_attn_combine(const float* po, const flo
       const int c = min(c0 + kCombGroups * k, n_split - 1);  // past the end: a repeat, weighted 0 below
       mv[k] = pmg[(long long)c * kQRows];
       lv[k] = plg[(long long)c * kQRows];
-      ov[k] = pog[(long long)c * pstride];
+      ov[k] = unpack_f16x4(pog[(long long)c * pstride]);
     }
     __builtin_amdgcn_sched_barrier(0);  // every load of the batch is issued before any is used
     float Mb = M;
@@ -588,7 +588,7 @@ static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t attn_partials_bytes(const AttnPlan& p) {
   const size_t parts = (size_t)kHkv * p.n_split;
-  return align256(parts * kD * kQRows * 4) + 2 * align256(parts * kQRows * 4);
+  return align256(parts * kD * kQRows * 2) + 2 * align256(parts * kQRows * 4);
 }
 
 template <int NB>
@@ -605,8 +605,8 @@ WsLayout ws_layout(const AttnPlan& plan, const void* ws) {
   char* w = static_cast<char*>(const_cast<void*>(ws));
   WsLayout l;
   l.po = reinterpret_cast<float*>(w);
-  l.pm = reinterpret_cast<float*>(w + align256(parts * kD * kQRows * 4));
-  l.pl = reinterpret_cast<float*>(w + align256(parts * kD * kQRows * 4) + align256(parts * kQRows * 4));
+  l.pm = reinterpret_cast<float*>(w + align256(parts * kD * kQRows * 2));
+  l.pl = reinterpret_cast<float*>(w + align256(parts * kD * kQRows * 2) + align256(parts * kQRows * 4));
   return l;
 }
 

@@ -175,38 +175,72 @@ __device__ __forceinline__ void norm_rope_query_rows(uint8_t* qlds, const uint2 
 }
 
 
+// Split partials in float16. Per (split, query row) O is scaled by 2^-e, with 2^e the power of
+// two just above the row's largest |O| (max |O 2^-e| in [0.5, 1)), and e is added to m and l
+// is scaled with O: the combine's sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c is unchanged,
+// every finite O fits, and each element keeps float16's relative precision against the row's
+// largest value (2^-12 of max |O|, below the bf16 rounding of the output).
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 pack_f16x4(float a, float b, float c, float d) {
+  const f16x4 v = {(_Float16)a, (_Float16)b, (_Float16)c, (_Float16)d};  // nearest even
+  return __builtin_bit_cast(u32x2, v);
+}
+__device__ __forceinline__ f32x4 unpack_f16x4(const u32x2& u) {
+  const f16x4 v = __builtin_bit_cast(f16x4, u);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+// Store of one wave's partial for query rows 32 qgrp .. +31 (lane (n, h): row n, the half h of
+// the accumulator layout): O at po + ((part * 4 + qgrp) * 16 + j) * 64 + lane in 8-byte units
+// (slot j = 4t + jj, 4 float16 each, non-temporal: the combine reads it once), m and l at
+// pm / pl + part * 128 + query row. l_tot is the row's whole sum (both halves).
+__device__ __forceinline__ void store_partial_f16(const f32x16 (&o)[4], float m, float l_tot, int qgrp, int lane,
+                                                  float* po_all, float* pm, float* pl, long long part) {
+  const int n = lane & 31;
+  const int h = lane >> 5;
+  float amax = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(o[t][i]));
+  const float2 ap = pair32(amax);
+  const int e = __builtin_amdgcn_frexp_expf(fmaxf(ap.x, ap.y));  // 0 for an all-zero row
+  const float scale = __builtin_ldexpf(1.0f, -e);
+  u32x2* po = reinterpret_cast<u32x2*>(po_all) + (part * 4 + qgrp) * (16 * 64) + lane;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      __builtin_nontemporal_store(pack_f16x4(o[t][4 * jj] * scale, o[t][4 * jj + 1] * scale, o[t][4 * jj + 2] * scale,
+                                             o[t][4 * jj + 3] * scale),
+                                  &po[(4 * t + jj) * 64]);
+  if (h == 0) {
+    const int qrow = 32 * qgrp + n;
+    __builtin_nontemporal_store(m + (float)e, &pm[part * kQRows + qrow]);
+    __builtin_nontemporal_store(l_tot * scale, &pl[part * kQRows + qrow]);
+  }
+}
+
 // End of a split: the two parity waves of query group qgrp hold (m, l, O) over disjoint
 // blocks. The odd wave hands its O (16 KB: slot j = 4t + jj of the accumulator layout, 1 KB
 // per slot, slots 0..7 at xlo and 8..15 at xhi) and (m, l) to the even one through LDS, once
 // region_free() says nobody reads those regions any more; the even wave rescales both to
-// the larger m and stores the split's partial (float32, non-temporal: the combine reads it
-// once). With a single block (two_parities false) the odd wave holds nothing.
-// Partial layout: O at po + ((part * 4 + qgrp) * 16 + j) * 64 + lane (float4 units), m and l
-// at pm / pl + part * 128 + query row.
+// the larger m and stores the split's partial (store_partial_f16). With a single block
+// (two_parities false) the odd wave holds nothing.
 template <typename RegionFree>
-__device__ __forceinline__ void merge_and_store_partial(const f32x16 (&o)[4], float m_run, float l_run,
+__device__ __forceinline__ void merge_and_store_partial(f32x16 (&o)[4], float m_run, float l_run,
                                                         bool two_parities, int par, int qgrp, int lane,
                                                         uint8_t* xlo, uint8_t* xhi, RegionFree&& region_free,
                                                         float (*mlx)[2][32], int* cnt, float* po_all,
                                                         float* pm, float* pl, long long part) {
   const int n = lane & 31;
   const int h = lane >> 5;
-  const int qrow = 32 * qgrp + n;
   const float2 l_pair = pair32(l_run);
   const float l_tot = l_pair.x + l_pair.y;
-  f32x4* po = reinterpret_cast<f32x4*>(po_all) + (part * 4 + qgrp) * (16 * 64) + lane;
   if (!two_parities) {
     if (par == 1) return;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        __builtin_nontemporal_store(f32x4{o[t][4 * jj], o[t][4 * jj + 1], o[t][4 * jj + 2], o[t][4 * jj + 3]},
-                                    &po[(4 * t + jj) * 64]);
-    if (h == 0) {
-      __builtin_nontemporal_store(m_run, &pm[part * kQRows + qrow]);
-      __builtin_nontemporal_store(l_tot, &pl[part * kQRows + qrow]);
-    }
+    store_partial_f16(o, m_run, l_tot, qgrp, lane, po_all, pm, pl, part);
     return;
   }
   auto slot = [&](int j) { return reinterpret_cast<f32x4*>(j < 8 ? xlo + j * 1024 : xhi + (j - 8) * 1024) + lane; };
@@ -230,21 +264,15 @@ __device__ __forceinline__ void merge_and_store_partial(const f32x16 (&o)[4], fl
   const float m_new = fmaxf(m_run, m_o);  // m_run is finite: block 0 holds a visible key
   const float ae = __builtin_amdgcn_exp2f(m_run - m_new);
   const float ao = __builtin_amdgcn_exp2f(m_o - m_new);  // 0 if the odd wave saw no key
-  const float l_all = ae * l_tot + ao * l_o;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const f32x4 x = *slot(4 * t + jj);
-      f32x4 v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = ae * o[t][4 * jj + e] + ao * x[e];
-      __builtin_nontemporal_store(v, &po[(4 * t + jj) * 64]);
+      for (int e = 0; e < 4; ++e) o[t][4 * jj + e] = ae * o[t][4 * jj + e] + ao * x[e];
     }
-  if (h == 0) {
-    __builtin_nontemporal_store(m_new, &pm[part * kQRows + qrow]);
-    __builtin_nontemporal_store(l_all, &pl[part * kQRows + qrow]);
-  }
+  store_partial_f16(o, m_new, ae * l_tot + ao * l_o, qgrp, lane, po_all, pm, pl, part);
 }
 
 }  // namespace ax

@@ -38,7 +38,8 @@ AttnPlan attn_plan(int S, int Smax);     // bf16 cache
 AttnPlan attn_plan_f8(int S, int Smax);  // fp8 cache (longer splits: a block is half the bytes)
 size_t attn_partials_bytes(const AttnPlan& p);
 
-// Partial buffers inside the workspace: O [8][n_split][4][16][64] float4, then m and l
+// Partial buffers inside the workspace: O [8][n_split][4][16][64] groups of 4 float16 (scaled
+// by a power of two per (split, row) that is folded into m and l), then m and l
 // [8][n_split][128] float, each 256-byte aligned.
 struct WsLayout {
   float* po;
