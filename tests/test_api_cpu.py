@@ -126,9 +126,13 @@ def test_split_and_combine_validation_codes():
     assert cb(FAKE, 8, 128, 256, FAKE, None) == ax.AX_E_WORKSPACE
 
 
-def test_no_device_is_reported_not_launched():
+def _gpu_present() -> bool:
     import torch
-    if torch.cuda.is_available():
+    return torch.cuda.is_available()
+
+
+def test_no_device_is_reported_not_launched():
+    if _gpu_present():
         pytest.skip("a GPU is present: the valid call would launch")
     assert _layer() == ax.AX_E_UNSUPPORTED
 
@@ -217,14 +221,17 @@ def test_expert_layer_workspace_and_validation_codes():
     assert layer(eps=float("nan")) == ax.AX_E_ARG
     assert layer(ws_bytes=16) == ax.AX_E_WORKSPACE
     assert layer(ws=FAKE + 16) == ax.AX_E_WORKSPACE
-    assert layer() == ax.AX_E_UNSUPPORTED                      # valid arguments, no device here
     pk = ax.lib.ax_pack_weight_m64
     assert pk(None, 128, 64, FAKE, None) == ax.AX_E_NULL
     assert pk(FAKE, 100, 64, FAKE, None) == ax.AX_E_SHAPE
-    assert pk(FAKE, 128, 64, FAKE, None) == ax.AX_E_UNSUPPORTED
     g = ax.lib.ax_linear_m64
     assert g(None, FAKE, 128, 64, FAKE, FAKE, big, None) == ax.AX_E_NULL
     assert g(FAKE, FAKE, 100, 64, FAKE, FAKE, big, None) == ax.AX_E_SHAPE
     assert g(FAKE, FAKE, 128, 96, FAKE, FAKE, big, None) == ax.AX_E_SHAPE
     assert g(FAKE, FAKE, 128, 64, FAKE, FAKE, 16, None) == ax.AX_E_WORKSPACE
-    assert g(FAKE, FAKE, 128, 64, FAKE, FAKE, big, None) == ax.AX_E_UNSUPPORTED
+    # Valid arguments pass validation and would launch on the fake pointers where a device exists:
+    # only without one may they be called, to see them reported as unsupported.
+    if not _gpu_present():
+        assert layer() == ax.AX_E_UNSUPPORTED
+        assert pk(FAKE, 128, 64, FAKE, None) == ax.AX_E_UNSUPPORTED
+        assert g(FAKE, FAKE, 128, 64, FAKE, FAKE, big, None) == ax.AX_E_UNSUPPORTED
