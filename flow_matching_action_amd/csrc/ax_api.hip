@@ -189,7 +189,7 @@ int ax_expert_attn_combine(const void* ws, size_t ws_bytes, int S, int Smax, uin
 
 size_t ax_expert_attn_fp8_workspace_bytes(int S, int Smax) {
   if (check_shape(S, Smax) != AX_OK) return 0;
-  return ax::attn_partials_bytes(ax::attn_plan_f8(S, Smax));
+  return ax::attn_partials_bytes_f8(ax::attn_plan_f8(S, Smax));
 }
 
 static int check_ws_f8(const void* ws, size_t ws_bytes, int S, int Smax) {
@@ -268,7 +268,7 @@ int ax_expert_attn_fp8_combine(const void* ws, size_t ws_bytes, int S, int Smax,
   if (r == AX_OK) r = check_ws_f8(ws, ws_bytes, S, Smax);
   if (r == AX_OK) r = check_device();
   if (r != AX_OK) return r;
-  return status(ax::launch_attn_combine(ax::attn_plan_f8(S, Smax), ws, out, as_stream(stream)));
+  return status(ax::launch_attn_f8_combine(ax::attn_plan_f8(S, Smax), ws, out, as_stream(stream)));
 }
 
 // ---- text-model decode step -------------------------------------------------------------------

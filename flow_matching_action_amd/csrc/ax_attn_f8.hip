@@ -418,6 +418,112 @@ __global__ __launch_bounds__(256) void k_tail_quant_f8(const uint16_t* k, const 
   if (j16 == 0) (is_v ? Vs : Ks)[crow] = scale;
 }
 
+// Combine of the fp8 kernel's partials: out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c,
+// M = max_c m_c. Workgroup (head g, rows 8r .. 8r+7, column half hc): 512 threads in 4 split
+// groups of 128 (8 rows x 16 column quads); group k reduces splits k, k + 4, ..., issuing the loads
+// of up to kCombBatch splits before using any of them, so the whole partial set is in flight at
+// once. The 8 rows of a (slot, half) of the accumulator layout are one 128-byte line. The groups
+// meet in LDS.
+constexpr int kCombGroups = 4;
+constexpr int kCombBatch = 8;
+__global__ __launch_bounds__(512) void k_attn_f8_combine(const float* po, const float* pm, const float* pl,
+                                                         uint16_t* out, int n_split) {
+  __shared__ float sM[kCombGroups][8], sL[kCombGroups][8];
+  __shared__ f32x4 sA[kCombGroups][128];
+  const int g = blockIdx.x % kHkv;
+  const int rest = blockIdx.x / kHkv;   // 0..31
+  const int rblk = rest >> 1;           // rows 8 rblk .. +7
+  const int hc = rest & 1;              // column quads 16 hc .. +15
+  const int grp = threadIdx.x >> 7;
+  const int t = threadIdx.x & 127;
+  const int rloc = t >> 4;
+  const int quad = 16 * hc + (t & 15);
+  const int q = 8 * rblk + rloc;
+  const int d0 = 4 * quad;              // = 32 tt + 8 jj + 4 h
+  const int tt = d0 >> 5, jj = (d0 >> 3) & 3, h = (d0 >> 2) & 1;
+  const int slot = 4 * tt + jj, lane = (q & 31) + 32 * h;
+  const float* pmg = pm + (long long)g * n_split * kQRows + q;
+  const float* plg = pl + (long long)g * n_split * kQRows + q;
+  const u32x2* pog = reinterpret_cast<const u32x2*>(po) + ((long long)g * n_split * 4 + (q >> 5)) * (16 * 64) +
+                     slot * 64 + lane;
+  const long long pstride = 4 * 16 * 64;  // 4-float16 groups per split partial
+  float M = -INFINITY, L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = grp; c0 < n_split; c0 += kCombGroups * kCombBatch) {
+    float mv[kCombBatch], lv[kCombBatch];
+    f32x4 ov[kCombBatch];
+#pragma unroll
+    for (int k = 0; k < kCombBatch; ++k) {
+      const int c = min(c0 + kCombGroups * k, n_split - 1);  // past the end: a repeat, weighted 0 below
+      mv[k] = pmg[(long long)c * kQRows];
+      lv[k] = plg[(long long)c * kQRows];
+      ov[k] = unpack_f16x4(pog[(long long)c * pstride]);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the batch is issued before any is used
+    float Mb = M;
+#pragma unroll
+    for (int k = 0; k < kCombBatch; ++k)
+      if (c0 + kCombGroups * k < n_split) Mb = fmaxf(Mb, mv[k]);
+    const float r = __builtin_amdgcn_exp2f(M - Mb);  // 0 while M is -inf
+    L *= r;
+    acc[0] *= r; acc[1] *= r; acc[2] *= r; acc[3] *= r;
+    M = Mb;
+#pragma unroll
+    for (int k = 0; k < kCombBatch; ++k) {
+      const float w = (c0 + kCombGroups * k < n_split) ? __builtin_amdgcn_exp2f(mv[k] - M) : 0.f;
+      L += w * lv[k];
+      acc[0] += w * ov[k][0]; acc[1] += w * ov[k][1]; acc[2] += w * ov[k][2]; acc[3] += w * ov[k][3];
+    }
+  }
+  if ((t & 15) == 0) {
+    sM[grp][rloc] = M;
+    sL[grp][rloc] = L;
+  }
+  sA[grp][t] = acc;
+  __syncthreads();
+  if (grp != 0) return;
+  float Mt = sM[0][rloc];  // group 0 holds split 0, so Mt is finite
+#pragma unroll
+  for (int k = 1; k < kCombGroups; ++k) Mt = fmaxf(Mt, sM[k][rloc]);
+  float Lt = 0.f;
+  f32x4 At = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < kCombGroups; ++k) {
+    const float w = __builtin_amdgcn_exp2f(sM[k][rloc] - Mt);  // 0 for a group without splits
+    Lt += w * sL[k][rloc];
+    const f32x4 v = sA[k][t];
+    At[0] += w * v[0]; At[1] += w * v[1]; At[2] += w * v[2]; At[3] += w * v[3];
+  }
+  const float inv = 1.0f / Lt;
+  uint2 o2;
+  o2.x = pack_bf16x2(At[0] * inv, At[1] * inv);
+  o2.y = pack_bf16x2(At[2] * inv, At[3] * inv);
+  *reinterpret_cast<uint2*>(out + ((long long)g * kQRows + q) * kD + d0) = o2;
+}
+
+static size_t align256_f8(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t attn_partials_bytes_f8(const AttnPlan& p) {
+  const size_t parts = (size_t)kHkv * p.n_split;
+  return align256_f8(parts * kD * kQRows * 2) + 2 * align256_f8(parts * kQRows * 4);
+}
+
+WsLayoutF8 ws_layout_f8(const AttnPlan& plan, const void* ws) {
+  const size_t parts = (size_t)kHkv * plan.n_split;
+  char* w = static_cast<char*>(const_cast<void*>(ws));
+  WsLayoutF8 l;
+  l.po = reinterpret_cast<float*>(w);
+  l.pm = reinterpret_cast<float*>(w + align256_f8(parts * kD * kQRows * 2));
+  l.pl = reinterpret_cast<float*>(w + align256_f8(parts * kD * kQRows * 2) + align256_f8(parts * kQRows * 4));
+  return l;
+}
+
+hipError_t launch_attn_f8_combine(const AttnPlan& plan, const void* ws, uint16_t* out, hipStream_t st) {
+  const WsLayoutF8 l = ws_layout_f8(plan, ws);
+  hipLaunchKernelGGL(k_attn_f8_combine, dim3(kHkv * 32), dim3(512), 0, st, l.po, l.pm, l.pl, out, plan.n_split);
+  return hipGetLastError();
+}
+
 AttnPlan attn_plan_f8(int S, int /*Smax*/) {
   AttnPlan p;
   p.n_keys = S + kT;
@@ -443,7 +549,7 @@ static hipError_t launch_f8_nb(const F8Args& a, bool norm, hipStream_t st) {
 }
 
 hipError_t launch_attn_f8_split(const AttnPlan& plan, const AttnLaunchF8& p, hipStream_t st) {
-  const WsLayout l = ws_layout(plan, p.ws);
+  const WsLayoutF8 l = ws_layout_f8(plan, p.ws);
   F8Args a;
   a.q = p.q;
   a.gq = p.gq;
@@ -485,7 +591,7 @@ hipError_t launch_attn_f8_split(const AttnPlan& plan, const AttnLaunchF8& p, hip
 hipError_t launch_attn_f8(const AttnPlan& plan, const AttnLaunchF8& p, hipStream_t st) {
   const hipError_t e = launch_attn_f8_split(plan, p, st);
   if (e != hipSuccess) return e;
-  return launch_attn_combine(plan, p.ws, p.out, st);
+  return launch_attn_f8_combine(plan, p.ws, p.out, st);
 }
 
 hipError_t launch_tail_quant_f8(const uint16_t* k, const uint16_t* v, uint8_t* Kc, float* Ks, uint8_t* Vc,

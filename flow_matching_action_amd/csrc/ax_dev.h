@@ -142,6 +142,25 @@ __device__ __forceinline__ void norm_rope_pair(float* x, const float* A, const f
   for (int e = 0; e < 8; ++e) x[e] = y[e];
 }
 
+// norm_rope_pair with the result multiplied by post (folded into the row's 1/rms), for a row
+// that feeds a product whose scale is applied here instead of on every product.
+__device__ __forceinline__ void norm_rope_pair_scaled(float* x, const float* A, const float* B, float eps,
+                                                      float post) {
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+  ss += row_ror<8>(ss);
+  ss += row_ror<4>(ss);
+  ss += row_ror<2>(ss);
+  ss += row_ror<1>(ss);
+  const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / kD) + eps) * post;
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = inv * __builtin_fmaf(x[e ^ 4], B[e], x[e] * A[e]);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = y[e];
+}
+
 // Pair-layout row access: the lane's two 8-byte pieces (4 bf16 each) of a bf16 row.
 __device__ __forceinline__ void unpack_pair(const uint2& lo, const uint2& hi, float* x) {
   x[0] = __uint_as_float(lo.x << 16); x[1] = __uint_as_float(lo.x & 0xffff0000u);

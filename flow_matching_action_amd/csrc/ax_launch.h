@@ -36,17 +36,29 @@ struct AttnPlan {
 
 AttnPlan attn_plan(int S, int Smax);     // bf16 cache
 AttnPlan attn_plan_f8(int S, int Smax);  // fp8 cache (longer splits: a block is half the bytes)
-size_t attn_partials_bytes(const AttnPlan& p);
 
-// Partial buffers inside the workspace: O [8][n_split][4][16][64] groups of 4 float16 (scaled
-// by a power of two per (split, row) that is folded into m and l), then m and l
-// [8][n_split][128] float, each 256-byte aligned.
+// bf16 partials inside the workspace, one row per (kv head, key range, folded query row): O
+// [8][n_split][128][128] float16 scaled by 2^-e per (row, 32-column quarter), m and l
+// [8][n_split][128] float, e [8][n_split][128][4] int; each 256-byte aligned.
 struct WsLayout {
+  uint16_t* po;
+  float* pm;
+  float* pl;
+  int* pe;
+};
+size_t attn_partials_bytes(const AttnPlan& p);
+WsLayout ws_layout(const AttnPlan& plan, const void* ws);
+
+// fp8-cache partials: O [8][n_split][4][16][64] groups of 4 float16 (scaled by a power of two per
+// (split, row) that is folded into m and l), then m and l [8][n_split][128] float, each 256-byte
+// aligned.
+struct WsLayoutF8 {
   float* po;
   float* pm;
   float* pl;
 };
-WsLayout ws_layout(const AttnPlan& plan, const void* ws);
+size_t attn_partials_bytes_f8(const AttnPlan& p);
+WsLayoutF8 ws_layout_f8(const AttnPlan& plan, const void* ws);
 
 struct AttnLaunch {
   const uint16_t* q;       // [16][64][128] (== folded [8][128][128]): raw if q_norm, else roped
@@ -86,6 +98,7 @@ struct AttnLaunchF8 {
 };
 hipError_t launch_attn_f8(const AttnPlan& plan, const AttnLaunchF8& p, hipStream_t st);        // both
 hipError_t launch_attn_f8_split(const AttnPlan& plan, const AttnLaunchF8& p, hipStream_t st);  // partials
+hipError_t launch_attn_f8_combine(const AttnPlan& plan, const void* ws, uint16_t* out, hipStream_t st);
 hipError_t launch_tail_quant_f8(const uint16_t* k, const uint16_t* v, uint8_t* Kc, float* Ks, uint8_t* Vc,
                                 float* Vs, int Smax, hipStream_t st);
 

@@ -142,9 +142,17 @@ def test_fp8_workspace_bytes():
     assert ax.expert_attn_fp8_workspace_bytes(8128, 8192) > 0
     assert ax.expert_attn_fp8_workspace_bytes(193, 256) == 0
     assert ax.expert_attn_fp8_workspace_bytes(0, 63) == 0
-    # fp8 splits hold up to 384 keys (bf16: 192): never more partials than the bf16 plan
-    for S, Smax in ((4700, 8192), (8128, 8192), (65472, 65536)):
-        assert ax.expert_attn_fp8_workspace_bytes(S, Smax) <= ax.expert_attn_workspace_bytes(S, Smax)
+
+
+def test_bf16_workspace_holds_one_partial_row_per_range_and_query_row():
+    # 15 cache key ranges of 10 blocks + the own-token range at S = 4700; per (kv head, range, folded
+    # query row): 128 float16 of O, m and l (float32) and 4 exponents (int32)
+    per_row = 128 * 2 + 4 + 4 + 4 * 4
+    assert ax.expert_attn_workspace_bytes(4700, 8192) == 16 * 8 * 128 * per_row
+    assert ax.expert_attn_workspace_bytes(4700, 5120) == 16 * 8 * 128 * per_row   # rows read, not Smax, set it
+    assert ax.expert_attn_workspace_bytes(0, 64) == 1 * 8 * 128 * per_row         # the own range alone
+    # ranges never exceed 10 blocks: long caches take more ranges
+    assert ax.expert_attn_workspace_bytes(65472, 65536) >= (65472 // 320 + 1) * 8 * 128 * per_row
 
 
 def test_fp8_validation_codes():
