@@ -288,52 +288,62 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
   //    same tokens (same RoPE rows, gamma k). Roped q arrives ready.
   await_cnt(kCPro + W, 1, expired);
   if constexpr (NORM) {
-    // every LDS read first (rows, RoPE rows, gammas), then the arithmetic, then the stores, so
-    // that the four rows' work overlaps instead of each row waiting for the previous one's stores
-    float g8[8], gk8[8];
+    // the four query rows in one branch-free pass (all LDS reads, then the arithmetic, then the
+    // stores, so that the rows' dependency chains interleave); the own k rows in a second pass
+    float g8[8];
     unpack_pair(lds_ld<uint2>(AX_LDS(sGam) + 8 * j16), lds_ld<uint2>(AX_LDS(sGam) + 128 + 8 * j16), g8);
-    unpack_pair(lds_ld<uint2>(AX_LDS(sGam) + 256 + 8 * j16), lds_ld<uint2>(AX_LDS(sGam) + 384 + 8 * j16), gk8);
-    uint2 lo[4], hi[4], klo[4], khi[4];
-    f32x4 cs[4], sn[4];
+    uint2 lo[4], hi[4];
+    float cc[4][4], ss[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * W + 4 * i + r4;  // query row = token
       lo[i] = lds_ld<uint2>(AX_LDS(sQ) + r * 256 + pair_off_lo(j16, qswz(r)));
       hi[i] = lds_ld<uint2>(AX_LDS(sQ) + r * 256 + pair_off_hi(j16, qswz(r)));
-      cs[i] = lds_ld<f32x4>(AX_LDS(sRope) + (16 * W + 4 * i) * 256 + 16 * lane);
-      sn[i] = lds_ld<f32x4>(AX_LDS(sRope) + kT * 256 + (16 * W + 4 * i) * 256 + 16 * lane);
-      if (c.own) {
-        const int tr = r & (kBlk - 1);
-        const lds_u8* krow = ring + (r >> 5) * kSTile + tr * 256;
-        klo[i] = lds_ld<uint2>(krow + pair_off_lo(j16, kswz(tr)));
-        khi[i] = lds_ld<uint2>(krow + pair_off_hi(j16, kswz(tr)));
+      const f32x4 cs = lds_ld<f32x4>(AX_LDS(sRope) + (16 * W + 4 * i) * 256 + 16 * lane);
+      const f32x4 sn = lds_ld<f32x4>(AX_LDS(sRope) + kT * 256 + (16 * W + 4 * i) * 256 + 16 * lane);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        cc[i][e] = cs[e];
+        ss[i][e] = sn[e];
       }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float cc[4] = {cs[i][0], cs[i][1], cs[i][2], cs[i][3]};
-      const float ss[4] = {sn[i][0], sn[i][1], sn[i][2], sn[i][3]};
       float x[8], A[8], B[8];
       unpack_pair(lo[i], hi[i], x);
-      rope_coef_pair(g8, cc, ss, A, B);
+      rope_coef_pair(g8, cc[i], ss[i], A, B);
       norm_rope_pair(x, A, B, a.eps);
       pack_pair(x, lo[i], hi[i]);
-      if (c.own) {
-        float kA[8], kB[8], y[8];
-        rope_coef_pair(gk8, cc, ss, kA, kB);
-        unpack_pair(klo[i], khi[i], y);
-        norm_rope_pair(y, kA, kB, a.eps);
-        pack_pair(y, klo[i], khi[i]);
-      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * W + 4 * i + r4;
       lds_st(AX_LDS(sQ) + r * 256 + pair_off_lo(j16, qswz(r)), lo[i]);
       lds_st(AX_LDS(sQ) + r * 256 + pair_off_hi(j16, qswz(r)), hi[i]);
-      if (c.own) {
-        const int tr = r & (kBlk - 1);
-        lds_u8* krow = ring + (r >> 5) * kSTile + tr * 256;
+    }
+    if (c.own) {
+      float gk8[8];
+      unpack_pair(lds_ld<uint2>(AX_LDS(sGam) + 256 + 8 * j16), lds_ld<uint2>(AX_LDS(sGam) + 384 + 8 * j16), gk8);
+      uint2 klo[4], khi[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tr = (16 * W + 4 * i + r4) & (kBlk - 1);
+        const lds_u8* krow = ring + ((16 * W + 4 * i) >> 5) * kSTile + tr * 256;
+        klo[i] = lds_ld<uint2>(krow + pair_off_lo(j16, kswz(tr)));
+        khi[i] = lds_ld<uint2>(krow + pair_off_hi(j16, kswz(tr)));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float y[8], kA[8], kB[8];
+        rope_coef_pair(gk8, cc[i], ss[i], kA, kB);
+        unpack_pair(klo[i], khi[i], y);
+        norm_rope_pair(y, kA, kB, a.eps);
+        pack_pair(y, klo[i], khi[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tr = (16 * W + 4 * i + r4) & (kBlk - 1);
+        lds_u8* krow = ring + ((16 * W + 4 * i) >> 5) * kSTile + tr * 256;
         lds_st(krow + pair_off_lo(j16, kswz(tr)), klo[i]);
         lds_st(krow + pair_off_hi(j16, kswz(tr)), khi[i]);
       }
