@@ -6,12 +6,15 @@ S = 4700, bf16. Steps rotate over 64 distinct layer caches (2.1 GB, far beyond t
 256 MB Infinity Cache) with fresh q / own k / own v per (Euler step, layer), the
 64-layer x 10-step sequence of the flow-matching sampler, in stream order. The K
 timed steps are one hipGraph replay, bracketed by device synchronisation and
-timed with HIP events on the stream the graph runs on.
+timed with HIP events on the stream the graph runs on. Before every replay, outside
+the timed events, a 512 MB buffer is read and written, twice the Infinity Cache, so
+each replay starts with no cache rows in L2 or the Infinity Cache whatever K is; the
+line reports the layers and bytes one replay touches.
 
-The roofline figures are those of the dominant kernel, the fused norm + RoPE + tail
-write + split attention launch: a second graph of the same K steps, with that launch
-alone, is timed the same way, and its algorithmic bytes (the step's, less the output
-that the combine writes) are divided by its average launch time.
+The roofline figures are those of the dominant kernel, k_attn_split (q/k norm + RoPE +
+tail write + split attention in one launch): a second graph of the same K steps, with
+that launch alone, is timed the same way, and its algorithmic bytes (the step's, less
+the output that the combine writes) are divided by its average launch time.
 
 The fp8-cache variant (e4m3 codes + float32 row scales) is measured the same way on its own
 workload, Smax = 8192, S = 8128 (the full cache), over 64 rotating fp8 caches (1.1 GB), and
@@ -310,31 +313,67 @@ def load_traffic(which: str = "bf16"):
         return None
 
 
-def cpu_baseline(n_layers: int = 6) -> dict:
-    """The fp64 oracle on the host cores, on a bounded sample of the same workload shape."""
-    import numpy as np
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
+def _usable_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(n_layers: int = 12) -> dict:
+    """The fp64 oracle on the host cores, on a bounded sample of the same workload shape: once with the
+    BLAS pool at one thread, once at every core this process may use (the headline figure)."""
     import oracle
     from flow_matching_action_amd import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = os.cpu_count() or 1
-    times = []
-    for i in range(n_layers):
-        inp = synth.layer_inputs(SMAX, S, seed=7000 + i)
-        t0 = time.perf_counter()
-        oracle.expert_attn_layer(inp["q"], inp["k"], inp["v"], inp["gq"], inp["gk"], inp["Kc"], inp["Vc"],
-                                 S, SMAX, ROPE_DELTA)
-        times.append(time.perf_counter() - t0)
-    us = statistics.median(times) * 1e6
-    return {"value": round(us, 1), "unit": "us/layer", "cores": int(threads), "kind": "oracle",
+    from threadpoolctl import threadpool_info, threadpool_limits
+    blas = [{"api": p.get("internal_api"), "version": p.get("version"), "threading": p.get("threading_layer"),
+             "num_threads": p.get("num_threads")} for p in threadpool_info() if p.get("user_api") == "blas"]
+    inputs = [synth.layer_inputs(SMAX, S, seed=7000 + i) for i in range(n_layers)]
+
+    def run(threads: int) -> float:
+        times = []
+        with threadpool_limits(limits=threads, user_api="blas"):
+            for inp in inputs:
+                t0 = time.perf_counter()
+                oracle.expert_attn_layer(inp["q"], inp["k"], inp["v"], inp["gq"], inp["gk"], inp["Kc"], inp["Vc"],
+                                         S, SMAX, ROPE_DELTA)
+                times.append(time.perf_counter() - t0)
+        return statistics.median(times) * 1e6
+
+    cores = _usable_cores()
+    first = inputs[0]
+    oracle.expert_attn_layer(first["q"], first["k"], first["v"], first["gq"], first["gk"], first["Kc"], first["Vc"],
+                             S, SMAX, ROPE_DELTA)   # untimed: page faults and BLAS pool start-up
+    us_one = run(1)
+    us_all = run(cores)
+    return {"value": round(us_all, 1), "unit": "us/layer", "cores": int(cores), "kind": "oracle",
             "sample": f"{n_layers} layers of the Smax=8192 S=4700 workload (seeds 7000..{7000 + n_layers - 1}), "
-                      f"median per layer; numpy float64 on the host"}
+                      f"median per layer; numpy float64 on the host",
+            "single_thread": {"value": round(us_one, 1), "unit": "us/layer", "cores": 1},
+            "all_core": {"value": round(us_all, 1), "unit": "us/layer", "cores": int(cores)},
+            "cpu_model": _cpu_model(), "blas": blas}
+
+
+FLUSH_BYTES = 512 << 20   # twice the Infinity Cache
 
 
 def timed_graph(torch, stream, enqueue, first: int, K: int, replays: int) -> list:
-    """Capture enqueue(first .. first+K-1) as one graph; wall time of each replay (ms), HIP events on stream."""
+    """Capture enqueue(first .. first+K-1) as one graph; wall time of each replay (ms), HIP events on stream.
+    Before each replay, outside the events, a 512 MB buffer is read and written, so no replay finds the
+    previous one's rows in L2 or the Infinity Cache."""
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
         with torch.cuda.graph(graph, stream=stream):
@@ -345,6 +384,8 @@ def timed_graph(torch, stream, enqueue, first: int, K: int, replays: int) -> lis
     for _ in range(max(1, replays)):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            flush.add_(1.0)
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             e0.record(stream)
@@ -409,7 +450,10 @@ def main() -> int:
             wl.step(i, stream)
     torch.cuda.synchronize()
 
-    # the K timed steps as one graph (headline), then the dominant launch alone over the same steps
+    # the K timed steps as one graph (headline), then the dominant launch alone over the same steps.
+    # Distinct layer caches one replay touches: steps W .. W+K-1 use layers (W + i) % 64.
+    layers_touched = min(K, N_LAYERS)
+    bytes_touched = layers_touched * 2 * 8 * (S + 64) * 256
     times_ms = timed_graph(torch, stream, wl.step, W, K, args.replays)
     ms_total = statistics.median(times_ms)
     us_layer = ms_total * 1e3 / K
@@ -437,12 +481,16 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1) caches, q, own k/v; hidden rows 7.0)",
         "config": {"workload": "expert attention layer step, Smax=8192 S=4700 bf16, 64 rotating layer caches "
                                "(2.1 GB, cold), fresh q/k/v per (Euler step, layer), hipGraph of K steps",
-                   "Smax": SMAX, "S": S, "layers_rotated": N_LAYERS, "rope_delta": ROPE_DELTA},
+                   "Smax": SMAX, "S": S, "layers_rotated": N_LAYERS, "rope_delta": ROPE_DELTA,
+                   "layers_touched_per_replay": layers_touched,
+                   "distinct_cache_bytes_per_replay": bytes_touched,
+                   "cache_flush_between_replays_bytes": FLUSH_BYTES},
         "achieved_hbm_gbs": round(gbs, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbs_attn, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs_attn / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "k_attn_fused (q/k norm + RoPE + tail write + split attention), one launch per step",
+                     "kernel": "k_attn_split (q/k norm + RoPE + tail write + split attention), one launch per "
+                               "step; the step adds k_attn_combine",
                      "kernel_us_per_launch": round(us_attn, 3),
                      "algorithmic_bytes_per_launch": b_attn,
                      "algorithmic_flops_per_launch": algorithmic_flops(S),

@@ -24,6 +24,7 @@ AX_E_ALIGN = -3
 AX_E_WORKSPACE = -4
 AX_E_UNSUPPORTED = -5
 AX_E_ARG = -6
+AX_STATUS_WAIT_EXPIRED = 1
 
 N_Q_HEADS, N_KV_HEADS, N_TOK, HEAD_DIM = 16, 8, 64, 128
 
@@ -47,6 +48,8 @@ lib.ax_abi_version.restype = _I
 lib.ax_abi_version.argtypes = []
 lib.ax_strerror.restype = ctypes.c_char_p
 lib.ax_strerror.argtypes = [_I]
+lib.ax_debug_set_wait_limit.restype = _I
+lib.ax_debug_set_wait_limit.argtypes = [_I]
 lib.ax_rope_tables.restype = _I
 lib.ax_rope_tables.argtypes = [_I, _I, _I, ctypes.c_double, _P, _P]
 lib.ax_qk_norm_rope.restype = _I
@@ -99,7 +102,7 @@ lib.ax_linear_m64.argtypes = [_P, _P, _I, _I, _P, _P, ctypes.c_size_t, _P]
 lib.ax_copy_words.restype = _I
 lib.ax_copy_words.argtypes = [_P, _P, ctypes.c_size_t, _P]
 
-EXPORTS = ("ax_abi_version", "ax_strerror", "ax_rope_tables", "ax_qk_norm_rope", "ax_cache_tail_write",
+EXPORTS = ("ax_abi_version", "ax_strerror", "ax_debug_set_wait_limit", "ax_rope_tables", "ax_qk_norm_rope", "ax_cache_tail_write",
            "ax_qk_norm_rope_tail", "ax_expert_attn_workspace_bytes", "ax_expert_attn",
            "ax_expert_layer_attn", "ax_expert_layer_attn_split", "ax_expert_attn_combine",
            "ax_expert_attn_fp8_workspace_bytes", "ax_cache_tail_write_fp8", "ax_expert_attn_fp8",
@@ -137,6 +140,17 @@ def abi_version() -> int:
 
 def strerror(code: int) -> str:
     return lib.ax_strerror(code).decode()
+
+
+def debug_set_wait_limit(polls: int) -> None:
+    """Polls before a bounded in-workgroup wait gives up, for later launches (0 = the default)."""
+    _check("ax_debug_set_wait_limit", lib.ax_debug_set_wait_limit(int(polls)))
+
+
+def workspace_status(ws) -> int:
+    """The status word (first 4 bytes) of an attention workspace tensor; synchronises the device."""
+    torch.cuda.synchronize()
+    return int(ws[:4].view(torch.int32).item())
 
 
 def rope_tables(pos0: int, n_tok: int = N_TOK, head_dim: int = HEAD_DIM, theta: float = 5e6):

@@ -51,11 +51,27 @@ int status(hipError_t e) { return e == hipSuccess ? AX_OK : static_cast<int>(e);
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// Polls of a bounded in-workgroup wait (0: the default); read at each launch.
+std::atomic<int> g_wait_limit{0};
+
 }  // namespace
+
+namespace ax {
+int wait_limit() {
+  const int v = g_wait_limit.load(std::memory_order_relaxed);
+  return v > 0 ? v : kDefaultWaitLimit;
+}
+}  // namespace ax
 
 extern "C" {
 
 int ax_abi_version(void) { return AX_ABI_VERSION; }
+
+int ax_debug_set_wait_limit(int polls) {
+  if (polls < 0) return AX_E_ARG;
+  g_wait_limit.store(polls, std::memory_order_relaxed);
+  return AX_OK;
+}
 
 const char* ax_strerror(int code) {
   switch (code) {

@@ -74,7 +74,8 @@ struct SplitArgs {
   int own_tail;            // own rows come from k/v tensors; q head parity 0 writes them to the cache tail
   uint16_t* Kc;
   uint16_t* Vc;
-  WsLayout part;
+  WsLayout part;            // the status word and the partials
+  int spin_limit;           // polls before a wait gives up
   int S, Smax, n_split, kps;
   int n_cache_split;       // ranges over cache keys [0, S); range n_cache_split holds the 64 own tokens
 };
@@ -135,16 +136,17 @@ __shared__ __attribute__((aligned(16))) uint8_t sRope[2 * kT * 256];
 __shared__ __attribute__((aligned(16))) uint8_t sGam[2 * 256];
 __shared__ int sCnt[kCN];
 
-// Bounded waits on the counters: a wave whose wait runs out (about 30 ms; thousands of times any
-// real wait) carries on and remembers it, so that its partial is marked NaN.
+// Bounded waits on the counters: a wave whose wait runs out (by default about 30 ms; thousands of
+// times any real wait) carries on and remembers it; its partial is then marked NaN and the
+// workspace status word flagged.
 // The loop stays rolled: every wave of the workgroup shares one short copy of it in the
 // instruction cache.
-__device__ __forceinline__ void await_cnt(int i, int n, bool& expired) {
+__device__ __forceinline__ void await_cnt(int i, int n, int limit, bool& expired) {
   __builtin_amdgcn_sched_barrier(0);
-  int spin = kSpinLimit;
+  int spin = limit;
 #pragma clang loop unroll(disable)
   while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(&sCnt[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) < n) {
-    if (--spin == 0) {
+    if (--spin <= 0) {
       expired = true;
       break;
     }
@@ -251,7 +253,7 @@ __device__ __forceinline__ void split_loader(const SplitArgs& a, const SplitCtx&
   //    previous block are finished. Each block is 4 loads of this wave.
   const int nb = c.nb;
   auto issue = [&](int b) {
-    if (b >= kSRing) await_cnt(kCDone + b % kSRing, 2 * (b / kSRing), expired);
+    if (b >= kSRing) await_cnt(kCDone + b % kSRing, 2 * (b / kSRing), a.spin_limit, expired);
     dma_block_share(kc, vc, c, L, b, ring + (b % kSRing) * kSTile);
   };
   const int d0 = nb < kSDepth ? nb : kSDepth;
@@ -265,7 +267,7 @@ __device__ __forceinline__ void split_loader(const SplitArgs& a, const SplitCtx&
     arrive(&sCnt[kCLand + b], lane);
     if (b + kSDepth < nb) issue(b + kSDepth);
   }
-  (void)expired;  // a loader's expired wait shows as a block its compute waves never see land
+  report_expired(a.part.status, expired, lane);
 }
 
 // ---------------------------------------------------------------------------------- compute
@@ -286,7 +288,7 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
   // 1. Norm + RoPE of query rows 16 W .. 16 W + 15 in place (the arithmetic of the stand-alone
   //    norm/RoPE kernel, so the bits are the same); in the own range also the own k rows of the
   //    same tokens (same RoPE rows, gamma k). Roped q arrives ready.
-  await_cnt(kCPro + W, 1, expired);
+  await_cnt(kCPro + W, 1, a.spin_limit, expired);
   if constexpr (NORM) {
     // the four query rows in one branch-free pass (all LDS reads, then the arithmetic, then the
     // stores, so that the rows' dependency chains interleave); the own k rows in a second pass
@@ -350,7 +352,7 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
     }
   }
   arrive(&sCnt[kCNorm], lane);
-  await_cnt(kCNorm, kSC, expired);  // all 64 query rows (and in the own range the own k rows) ready
+  await_cnt(kCNorm, kSC, a.spin_limit, expired);  // all 64 query rows (and in the own range the own k rows) ready
 
   // 2. The query rows of row tile T as MFMA B operands (k-step kk).
   const int n = lane & 31;
@@ -447,7 +449,7 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
   };
   auto landed = [&](int b) {
     if (c.own) return;  // the own blocks are ready with the normed query rows
-    await_cnt(kCLand + b, kSL, expired);
+    await_cnt(kCLand + b, kSL, a.spin_limit, expired);
   };
 
   if (NB > 0) {
@@ -511,7 +513,7 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
   //    and row total l.
   const float2 lp = pair32(l);
   const float lt = lp.x + lp.y;
-  await_cnt(kCFrag, kSC, expired);
+  await_cnt(kCFrag, kSC, a.spin_limit, expired);
   lds_u8* xw = AX_LDS(sRope) + (2 * T + P) * 8192;  // written by this wave
   lds_u8* xr = AX_LDS(sRope) + (2 * T + (1 - P)) * 8192;  // written by the partner
   lds_u8* mw = AX_LDS(sQ) + (2 * T + P) * 512;        // this wave's m, then row total l, per lane
@@ -532,7 +534,7 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
   lds_st(mw + 4 * lane, m);
   lds_st(mw + 256 + 4 * lane, lt);
   arrive(&sCnt[kCMrg + T], lane);
-  await_cnt(kCMrg + T, 2, expired);
+  await_cnt(kCMrg + T, 2, a.spin_limit, expired);
   const float mo = lds_ld<float>(mr + 4 * lane);
   const float lo_ = lds_ld<float>(mr + 256 + 4 * lane);
   const float M = fmax_(m, mo);  // finite: parity 0 has a block
@@ -574,6 +576,7 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
     a.part.pm[part * kQRows + row] = bad ? __builtin_nanf("") : M;
     a.part.pl[part * kQRows + row] = L;
   }
+  report_expired(a.part.status, expired, lane);
 }
 
 // NORM: q and the own k arrive raw and are normed + roped here (the layer step); otherwise both
@@ -679,13 +682,15 @@ static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t attn_partials_bytes(const AttnPlan& p) {
   const size_t rows = (size_t)kHkv * p.n_split * kQRows;
-  return align256(rows * kD * 2) + 2 * align256(rows * 4) + align256(rows * 4 * 4);
+  return kStatusBytes + align256(rows * kD * 2) + 2 * align256(rows * 4) + align256(rows * 4 * 4);
 }
 
 WsLayout ws_layout(const AttnPlan& plan, const void* ws) {
   const size_t rows = (size_t)kHkv * plan.n_split * kQRows;
   char* w = static_cast<char*>(const_cast<void*>(ws));
   WsLayout l;
+  l.status = reinterpret_cast<int*>(w);
+  w += kStatusBytes;
   l.po = reinterpret_cast<uint16_t*>(w);
   w += align256(rows * kD * 2);
   l.pm = reinterpret_cast<float*>(w);
@@ -720,6 +725,7 @@ hipError_t launch_attn_split(const AttnPlan& plan, const AttnLaunch& p, hipStrea
   }
   a.Kc = p.Kc; a.Vc = p.Vc;
   a.part = ws_layout(plan, p.ws);
+  a.spin_limit = wait_limit();
   a.S = p.S; a.Smax = p.Smax; a.n_split = plan.n_split; a.kps = plan.keys_per_split;
   a.n_cache_split = plan.n_cache_split;
   const dim3 grid(kHkv * plan.n_split * 2);

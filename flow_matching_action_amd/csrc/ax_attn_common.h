@@ -88,17 +88,31 @@ __device__ __forceinline__ void arrive(int* cnt, int lane) {
 }
 
 // The wait is bounded (about 30 ms at 2.4 GHz, thousands of times any real wait) so that a
-// wave always exits even if a count were wrong; the results would then be wrong, not hung.
-constexpr int kSpinLimit = 1 << 20;
-__device__ __forceinline__ void await(int* cnt, int n) {
+// wave always exits even if a count were wrong. A wave whose wait runs out carries on with
+// whatever LDS holds, remembers it in expired, and reports it through the workspace status
+// word (report_expired), so a wrong count shows instead of passing as output. The bound is a
+// kernel argument: a host-side debug setting can shrink it to force the path without a hang.
+__device__ __forceinline__ void await(int* cnt, int n, int limit, bool& expired) {
   __builtin_amdgcn_sched_barrier(0);
-  for (int spin = 0; spin < kSpinLimit; ++spin) {
-    if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >= n)
+  int spin = limit;
+#pragma clang loop unroll(disable)
+  while (__builtin_amdgcn_readfirstlane(__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) < n) {
+    if (--spin <= 0) {
+      expired = true;
       break;
+    }
     __builtin_amdgcn_s_sleep(1);
   }
   asm volatile("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
+}
+
+// Workspace status word (the first 4 bytes of every workspace; the first 256 bytes are
+// reserved for it): flags OR-ed in by the kernels, never cleared by them.
+constexpr int kStatusWaitExpired = 1;
+constexpr size_t kStatusBytes = 256;
+__device__ __forceinline__ void report_expired(int* status, bool expired, int lane) {
+  if (expired && lane == 0) __hip_atomic_fetch_or(status, kStatusWaitExpired, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // RoPE table values of token tok for the 8 frequencies 8 (j16 & 7) .. +7: lanes j16 < 8 load
@@ -175,11 +189,13 @@ __device__ __forceinline__ void norm_rope_query_rows(uint8_t* qlds, const uint2 
 }
 
 
-// Split partials in float16. Per (split, query row) O is scaled by 2^-e, with 2^e the power of
-// two just above the row's largest |O| (max |O 2^-e| in [0.5, 1)), and e is added to m and l
-// is scaled with O: the combine's sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c is unchanged,
-// every finite O fits, and each element keeps float16's relative precision against the row's
-// largest value (2^-12 of max |O|, below the bf16 rounding of the output).
+// Split partials in float16. O is stored as O 2^-e per (split, query row), with 2^e the power of
+// two just above the row's largest |O| (max |O 2^-e| in [0.5, 1)); e is stored beside the row's
+// m and l, which stay float32 and unscaled. The scaling is ldexp, exact for every finite O
+// (denormal ones included: e >= -149 and |O 2^-e| < 1), so nothing overflows whatever the
+// magnitudes; the combine multiplies the row's weight by 2^e. Float16 then keeps 11 significant
+// bits of every element within 2^14 of the row's largest |O| (its normal range), and smaller
+// elements an absolute error below 2^-25 of that largest value.
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x2 pack_f16x4(float a, float b, float c, float d) {
@@ -191,12 +207,18 @@ __device__ __forceinline__ f32x4 unpack_f16x4(const u32x2& u) {
   return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
 
+// The fp8 kernel folds the value scales into P with a fixed factor 2^kF8VShift (the products
+// p * scale * 2^64 stay in bf16's normal range for every float32 scale from the denormals up to
+// 2^25), so its O accumulates in units of 2^-64; the stored exponent takes the factor back out.
+constexpr int kF8VShift = 64;
+
 // Store of one wave's partial for query rows 32 qgrp .. +31 (lane (n, h): row n, the half h of
 // the accumulator layout): O at po + ((part * 4 + qgrp) * 16 + j) * 64 + lane in 8-byte units
-// (slot j = 4t + jj, 4 float16 each, non-temporal: the combine reads it once), m and l at
-// pm / pl + part * 128 + query row. l_tot is the row's whole sum (both halves).
+// (slot j = 4t + jj, 4 float16 each, non-temporal: the combine reads it once), m, l and e at
+// pm / pl / pe + part * 128 + query row. l_tot is the row's whole sum (both halves); O is in
+// units of 2^-kF8VShift, so e - kF8VShift is stored.
 __device__ __forceinline__ void store_partial_f16(const f32x16 (&o)[4], float m, float l_tot, int qgrp, int lane,
-                                                  float* po_all, float* pm, float* pl, long long part) {
+                                                  float* po_all, float* pm, float* pl, int* pe, long long part) {
   const int n = lane & 31;
   const int h = lane >> 5;
   float amax = 0.f;
@@ -206,19 +228,20 @@ __device__ __forceinline__ void store_partial_f16(const f32x16 (&o)[4], float m,
     for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(o[t][i]));
   const float2 ap = pair32(amax);
   const int e = __builtin_amdgcn_frexp_expf(fmaxf(ap.x, ap.y));  // 0 for an all-zero row
-  const float scale = __builtin_ldexpf(1.0f, -e);
   u32x2* po = reinterpret_cast<u32x2*>(po_all) + (part * 4 + qgrp) * (16 * 64) + lane;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj)
-      __builtin_nontemporal_store(pack_f16x4(o[t][4 * jj] * scale, o[t][4 * jj + 1] * scale, o[t][4 * jj + 2] * scale,
-                                             o[t][4 * jj + 3] * scale),
+      __builtin_nontemporal_store(pack_f16x4(__builtin_ldexpf(o[t][4 * jj], -e), __builtin_ldexpf(o[t][4 * jj + 1], -e),
+                                             __builtin_ldexpf(o[t][4 * jj + 2], -e),
+                                             __builtin_ldexpf(o[t][4 * jj + 3], -e)),
                                   &po[(4 * t + jj) * 64]);
   if (h == 0) {
     const int qrow = 32 * qgrp + n;
-    __builtin_nontemporal_store(m + (float)e, &pm[part * kQRows + qrow]);
-    __builtin_nontemporal_store(l_tot * scale, &pl[part * kQRows + qrow]);
+    __builtin_nontemporal_store(m, &pm[part * kQRows + qrow]);
+    __builtin_nontemporal_store(l_tot, &pl[part * kQRows + qrow]);
+    __builtin_nontemporal_store(e - kF8VShift, &pe[part * kQRows + qrow]);
   }
 }
 
@@ -233,14 +256,15 @@ __device__ __forceinline__ void merge_and_store_partial(f32x16 (&o)[4], float m_
                                                         bool two_parities, int par, int qgrp, int lane,
                                                         uint8_t* xlo, uint8_t* xhi, RegionFree&& region_free,
                                                         float (*mlx)[2][32], int* cnt, float* po_all,
-                                                        float* pm, float* pl, long long part) {
+                                                        float* pm, float* pl, int* pe, long long part,
+                                                        int limit, bool& expired) {
   const int n = lane & 31;
   const int h = lane >> 5;
   const float2 l_pair = pair32(l_run);
   const float l_tot = l_pair.x + l_pair.y;
   if (!two_parities) {
     if (par == 1) return;
-    store_partial_f16(o, m_run, l_tot, qgrp, lane, po_all, pm, pl, part);
+    store_partial_f16(o, expired ? __builtin_nanf("") : m_run, l_tot, qgrp, lane, po_all, pm, pl, pe, part);
     return;
   }
   auto slot = [&](int j) { return reinterpret_cast<f32x4*>(j < 8 ? xlo + j * 1024 : xhi + (j - 8) * 1024) + lane; };
@@ -258,7 +282,7 @@ __device__ __forceinline__ void merge_and_store_partial(f32x16 (&o)[4], float m_
     arrive(&cnt[kCntMerge + qgrp], lane);
     return;
   }
-  await(&cnt[kCntMerge + qgrp], 1);
+  await(&cnt[kCntMerge + qgrp], 1, limit, expired);
   const float m_o = mlx[qgrp][0][n];
   const float l_o = mlx[qgrp][1][n];
   const float m_new = fmaxf(m_run, m_o);  // m_run is finite: block 0 holds a visible key
@@ -272,7 +296,9 @@ __device__ __forceinline__ void merge_and_store_partial(f32x16 (&o)[4], float m_
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[t][4 * jj + e] = ae * o[t][4 * jj + e] + ao * x[e];
     }
-  store_partial_f16(o, m_new, ae * l_tot + ao * l_o, qgrp, lane, po_all, pm, pl, part);
+  // an expired wait leaves this row's partial NaN (m), besides the status word
+  store_partial_f16(o, expired ? __builtin_nanf("") : m_new, ae * l_tot + ao * l_o, qgrp, lane, po_all, pm, pl, pe,
+                    part);
 }
 
 }  // namespace ax

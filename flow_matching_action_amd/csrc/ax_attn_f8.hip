@@ -52,6 +52,9 @@ struct F8Args {
   float* po;
   float* pm;
   float* pl;
+  int* pe;
+  int* status;             // workspace status word
+  int spin_limit;          // polls before a wait gives up
   int S, Smax, n_split, kps, n_cache_split;
 };
 
@@ -119,6 +122,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_f8(F8Args a) {
   const bool own_tail = a.k_own != nullptr;          // own rows quantised here into tiles and cache tail
 
   if (tid < kNCnt) cnt[tid] = 0;
+  bool expired = false;  // a bounded wait of this wave ran out
   if (wave < kComputeWaves) {
     const uint16_t* qh = a.q + (long long)(2 * g) * kT * kD;
     static_for<4>([&](auto pc) {
@@ -136,7 +140,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_f8(F8Args a) {
     if (own_split && own_tail) {
       // the compute waves fill the own split's tiles; nothing to load
       static_for<NB>([&](auto bc) { arrive(&cnt[kCntBlock + decltype(bc)::value], lane); });
-      return;
+      return;  // (no waits)
     }
     // cache row of visible key vk (own tokens from the cache tail); rows past the split end
     // reload a visible row, which the compute waves mask
@@ -170,7 +174,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_f8(F8Args a) {
       arrive(&cnt[kCntBlock + b], lane);
       if constexpr (b + D < NB) issue_block(std::integral_constant<int, b + D>{});
     });
-    return;
+    return;  // (no waits)
   }
 
   // ---------------- compute waves (512 threads)
@@ -260,7 +264,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_f8(F8Args a) {
     }
   }
   arrive(&cnt[kCntQNormed], lane);
-  await(&cnt[kCntQNormed], kComputeWaves);  // all 128 query rows (and the own blocks) are in LDS
+  await(&cnt[kCntQNormed], kComputeWaves, a.spin_limit, expired);  // all 128 query rows (and the own blocks) are in LDS
 
   const int qgrp = wave & 3;  // query rows 32 qgrp .. +31
   const int par = wave >> 2;  // blocks b with b % 2 == par
@@ -297,7 +301,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_f8(F8Args a) {
     constexpr int b = decltype(bc)::value;
     const int kb = k_begin + b * kBlk;
     if ((b & 1) != par) return;
-    await(&cnt[kCntBlock + b], kLoaderWaves);
+    await(&cnt[kCntBlock + b], kLoaderWaves, a.spin_limit, expired);
     if (kb < k_end) {
       const uint8_t* tile = &tiles[b][0];
       f32x16 s;
@@ -368,7 +372,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_f8(F8Args a) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const f32x4* vsp = reinterpret_cast<const f32x4*>(&scl[b][2 * c + h][8]);
-        const f32x4 va = vsp[0], vb = vsp[1];
+        const f32x4 va = vsp[0] * 0x1p64f, vb = vsp[1] * 0x1p64f;  // 2^kF8VShift
         bf16x8 pb;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -390,12 +394,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_attn_f8(F8Args a) {
 
   // merge hand-off in tiles 2 qgrp and 2 qgrp + 1, once their blocks (if any) are consumed
   auto region_free = [&]() {
-    if (2 * qgrp < NB) await(&cnt[kCntDone + 2 * qgrp], 4);
-    if (2 * qgrp + 1 < NB) await(&cnt[kCntDone + 2 * qgrp + 1], 4);
+    if (2 * qgrp < NB) await(&cnt[kCntDone + 2 * qgrp], 4, a.spin_limit, expired);
+    if (2 * qgrp + 1 < NB) await(&cnt[kCntDone + 2 * qgrp + 1], 4, a.spin_limit, expired);
   };
   const long long part = (long long)g * a.n_split + split;
   merge_and_store_partial(o, m_run, l_run, NB >= 2, par, qgrp, lane, &tiles[2 * qgrp][0], &tiles[2 * qgrp + 1][0],
-                          region_free, mlx, cnt, a.po, a.pm, a.pl, part);
+                          region_free, mlx, cnt, a.po, a.pm, a.pl, a.pe, part, a.spin_limit, expired);
+  report_expired(a.status, expired, lane);
 }
 
 // Stand-alone tail write: row (tensor, head g, token i) of k (roped) and v quantised per row
@@ -419,7 +424,7 @@ __global__ __launch_bounds__(256) void k_tail_quant_f8(const uint16_t* k, const 
 }
 
 // Combine of the fp8 kernel's partials: out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c,
-// M = max_c m_c. Workgroup (head g, rows 8r .. 8r+7, column half hc): 512 threads in 4 split
+// M = max_c m_c, O_c the float16 partial times 2^(e_c). Workgroup (head g, rows 8r .. 8r+7, column half hc): 512 threads in 4 split
 // groups of 128 (8 rows x 16 column quads); group k reduces splits k, k + 4, ..., issuing the loads
 // of up to kCombBatch splits before using any of them, so the whole partial set is in flight at
 // once. The 8 rows of a (slot, half) of the accumulator layout are one 128-byte line. The groups
@@ -427,7 +432,7 @@ __global__ __launch_bounds__(256) void k_tail_quant_f8(const uint16_t* k, const 
 constexpr int kCombGroups = 4;
 constexpr int kCombBatch = 8;
 __global__ __launch_bounds__(512) void k_attn_f8_combine(const float* po, const float* pm, const float* pl,
-                                                         uint16_t* out, int n_split) {
+                                                         const int* pe, uint16_t* out, int n_split) {
   __shared__ float sM[kCombGroups][8], sL[kCombGroups][8];
   __shared__ f32x4 sA[kCombGroups][128];
   const int g = blockIdx.x % kHkv;
@@ -444,6 +449,7 @@ __global__ __launch_bounds__(512) void k_attn_f8_combine(const float* po, const 
   const int slot = 4 * tt + jj, lane = (q & 31) + 32 * h;
   const float* pmg = pm + (long long)g * n_split * kQRows + q;
   const float* plg = pl + (long long)g * n_split * kQRows + q;
+  const int* peg = pe + (long long)g * n_split * kQRows + q;
   const u32x2* pog = reinterpret_cast<const u32x2*>(po) + ((long long)g * n_split * 4 + (q >> 5)) * (16 * 64) +
                      slot * 64 + lane;
   const long long pstride = 4 * 16 * 64;  // 4-float16 groups per split partial
@@ -451,12 +457,14 @@ __global__ __launch_bounds__(512) void k_attn_f8_combine(const float* po, const 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int c0 = grp; c0 < n_split; c0 += kCombGroups * kCombBatch) {
     float mv[kCombBatch], lv[kCombBatch];
+    int ev[kCombBatch];
     f32x4 ov[kCombBatch];
 #pragma unroll
     for (int k = 0; k < kCombBatch; ++k) {
       const int c = min(c0 + kCombGroups * k, n_split - 1);  // past the end: a repeat, weighted 0 below
       mv[k] = pmg[(long long)c * kQRows];
       lv[k] = plg[(long long)c * kQRows];
+      ev[k] = peg[(long long)c * kQRows];
       ov[k] = unpack_f16x4(pog[(long long)c * pstride]);
     }
     __builtin_amdgcn_sched_barrier(0);  // every load of the batch is issued before any is used
@@ -472,7 +480,8 @@ __global__ __launch_bounds__(512) void k_attn_f8_combine(const float* po, const 
     for (int k = 0; k < kCombBatch; ++k) {
       const float w = (c0 + kCombGroups * k < n_split) ? __builtin_amdgcn_exp2f(mv[k] - M) : 0.f;
       L += w * lv[k];
-      acc[0] += w * ov[k][0]; acc[1] += w * ov[k][1]; acc[2] += w * ov[k][2]; acc[3] += w * ov[k][3];
+      const float wo = __builtin_ldexpf(w, ev[k]);  // O_c = float16 partial x 2^e_c
+      acc[0] += wo * ov[k][0]; acc[1] += wo * ov[k][1]; acc[2] += wo * ov[k][2]; acc[3] += wo * ov[k][3];
     }
   }
   if ((t & 15) == 0) {
@@ -503,24 +512,32 @@ __global__ __launch_bounds__(512) void k_attn_f8_combine(const float* po, const 
 
 static size_t align256_f8(size_t x) { return (x + 255) & ~size_t(255); }
 
+// The status word, then O, m, l and e, each 256-byte aligned.
 size_t attn_partials_bytes_f8(const AttnPlan& p) {
   const size_t parts = (size_t)kHkv * p.n_split;
-  return align256_f8(parts * kD * kQRows * 2) + 2 * align256_f8(parts * kQRows * 4);
+  return kStatusBytes + align256_f8(parts * kD * kQRows * 2) + 3 * align256_f8(parts * kQRows * 4);
 }
 
 WsLayoutF8 ws_layout_f8(const AttnPlan& plan, const void* ws) {
   const size_t parts = (size_t)kHkv * plan.n_split;
   char* w = static_cast<char*>(const_cast<void*>(ws));
   WsLayoutF8 l;
+  l.status = reinterpret_cast<int*>(w);
+  w += kStatusBytes;
   l.po = reinterpret_cast<float*>(w);
-  l.pm = reinterpret_cast<float*>(w + align256_f8(parts * kD * kQRows * 2));
-  l.pl = reinterpret_cast<float*>(w + align256_f8(parts * kD * kQRows * 2) + align256_f8(parts * kQRows * 4));
+  w += align256_f8(parts * kD * kQRows * 2);
+  l.pm = reinterpret_cast<float*>(w);
+  w += align256_f8(parts * kQRows * 4);
+  l.pl = reinterpret_cast<float*>(w);
+  w += align256_f8(parts * kQRows * 4);
+  l.pe = reinterpret_cast<int*>(w);
   return l;
 }
 
 hipError_t launch_attn_f8_combine(const AttnPlan& plan, const void* ws, uint16_t* out, hipStream_t st) {
   const WsLayoutF8 l = ws_layout_f8(plan, ws);
-  hipLaunchKernelGGL(k_attn_f8_combine, dim3(kHkv * 32), dim3(512), 0, st, l.po, l.pm, l.pl, out, plan.n_split);
+  hipLaunchKernelGGL(k_attn_f8_combine, dim3(kHkv * 32), dim3(512), 0, st, l.po, l.pm, l.pl, l.pe, out,
+                     plan.n_split);
   return hipGetLastError();
 }
 
@@ -566,6 +583,9 @@ hipError_t launch_attn_f8_split(const AttnPlan& plan, const AttnLaunchF8& p, hip
   a.po = l.po;
   a.pm = l.pm;
   a.pl = l.pl;
+  a.pe = l.pe;
+  a.status = l.status;
+  a.spin_limit = wait_limit();
   a.S = p.S;
   a.Smax = p.Smax;
   a.n_split = plan.n_split;

@@ -53,6 +53,8 @@ struct DecArgs {
   float* po;              // [8][n_split][8 rows][128]
   float* pm;              // [8][n_split][8]
   float* pl;
+  int* status;            // workspace status word
+  int spin_limit;         // polls before a wait gives up
   int pos, Smax, n_split, kps;
 };
 
@@ -78,6 +80,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void k_decode_attn(DecArgs a) {
 
   if (tid < kDcN) cnt[tid] = 0;
   lds_barrier();  // counters cleared (the only workgroup barrier)
+  bool expired = false;  // a bounded wait of this wave ran out
 
   if (wave >= kDecCompute) {
     // ---------------- loader waves: rows 8w .. 8w+7 of each block, K then V (two 1 KB loads each)
@@ -154,7 +157,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void k_decode_attn(DecArgs a) {
     }
     arrive(&cnt[kDcQ], lane);
   }
-  await(&cnt[kDcQ], 1);
+  await(&cnt[kDcQ], 1, a.spin_limit, expired);
 
   const int n = lane & 31;
   const int h = lane >> 5;
@@ -190,7 +193,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void k_decode_attn(DecArgs a) {
     constexpr int b = decltype(bc)::value;
     if (b % kDecCompute != wave) return;
     const int kb = k_begin + b * kBlk;
-    await(&cnt[kDcBlock + b], kDecCompute);
+    await(&cnt[kDcBlock + b], kDecCompute, a.spin_limit, expired);
     if (kb >= k_end) return;
     uint8_t* tile = &tiles[b][0];
     // (a split's last block can reach past the split's end: key pos must be one of this split's)
@@ -248,19 +251,23 @@ __global__ __launch_bounds__(kDecThreads, 1) void k_decode_attn(DecArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
     }
-    float psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sc, -m_run));
-      psum += s[i];
-    }
-    l_run += psum;
+    for (int i = 0; i < 16; ++i) s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sc, -m_run));
+    // the row sum adds the same bf16-rounded p that the PV product uses, so each output row is an
+    // exact convex combination of v rows
+    const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+    float ps[2] = {0.f, 0.f};
     const uint8_t* tv = tile + kDecTile / 2;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       bf16x8 pb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[8 * c + e];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2_t pr = {pb[e], pb[e + 1]};
+        ps[c] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ps[c], false);
+      }
       v4i16 vt[4][2];
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -276,6 +283,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void k_decode_attn(DecArgs a) {
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[t], 0, 0, 0);
       }
     }
+    l_run += ps[0] + ps[1];
   });
 
   // merge of the compute waves (rows 0..7: lanes n < 8 of both halves), then the partial
@@ -295,9 +303,11 @@ __global__ __launch_bounds__(kDecThreads, 1) void k_decode_attn(DecArgs a) {
       }
     }
     arrive(&cnt[kDcMerge], lane);
+    report_expired(a.status, expired, lane);
     return;
   }
-  await(&cnt[kDcMerge], kDecCompute - 1);
+  await(&cnt[kDcMerge], kDecCompute - 1, a.spin_limit, expired);
+  report_expired(a.status, expired, lane);
   if (n >= kDecRows) return;
   float m_all = m_run, l_all = l_tot;  // block 0 holds a visible key: m_run is finite
 #pragma unroll
@@ -327,7 +337,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void k_decode_attn(DecArgs a) {
     for (int jj = 0; jj < 4; ++jj)
       po[(32 * t + 8 * jj + 4 * h) / 4] = f32x4{o[t][4 * jj], o[t][4 * jj + 1], o[t][4 * jj + 2], o[t][4 * jj + 3]};
   if (h == 0) {
-    a.pm[prow] = m_all;
+    a.pm[prow] = expired ? __builtin_nanf("") : m_all;
     a.pl[prow] = l_all;
   }
 }
@@ -411,9 +421,10 @@ AttnPlan decode_plan(int pos) {
 
 static size_t align256d(size_t x) { return (x + 255) & ~size_t(255); }
 
+// The status word, then O, m and l, each 256-byte aligned.
 size_t decode_partials_bytes(const AttnPlan& p) {
   const size_t rows = (size_t)kHkv * p.n_split * kDecRows;
-  return align256d(rows * kD * 4) + 2 * align256d(rows * 4);
+  return kStatusBytes + align256d(rows * kD * 4) + 2 * align256d(rows * 4);
 }
 
 template <int NB>
@@ -426,6 +437,9 @@ hipError_t launch_decode(const AttnPlan& plan, const DecodeLaunch& p, hipStream_
   const size_t rows = (size_t)kHkv * plan.n_split * kDecRows;
   char* w = static_cast<char*>(p.ws);
   DecArgs a;
+  a.status = reinterpret_cast<int*>(w);
+  a.spin_limit = wait_limit();
+  w += kStatusBytes;
   a.q = p.q; a.k = p.k; a.v = p.v; a.gq = p.gq; a.gk = p.gk; a.cos_t = p.cos_t; a.sin_t = p.sin_t; a.eps = p.eps;
   a.Kc = p.Kc; a.Vc = p.Vc;
   a.po = reinterpret_cast<float*>(w);

@@ -37,10 +37,17 @@ struct AttnPlan {
 AttnPlan attn_plan(int S, int Smax);     // bf16 cache
 AttnPlan attn_plan_f8(int S, int Smax);  // fp8 cache (longer splits: a block is half the bytes)
 
-// bf16 partials inside the workspace, one row per (kv head, key range, folded query row): O
-// [8][n_split][128][128] float16 scaled by 2^-e per (row, 32-column quarter), m and l
-// [8][n_split][128] float, e [8][n_split][128][4] int; each 256-byte aligned.
+// Polls a bounded in-workgroup wait makes before it gives up: the default (about 30 ms of
+// polling), or the value set through ax_debug_set_wait_limit.
+constexpr int kDefaultWaitLimit = 1 << 20;
+int wait_limit();
+
+// bf16 partials inside the workspace, after the status word (the first 256 bytes): one row per
+// (kv head, key range, folded query row): O [8][n_split][128][128] float16 scaled by 2^-e per
+// (row, 32-column quarter), m and l [8][n_split][128] float, e [8][n_split][128][4] int; each
+// 256-byte aligned.
 struct WsLayout {
+  int* status;
   uint16_t* po;
   float* pm;
   float* pl;
@@ -49,13 +56,15 @@ struct WsLayout {
 size_t attn_partials_bytes(const AttnPlan& p);
 WsLayout ws_layout(const AttnPlan& plan, const void* ws);
 
-// fp8-cache partials: O [8][n_split][4][16][64] groups of 4 float16 (scaled by a power of two per
-// (split, row) that is folded into m and l), then m and l [8][n_split][128] float, each 256-byte
-// aligned.
+// fp8-cache partials, after the status word: O [8][n_split][4][16][64] groups of 4 float16
+// (scaled by 2^-e per (split, row)), then m and l [8][n_split][128] float and e
+// [8][n_split][128] int, each 256-byte aligned.
 struct WsLayoutF8 {
+  int* status;
   float* po;
   float* pm;
   float* pl;
+  int* pe;
 };
 size_t attn_partials_bytes_f8(const AttnPlan& p);
 WsLayoutF8 ws_layout_f8(const AttnPlan& plan, const void* ws);

@@ -437,6 +437,8 @@ static size_t layer_ws_layout(const AttnPlan& plan, void* ws, LayerWs* l) {
     off += al256(bytes);
     return p;
   };
+  // the attention step's workspace first: its status word is the layer workspace's
+  void* attn_ws = take(attn_partials_bytes(plan));
   const size_t act = (size_t)kGemmM * kLayerHidden * 2;
   uint16_t* n1 = reinterpret_cast<uint16_t*>(take(act));
   uint16_t* q = reinterpret_cast<uint16_t*>(take((size_t)kHq * kGemmM * 128 * 2));
@@ -446,7 +448,6 @@ static size_t layer_ws_layout(const AttnPlan& plan, void* ws, LayerWs* l) {
   uint16_t* x2 = reinterpret_cast<uint16_t*>(take(act));
   uint16_t* n2 = reinterpret_cast<uint16_t*>(take(act));
   uint16_t* mlp = reinterpret_cast<uint16_t*>(take((size_t)kGemmM * kLayerMlp * 2));
-  void* attn_ws = take(attn_partials_bytes(plan));
   // float32 partials of the largest projection (gate and up share one launch: rows of 2 x 6144)
   size_t pmax = 0;
   for (size_t b : {(size_t)gemm_splits(kCfgQkv, kLayerHidden) * kGemmM * kLayerQkv * 4,

@@ -40,7 +40,17 @@
  *   written; a positive value = the hipError_t of a failed launch.
  * - Calls on the same cache/workspace buffers must be ordered on one stream
  *   (or synchronised); the library keeps no state between calls besides a
- *   per-device record of whether the device is a gfx950.
+ *   per-device record of whether the device is a gfx950 and the debug wait
+ *   limit (ax_debug_set_wait_limit).
+ * - Workspace status word: the first 4 bytes of the workspace of every
+ *   attention entry point (bf16 and fp8 cache, decode, whole layer) are an
+ *   int32 status word (the first 256 bytes are reserved for it). The kernels OR AX_STATUS_* flags into it and never clear it; the
+ *   rest of a workspace holds scratch whose contents on entry do not matter.
+ *   A caller that wants the status zeroes the word once and reads it back
+ *   after synchronising. AX_STATUS_WAIT_EXPIRED: a workgroup's bounded wait
+ *   for an in-workgroup hand-off gave up (by default after about 30 ms of
+ *   polling, thousands of times any real wait); the workgroup finishes anyway,
+ *   the affected split's result is NaN, and the output must not be trusted.
  */
 #ifndef AX_H
 #define AX_H
@@ -70,8 +80,19 @@ enum {
   AX_E_ARG = -6          /* another invalid scalar (eps < 0 or not finite, theta <= 0, ...) */
 };
 
+#define AX_STATUS_WAIT_EXPIRED 1
+
 /* ABI version of the loaded library (AX_ABI_VERSION). */
 int ax_abi_version(void);
+
+/*
+ * Debug setting, process-wide: the number of polls after which a bounded
+ * in-workgroup wait gives up, for launches enqueued after the call
+ * (0 = the default). A tiny limit makes waits give up early, so that the
+ * AX_STATUS_WAIT_EXPIRED path can be exercised without a hang; results are
+ * then wrong by design. AX_E_ARG for polls < 0.
+ */
+int ax_debug_set_wait_limit(int polls);
 
 /* Static text for a return code of any entry point (never NULL). */
 const char* ax_strerror(int code);
@@ -120,8 +141,10 @@ int ax_qk_norm_rope_tail(const uint16_t* q_in, const uint16_t* k_in, const uint1
 
 /*
  * Bytes of caller-owned device workspace that ax_expert_attn and
- * ax_expert_layer_attn need for (S, Smax): the per-split partial outputs,
- * running maxima and row sums (float32). 0 if (S, Smax) is invalid.
+ * ax_expert_layer_attn need for (S, Smax): the status word, then the
+ * per-split partials (O in float16 scaled by a power of two per row and
+ * 32-column quarter, with the exponents; running maxima and row sums in
+ * float32). 0 if (S, Smax) is invalid.
  */
 size_t ax_expert_attn_workspace_bytes(int S, int Smax);
 
@@ -136,9 +159,12 @@ size_t ax_expert_attn_workspace_bytes(int S, int Smax);
  * written; exactly one NULL is AX_E_NULL.
  * out: [16][64][128] bf16 (nearest-even rounding of the float32 result).
  * Arithmetic: bf16 products on the matrix cores, float32 accumulation,
- * float32 softmax and split combine. ws: workspace of at least
- * ax_expert_attn_workspace_bytes(S, Smax) bytes, 256-byte aligned; its
- * contents on entry do not matter and on return are unspecified.
+ * float32 softmax and split combine; the split partials pass through
+ * float16 with a power-of-two scale per (row, 32-column quarter), which keeps
+ * 11 significant bits of every element within 2^14 of its quarter's largest
+ * |value|. ws: workspace of at least ax_expert_attn_workspace_bytes(S, Smax)
+ * bytes, 256-byte aligned; apart from the status word its contents on entry
+ * do not matter and on return are unspecified.
  */
 int ax_expert_attn(const uint16_t* q_roped, const uint16_t* k_own, const uint16_t* v_own,
                    uint16_t* Kc, uint16_t* Vc, int S, int Smax, uint16_t* out, void* ws,
@@ -160,8 +186,9 @@ int ax_expert_layer_attn(const uint16_t* q_in, const uint16_t* k_in, const uint1
  * The two launches of ax_expert_layer_attn, for callers that time or order
  * them separately (same pages and passages as above).
  * ax_expert_layer_attn_split: q/k RMSNorm, RoPE, the cache tail write and the
- * split attention; every split's partial (unnormalised O, running max, row
- * sum; float32) is left in ws. ax_expert_attn_combine: the log-sum-exp
+ * split attention; every split's partial (unnormalised O in scaled float16
+ * with its exponents, running max and row sum in float32) is left in ws.
+ * ax_expert_attn_combine: the log-sum-exp
  * combine of the partials in ws for the same (S, Smax) into out. The two in
  * this order on one stream with the same ws equal ax_expert_layer_attn. The
  * combine reads only ws; it is undefined unless the split call for (S, Smax)
@@ -208,9 +235,12 @@ int ax_cache_tail_write_fp8(const uint16_t* k_roped, const uint16_t* v, uint8_t*
  * are NULL the tail is taken as already written. Scores and the value sum use
  * the dequantised rows: each e4m3 code is converted exactly to bf16 for the
  * matrix cores, the key scales multiply the float32 scores and the value
- * scales the float32 softmax weights before they are rounded to bf16.
+ * scales (times a fixed 2^64, taken back out in the combine) the float32
+ * softmax weights before they are rounded to bf16; value scales from the
+ * float32 denormals up to 2^25 keep those products in bf16's normal range.
  * ws: at least ax_expert_attn_fp8_workspace_bytes(S, Smax) bytes, 256-byte
- * aligned.
+ * aligned (the status word, then partials as for the bf16 cache with one
+ * power-of-two scale per row).
  */
 int ax_expert_attn_fp8(const uint16_t* q_roped, const uint16_t* k_own, const uint16_t* v_own,
                        uint8_t* Kc8, float* Ks, uint8_t* Vc8, float* Vs, int S, int Smax,
@@ -250,8 +280,8 @@ int ax_expert_attn_fp8_combine(const void* ws, size_t ws_bytes, int S, int Smax,
  * scale 1/sqrt(128); out [64][128] bf16. Rows after pos are never read; every
  * row except pos is left untouched. 0 <= pos < Smax <= AX_SMAX_LIMIT.
  * ws: at least ax_text_decode_workspace_bytes(pos, Smax) bytes, 256-byte
- * aligned, contents on entry irrelevant. Two launches (split attention,
- * combine).
+ * aligned; apart from the status word its contents on entry do not matter.
+ * Two launches (split attention, combine).
  */
 size_t ax_text_decode_workspace_bytes(int pos, int Smax);
 int ax_text_decode_attn(const uint16_t* q_in, const uint16_t* k_in, const uint16_t* v_in,
@@ -275,8 +305,8 @@ int ax_text_decode_attn(const uint16_t* q_in, const uint16_t* k_in, const uint16
  * hands a bf16 tensor to the next (rounded to nearest even); inside an op the
  * arithmetic is float32 (products of bf16 on the matrix cores). Updates the
  * cache tail like ax_expert_layer_attn. x_out must not alias x_in. ws: at least
- * ax_expert_layer_workspace_bytes(S, Smax) bytes, 256-byte aligned. Eleven
- * launches.
+ * ax_expert_layer_workspace_bytes(S, Smax) bytes, 256-byte aligned, starting
+ * with the status word. Eleven launches.
  */
 size_t ax_expert_layer_workspace_bytes(int S, int Smax);
 int ax_expert_layer(const uint16_t* x_in, const uint16_t* ln1, const uint16_t* wqkv,

@@ -34,6 +34,35 @@ def pcc(a: np.ndarray, b: np.ndarray) -> float:
     return float(a @ b / np.sqrt((a @ a) * (b @ b)))
 
 
+GUARD_BYTES = 4096   # keeps 256-byte alignment of what lies between the guards
+GUARD_BYTE = 0xA5
+
+
+class Guarded:
+    """A device buffer of nbytes between two GUARD_BYTES bands of a fixed byte: every write of a
+    kernel must land inside (check() asserts both bands unchanged)."""
+
+    def __init__(self, nbytes: int, fill: int = 0):
+        self.nbytes = nbytes
+        self.buf = torch.full((nbytes + 2 * GUARD_BYTES,), GUARD_BYTE, dtype=torch.uint8, device=DEV)
+        self.t = self.buf[GUARD_BYTES:GUARD_BYTES + nbytes]
+        self.t.fill_(fill)
+        assert self.t.data_ptr() % 256 == 0
+
+    def check(self, what: str = "buffer") -> None:
+        torch.cuda.synchronize()
+        head = self.buf[:GUARD_BYTES]
+        tail = self.buf[GUARD_BYTES + self.nbytes:]
+        assert bool((head == GUARD_BYTE).all()), f"{what}: bytes before the buffer were written"
+        assert bool((tail == GUARD_BYTE).all()), f"{what}: bytes after the buffer were written"
+
+
+def assert_status_clear(ax, ws) -> None:
+    """The workspace status word: no bounded wait of any launch on ws gave up."""
+    st = ax.workspace_status(ws)
+    assert st == 0, f"workspace status word {st:#x} (AX_STATUS_WAIT_EXPIRED = 1)"
+
+
 def metrics(got: np.ndarray, ref: np.ndarray) -> dict:
     err = got - ref
     return {"max_abs": float(np.max(np.abs(err))), "pcc": pcc(got, ref),
@@ -52,11 +81,14 @@ class Layer:
         cos, sin = ax.rope_tables(self.S + inp["rope_delta"])
         self.cos = torch.from_numpy(cos).to(DEV)
         self.sin = torch.from_numpy(sin).to(DEV)
-        self.out = torch.zeros((16, 64, 128), dtype=torch.int16, device=DEV)
+        # the output and the workspace sit between guard bands; the workspace starts zeroed (its
+        # status word is then read back after every call)
+        self.out_g = Guarded(16 * 64 * 128 * 2)
+        self.out = self.out_g.t.view(torch.int16).view(16, 64, 128)
         nbytes = ax.expert_attn_workspace_bytes(self.S, self.Smax)
         assert nbytes > 0
-        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
-        assert self.ws.data_ptr() % 256 == 0
+        self.ws_g = Guarded(nbytes)
+        self.ws = self.ws_g.t
         # shapes the kernels assume
         assert self.Kc.shape == (8, self.Smax, 128) and self.Vc.shape == (8, self.Smax, 128)
         assert self.q.shape == (16, 64, 128) and self.k.shape == (8, 64, 128) and self.v.shape == (8, 64, 128)
@@ -66,4 +98,8 @@ class Layer:
         ax.expert_layer_attn(self.q, self.k, self.v, self.gq, self.gk, self.cos, self.sin, eps, self.Kc, self.Vc,
                              self.S, self.Smax, self.out, self.ws)
         torch.cuda.synchronize()
+        self.out_g.check("out")
+        self.ws_g.check("workspace")
+        if self.ws is self.ws_g.t:
+            assert_status_clear(ax, self.ws)
         return down(self.out)

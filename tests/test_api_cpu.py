@@ -145,14 +145,20 @@ def test_fp8_workspace_bytes():
 
 
 def test_bf16_workspace_holds_one_partial_row_per_range_and_query_row():
-    # 15 cache key ranges of 10 blocks + the own-token range at S = 4700; per (kv head, range, folded
-    # query row): 128 float16 of O, m and l (float32) and 4 exponents (int32)
+    # the 256-byte status word block, then, with 15 cache key ranges of 10 blocks + the own-token
+    # range at S = 4700, per (kv head, range, folded query row): 128 float16 of O, m and l (float32)
+    # and 4 exponents (int32)
     per_row = 128 * 2 + 4 + 4 + 4 * 4
-    assert ax.expert_attn_workspace_bytes(4700, 8192) == 16 * 8 * 128 * per_row
-    assert ax.expert_attn_workspace_bytes(4700, 5120) == 16 * 8 * 128 * per_row   # rows read, not Smax, set it
-    assert ax.expert_attn_workspace_bytes(0, 64) == 1 * 8 * 128 * per_row         # the own range alone
+    assert ax.expert_attn_workspace_bytes(4700, 8192) == 256 + 16 * 8 * 128 * per_row
+    assert ax.expert_attn_workspace_bytes(4700, 5120) == 256 + 16 * 8 * 128 * per_row   # rows read, not Smax
+    assert ax.expert_attn_workspace_bytes(0, 64) == 256 + 1 * 8 * 128 * per_row         # the own range alone
     # ranges never exceed 10 blocks: long caches take more ranges
-    assert ax.expert_attn_workspace_bytes(65472, 65536) >= (65472 // 320 + 1) * 8 * 128 * per_row
+    assert ax.expert_attn_workspace_bytes(65472, 65536) >= 256 + (65472 // 320 + 1) * 8 * 128 * per_row
+
+
+def test_debug_wait_limit_rejects_negative():
+    assert ax.lib.ax_debug_set_wait_limit(-1) == ax.AX_E_ARG
+    assert ax.lib.ax_debug_set_wait_limit(0) == ax.AX_OK   # back to the default
 
 
 def test_fp8_validation_codes():

@@ -13,7 +13,7 @@ import torch
 import oracle
 from flow_matching_action_amd import synth
 
-from gpu_util import DEV, bf16_to_f64, down, metrics, say, up
+from gpu_util import DEV, Guarded, assert_status_clear, bf16_to_f64, down, metrics, say, up
 
 pytestmark = pytest.mark.gpu
 
@@ -46,11 +46,12 @@ class Layer8:
         self.Ks, self.Vs = up8(inp["Ks"]), up8(inp["Vs"])
         cos, sin = ax.rope_tables(self.S + inp["rope_delta"])
         self.cos, self.sin = torch.from_numpy(cos).to(DEV), torch.from_numpy(sin).to(DEV)
-        self.out = torch.zeros((16, 64, 128), dtype=torch.int16, device=DEV)
+        self.out_g = Guarded(16 * 64 * 128 * 2)
+        self.out = self.out_g.t.view(torch.int16).view(16, 64, 128)
         nbytes = ax.expert_attn_fp8_workspace_bytes(self.S, self.Smax)
         assert nbytes > 0
-        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
-        assert self.ws.data_ptr() % 256 == 0
+        self.ws_g = Guarded(nbytes)
+        self.ws = self.ws_g.t
         assert self.Kc.shape == (8, self.Smax, 128) and self.Kc.dtype == torch.uint8
         assert self.Ks.shape == (8, self.Smax) and self.Ks.dtype == torch.float32
         assert self.Vc.shape == self.Kc.shape and self.Vs.shape == self.Ks.shape
@@ -60,6 +61,10 @@ class Layer8:
         ax.expert_layer_attn_fp8(self.q, self.k, self.v, self.gq, self.gk, self.cos, self.sin, eps, self.Kc, self.Ks,
                                  self.Vc, self.Vs, self.S, self.Smax, self.out, self.ws)
         torch.cuda.synchronize()
+        self.out_g.check("out")
+        self.ws_g.check("workspace")
+        if self.ws is self.ws_g.t:
+            assert_status_clear(ax, self.ws)
         return down(self.out)
 
 

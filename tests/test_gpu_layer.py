@@ -20,7 +20,7 @@ import torch
 import oracle
 from flow_matching_action_amd import synth
 
-from gpu_util import DEV, bf16_to_f64, down, metrics, say, up
+from gpu_util import DEV, Guarded, assert_status_clear, bf16_to_f64, down, metrics, say, up
 
 pytestmark = pytest.mark.gpu
 
@@ -130,16 +130,22 @@ class LayerBufs:
         cos, sin = ax.rope_tables(S + rope_delta)
         self.cos = torch.from_numpy(cos).to(DEV)
         self.sin = torch.from_numpy(sin).to(DEV)
-        self.out = torch.zeros((64, 1536), dtype=torch.int16, device=DEV)
+        self.out_g = Guarded(64 * 1536 * 2)
+        self.out = self.out_g.t.view(torch.int16).view(64, 1536)
         nb = ax.expert_layer_workspace_bytes(S, Smax)
         assert nb > 0
-        self.ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
-        assert self.ws.data_ptr() % 256 == 0
+        self.ws_g = Guarded(nb)
+        self.ws = self.ws_g.t
 
     def run(self, ax):
         w = self.w
         ax.expert_layer(self.x, w["ln1"], w["wqkv"], w["qn"], w["kn"], w["wo"], w["ln2"], w["w1"], w["w3"], w["w2"],
                         self.cos, self.sin, 1e-6, self.Kc, self.Vc, self.S, self.Smax, self.out, self.ws)
+        torch.cuda.synchronize()
+        self.out_g.check("out")
+        self.ws_g.check("workspace")
+        if self.ws is self.ws_g.t:
+            assert_status_clear(ax, self.ws)
 
 
 def _ref(w, x, cache, S, Smax, rope_delta=0):

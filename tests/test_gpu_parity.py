@@ -12,7 +12,7 @@ import torch
 import oracle
 from flow_matching_action_amd import synth
 
-from gpu_util import DEV, Layer, bf16_to_f64, down, metrics, say, up
+from gpu_util import DEV, Guarded, Layer, assert_status_clear, bf16_to_f64, down, metrics, say, up
 
 pytestmark = pytest.mark.gpu
 
