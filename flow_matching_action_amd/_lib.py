@@ -65,6 +65,8 @@ lib.ax_expert_attn.argtypes = [_P, _P, _P, _P, _P, _I, _I, _P, _P, ctypes.c_size
 lib.ax_expert_layer_attn.restype = _I
 lib.ax_expert_layer_attn.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _I, _I, _P, _P,
                                      ctypes.c_size_t, _P]
+lib.ax_expert_layer_attn_noalloc.restype = _I
+lib.ax_expert_layer_attn_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _I, _I, _P, _P]
 lib.ax_expert_layer_attn_split.restype = _I
 lib.ax_expert_layer_attn_split.argtypes = [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _I, _I, _P,
                                            ctypes.c_size_t, _P]
@@ -102,7 +104,8 @@ lib.ax_linear_m64.argtypes = [_P, _P, _I, _I, _P, _P, ctypes.c_size_t, _P]
 lib.ax_copy_words.restype = _I
 lib.ax_copy_words.argtypes = [_P, _P, ctypes.c_size_t, _P]
 
-EXPORTS = ("ax_abi_version", "ax_strerror", "ax_debug_set_wait_limit", "ax_rope_tables", "ax_qk_norm_rope", "ax_cache_tail_write",
+EXPORTS = ("ax_abi_version", "ax_strerror", "ax_debug_set_wait_limit", "ax_rope_tables",
+           "ax_expert_layer_attn_noalloc", "ax_qk_norm_rope", "ax_cache_tail_write",
            "ax_qk_norm_rope_tail", "ax_expert_attn_workspace_bytes", "ax_expert_attn",
            "ax_expert_layer_attn", "ax_expert_layer_attn_split", "ax_expert_attn_combine",
            "ax_expert_attn_fp8_workspace_bytes", "ax_cache_tail_write_fp8", "ax_expert_attn_fp8",
@@ -188,6 +191,13 @@ def expert_attn(q_roped, k_own, v_own, Kc, Vc, S: int, Smax: int, out, ws, strea
     _check("ax_expert_attn", lib.ax_expert_attn(
         _ptr(q_roped), _ptr(k_own), _ptr(v_own), _ptr(Kc), _ptr(Vc), int(S), int(Smax), _ptr(out), _ptr(ws),
         ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
+
+
+def expert_layer_attn_noalloc(q_in, k_in, v_in, gamma_q, gamma_k, rope_cos, rope_sin, eps, Kc, Vc, S: int,
+                              Smax: int, out, stream=None):
+    _check("ax_expert_layer_attn_noalloc", lib.ax_expert_layer_attn_noalloc(
+        _ptr(q_in), _ptr(k_in), _ptr(v_in), _ptr(gamma_q), _ptr(gamma_k), _ptr(rope_cos), _ptr(rope_sin),
+        float(eps), _ptr(Kc), _ptr(Vc), int(S), int(Smax), _ptr(out), _stream(stream)))
 
 
 def expert_layer_attn(q_in, k_in, v_in, gamma_q, gamma_k, rope_cos, rope_sin, eps, Kc, Vc, S: int, Smax: int,

@@ -56,6 +56,34 @@ std::atomic<int> g_wait_limit{0};
 
 }  // namespace
 
+// Scratch of ax_expert_layer_attn_noalloc: one copy per GPU the library runs on, held until the
+// process ends. In host code the array's name is only a stand-in: kernels get the device address
+// that hipGetSymbolAddress returns for it on the current device (scratch_ptr).
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+std::atomic<void*> g_scratch[kMaxDev];
+
+// Device address of the current device's scratch, looked up on the device's first call (with
+// that device current) and kept per device.
+int scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return AX_E_UNSUPPORTED;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return static_cast<int>(e);
+    if (p == nullptr) return AX_E_UNSUPPORTED;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return AX_OK;
+}
+
+}  // namespace
+
 namespace ax {
 int wait_limit() {
   const int v = g_wait_limit.load(std::memory_order_relaxed);
@@ -169,6 +197,24 @@ int ax_expert_layer_attn(const uint16_t* q_in, const uint16_t* k_in, const uint1
   if (r == AX_OK) r = check_eps(eps);
   if (r == AX_OK) r = check_ws(ws, ws_bytes, S, Smax);
   if (r == AX_OK) r = check_device();
+  if (r != AX_OK) return r;
+  const ax::AttnPlan plan = ax::attn_plan(S, Smax);
+  ax::AttnLaunch p{q_in, gamma_q, gamma_k, rope_cos, rope_sin, eps, k_in, v_in, Kc, Vc, out, ws, S, Smax,
+                   /*q_norm=*/1};
+  return status(ax::launch_attn(plan, p, as_stream(stream)));
+}
+
+int ax_expert_layer_attn_noalloc(const uint16_t* q_in, const uint16_t* k_in, const uint16_t* v_in,
+                                 const uint16_t* gamma_q, const uint16_t* gamma_k, const float* rope_cos,
+                                 const float* rope_sin, float eps, uint16_t* Kc, uint16_t* Vc, int S, int Smax,
+                                 uint16_t* out, void* stream) {
+  int r = check_ptrs({q_in, k_in, v_in, gamma_q, gamma_k, rope_cos, rope_sin, Kc, Vc, out});
+  if (r == AX_OK) r = check_shape(S, Smax);
+  if (r == AX_OK) r = check_eps(eps);
+  if (r == AX_OK && ax_expert_attn_workspace_bytes(S, Smax) > kNoAllocScratchBytes) r = AX_E_WORKSPACE;
+  if (r == AX_OK) r = check_device();
+  void* ws = nullptr;
+  if (r == AX_OK) r = scratch_ptr(&ws);
   if (r != AX_OK) return r;
   const ax::AttnPlan plan = ax::attn_plan(S, Smax);
   ax::AttnLaunch p{q_in, gamma_q, gamma_k, rope_cos, rope_sin, eps, k_in, v_in, Kc, Vc, out, ws, S, Smax,

@@ -183,6 +183,26 @@ int ax_expert_layer_attn(const uint16_t* q_in, const uint16_t* k_in, const uint1
                          int Smax, uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * ax_expert_layer_attn for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): no workspace
+ * argument, and no allocation of any kind. The partials live in a static
+ * 16 MiB device array of the library, one per GPU, held until the process
+ * ends, so (S, Smax) whose ax_expert_attn_workspace_bytes exceeds 16 MiB
+ * (S > 18240) are AX_E_WORKSPACE. Nothing in that array needs to start at
+ * zero: each call writes every partial it reads; its status word is not
+ * reported (a wait that gives up still leaves NaN in the output). All calls on
+ * one GPU share the array, so calls that overlap on one GPU (on different
+ * streams, unordered) race and give wrong results; order them on one stream.
+ * Output, cache update and arithmetic are those of ax_expert_layer_attn, bit
+ * for bit.
+ */
+int ax_expert_layer_attn_noalloc(const uint16_t* q_in, const uint16_t* k_in, const uint16_t* v_in,
+                                 const uint16_t* gamma_q, const uint16_t* gamma_k,
+                                 const float* rope_cos, const float* rope_sin, float eps,
+                                 uint16_t* Kc, uint16_t* Vc, int S, int Smax, uint16_t* out,
+                                 void* stream);
+
+/*
  * The two launches of ax_expert_layer_attn, for callers that time or order
  * them separately (same pages and passages as above).
  * ax_expert_layer_attn_split: q/k RMSNorm, RoPE, the cache tail write and the
