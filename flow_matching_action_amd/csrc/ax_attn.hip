@@ -156,6 +156,18 @@ __device__ __forceinline__ void await_cnt(int i, int n, int limit, bool& expired
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Chunk swizzles of the ring's 256-byte K and V rows (16 chunks of 16 bytes). LDS serves a
+// ds_read_b128 for 16 lanes per cycle and a ds_read_b64_tr_b16 for 32, all 64 banks at once, so
+// those lanes must hit 16 distinct chunks; the swizzles also keep 8-lane (b128) and 16-lane (tr)
+// halves on 8 distinct chunks of the same 128-byte half as those of the other half.
+// K: lanes 0..15 read rows perm_key(0..15) = {0..3, 8..11, 4..7, 12..15} at one chunk c: rows
+// 0..3 and 8..11 go to c ^ 0..7, rows 4..7 and 12..15 to c ^ 8..15.
+__device__ __forceinline__ int kswz2(int r) { return (r & 3) | ((r >> 1) & 4) | ((r << 1) & 8); }
+// V: the 32 lanes of two 16-lane transpose groups read rows 4t .. 4t + 3 at chunks {c, c + 1} and
+// {c + 2, c + 3} (c even): 2 (r & 3) spreads a group over 8 chunks, 8 (r & 1) moves odd rows to the
+// other half of the row's chunks, so the two groups together take all 16.
+__device__ __forceinline__ int vswz2(int r) { return (2 * (r & 3)) ^ (8 * (r & 1)); }
+
 // Per-workgroup facts every wave shares.
 struct SplitCtx {
   int g, hp, split, k_begin, k_end, nb, lane;
@@ -174,8 +186,8 @@ __device__ __forceinline__ void dma_block_share(const uint16_t* kc, const uint16
     const int r = r0 + (c.lane >> 4);
     int v = c.k_begin + kBlk * b + r;
     v = v < c.k_end ? v : c.k_begin;
-    dma_x4(kc + (long long)v * kD + 8 * ((c.lane & 15) ^ kswz(r)), tile + r0 * 256);
-    dma_x4(vc + (long long)v * kD + 8 * ((c.lane & 15) ^ vswz(r)), tile + kSV + r0 * 256);
+    dma_x4(kc + (long long)v * kD + 8 * ((c.lane & 15) ^ kswz2(r)), tile + r0 * 256);
+    dma_x4(vc + (long long)v * kD + 8 * ((c.lane & 15) ^ vswz2(r)), tile + kSV + r0 * 256);
   }
 }
 
@@ -238,8 +250,8 @@ __device__ __forceinline__ void split_loader(const SplitArgs& a, const SplitCtx&
       const int tr0 = 16 * (L & 1) + 4 * i;
       const int tr = tr0 + r4;
       const int tok = 16 * L + 4 * i + r4;
-      dma_x4(kt + (long long)tok * kD + 8 * (j16 ^ kswz(tr)), ot + tr0 * 256);
-      dma_x4(vt + (long long)tok * kD + 8 * (j16 ^ vswz(tr)), ot + kSV + tr0 * 256);
+      dma_x4(kt + (long long)tok * kD + 8 * (j16 ^ kswz2(tr)), ot + tr0 * 256);
+      dma_x4(vt + (long long)tok * kD + 8 * (j16 ^ vswz2(tr)), ot + kSV + tr0 * 256);
     }
   }
   lds_barrier();  // counters cleared (the workgroup's only barrier)
@@ -331,8 +343,8 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
       for (int i = 0; i < 4; ++i) {
         const int tr = (16 * W + 4 * i + r4) & (kBlk - 1);
         const lds_u8* krow = ring + ((16 * W + 4 * i) >> 5) * kSTile + tr * 256;
-        klo[i] = lds_ld<uint2>(krow + pair_off_lo(j16, kswz(tr)));
-        khi[i] = lds_ld<uint2>(krow + pair_off_hi(j16, kswz(tr)));
+        klo[i] = lds_ld<uint2>(krow + pair_off_lo(j16, kswz2(tr)));
+        khi[i] = lds_ld<uint2>(krow + pair_off_hi(j16, kswz2(tr)));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -346,8 +358,8 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
       for (int i = 0; i < 4; ++i) {
         const int tr = (16 * W + 4 * i + r4) & (kBlk - 1);
         lds_u8* krow = ring + ((16 * W + 4 * i) >> 5) * kSTile + tr * 256;
-        lds_st(krow + pair_off_lo(j16, kswz(tr)), klo[i]);
-        lds_st(krow + pair_off_hi(j16, kswz(tr)), khi[i]);
+        lds_st(krow + pair_off_lo(j16, kswz2(tr)), klo[i]);
+        lds_st(krow + pair_off_hi(j16, kswz2(tr)), khi[i]);
       }
     }
   }
@@ -370,12 +382,12 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
   const int krow = perm_key(n);
   int koff[4];
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) koff[jj] = krow * 256 + 16 * ((4 * h + jj) ^ kswz(krow));
+  for (int jj = 0; jj < 4; ++jj) koff[jj] = krow * 256 + 16 * ((4 * h + jj) ^ kswz2(krow));
   const int G = lane >> 4, li = lane & 15;
   const int vrow0 = 8 * (G >> 1) + (li >> 2);
   const int vx = 2 * (G & 1) + ((li & 3) >> 1);
-  const int voff[2] = {vrow0 * 256 + 16 * (vx ^ vswz(vrow0)) + 8 * (li & 1),
-                       vrow0 * 256 + 16 * ((4 + vx) ^ vswz(vrow0)) + 8 * (li & 1)};
+  const int voff[2] = {vrow0 * 256 + 16 * (vx ^ vswz2(vrow0)) + 8 * (li & 1),
+                       vrow0 * 256 + 16 * ((4 + vx) ^ vswz2(vrow0)) + 8 * (li & 1)};
   f32x16 o[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = splat16(0.f);
@@ -387,9 +399,11 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
   bf16x8 pb[2];
   const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
   auto tile_of = [&](int b) { return ring + (b % kSRing) * kSTile; };  // (b uniform: scalar ops)
+  // (the chunks of columns 64 .. 127 are those of columns 0 .. 63 with bit 3 flipped: the
+  // tiles are 16 KB aligned, so the XOR acts on the offset alone)
   auto read_k = [&](const lds_u8* base) {
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) kf[kk] = lds_ld<bf16x8>(base + koff[kk & 3] + 128 * (kk >> 2));
+    for (int kk = 0; kk < 8; ++kk) kf[kk] = lds_ld<bf16x8>(base + (koff[kk & 3] ^ (128 * (kk >> 2))));
   };
   auto read_v = [&](const lds_u8* base) {
 #pragma unroll
@@ -399,7 +413,7 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
           vt[kh][dt][hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16*)(base + kSV + (16 * kh + 4 * hf) * 256 + 128 * (dt >> 1) + voff[dt & 1]));
+              (lds_v4i16*)(base + kSV + (16 * kh + 4 * hf) * 256 + (voff[dt & 1] ^ (128 * (dt >> 1)))));
   };
   auto qk = [&](f32x16& sd) {
     sd = splat16(0.f);
@@ -443,15 +457,26 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
       sd[i] = (kofs < lim) ? sd[i] : -INFINITY;
     }
   };
-  // the V reads of block b are done: both uses of its tile (the two row tiles) count here
+  // Release of block b's tile (both row tiles count here) right after its V reads are issued,
+  // without waiting for them: a wave's LDS operations execute in order, so the increment cannot
+  // pass the reads, and a loader that sees it only then starts loads that land far later.
   auto release = [&](int b) {
-    if (!c.own) arrive(&sCnt[kCDone + b % kSRing], lane);
+    if (c.own) return;
+    __builtin_amdgcn_sched_barrier(0);
+    if (lane == 0) {
+      const unsigned off = (unsigned)(uintptr_t)(lds_int*)&sCnt[kCDone + b % kSRing];
+      asm volatile("ds_add_u32 %0, %1" ::"v"(off), "v"(1) : "memory");
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
   auto landed = [&](int b) {
     if (c.own) return;  // the own blocks are ready with the normed query rows
     await_cnt(kCLand + b, kSL, a.spin_limit, expired);
   };
 
+  // K of block b + 2 is read at the end of iteration b, and its landed count is read early in
+  // the iteration (before the V reads), so that neither the poll nor the K reads wait behind
+  // this block's V reads; only a block not yet landed takes the blocking poll.
   if (NB > 0) {
     landed(P);
     read_k(tile_of(P));
@@ -460,16 +485,23 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
     m = tile_rowmax(s) * kScoreScale;  // finite: the block holds a visible key
     if (c.partial && P == c.nb - 1) mask_tail(s, P);
     release(P);
+    if (NB > 1) {
+      landed(P + 2);
+      read_k(tile_of(P + 2));
+    }
 #pragma clang loop unroll(disable)
     for (int k = 1; k < NB; ++k) {
       const int b = P + 2 * k;
-      landed(b);
-      read_k(tile_of(b));
-      // (A) scores of block b beside the exponentials of the previous block
+      const bool more = k + 1 < NB;
+      // (the count is read behind this block's K reads, which the scores need first anyway)
+      const int early = (more && !c.own)
+                            ? __hip_atomic_load(&sCnt[kCLand + b + 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
+                            : kSL;
+      // (A) scores of block b beside the exponentials of block b - 2
       f32x16 sn;
       qk(sn);
       softmax();
-      // (B) PV of the previous block beside the row max of block b
+      // (B) PV of block b - 2 beside the row max of block b
       pv();
       const float bm = tile_rowmax(sn) * kScoreScale;
       read_v(tile_of(b));
@@ -487,7 +519,11 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
       }
       if (c.partial && b == c.nb - 1) mask_tail(sn, b);
       s = sn;
-      release(b);  // at the iteration's end: its V reads have long been issued
+      release(b);
+      if (more) {
+        if (__builtin_amdgcn_readfirstlane(early) < kSL) landed(b + 2);
+        read_k(tile_of(b + 2));
+      }
     }
     softmax();
     pv();
@@ -502,8 +538,8 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
       const int tr = tok & (kBlk - 1);
       const lds_u8* ot = ring + (tok >> 5) * kSTile;
       const long long dst = head_off + (long long)(a.Smax - kT + tok) * kD + 8 * j16;
-      *reinterpret_cast<u32x4*>(a.Kc + dst) = lds_ld<u32x4>(ot + tr * 256 + 16 * (j16 ^ kswz(tr)));
-      *reinterpret_cast<u32x4*>(a.Vc + dst) = lds_ld<u32x4>(ot + kSV + tr * 256 + 16 * (j16 ^ vswz(tr)));
+      *reinterpret_cast<u32x4*>(a.Kc + dst) = lds_ld<u32x4>(ot + tr * 256 + 16 * (j16 ^ kswz2(tr)));
+      *reinterpret_cast<u32x4*>(a.Vc + dst) = lds_ld<u32x4>(ot + kSV + tr * 256 + 16 * (j16 ^ vswz2(tr)));
     }
   }
 
@@ -546,6 +582,7 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
   const int row = 64 * c.hp + 32 * T + n;  // folded row of head g
   auto store = [&](auto pc) {
     constexpr int PP = decltype(pc)::value;
+    int exj[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int dt = 2 * PP + j;
@@ -563,19 +600,25 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
     for (int i = 0; i < 16; ++i) mx = fmax_(mx, fabsf(acc[i]));
     const float2 mp = pair32(mx);
     const int ex = __builtin_amdgcn_frexp_expf(fmax_(mp.x, mp.y));  // 0 for an all-zero quarter
-    u32x2* po = reinterpret_cast<u32x2*>(a.part.po + (part * kQRows + row) * kD + 32 * dt + 4 * h);
+    exj[j] = ex;
+    // lane-native groups: each store writes 1 KB of contiguous bytes
+    u32x2 v[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      po[2 * q] = pack_f16x4(__builtin_ldexpf(acc[4 * q], -ex), __builtin_ldexpf(acc[4 * q + 1], -ex),
-                             __builtin_ldexpf(acc[4 * q + 2], -ex), __builtin_ldexpf(acc[4 * q + 3], -ex));
-    if (h == 0) a.part.pe[(part * kQRows + row) * 4 + dt] = ex;
+      v[q] = pack_f16x4(__builtin_ldexpf(acc[4 * q], -ex), __builtin_ldexpf(acc[4 * q + 1], -ex),
+                        __builtin_ldexpf(acc[4 * q + 2], -ex), __builtin_ldexpf(acc[4 * q + 3], -ex));
+    u32x4* po = reinterpret_cast<u32x4*>(a.part.po) + ((((part * 2 + c.hp) * 2 + T) * 4 + dt) * 64 + lane) * 2;
+    po[0] = u32x4{v[0][0], v[0][1], v[1][0], v[1][1]};
+    po[1] = u32x4{v[2][0], v[2][1], v[3][0], v[3][1]};
   }
+  // the two quarters' exponents as one word of the row's record (e[2 PP], e[2 PP + 1])
+  if (h == 0)
+    reinterpret_cast<uint32_t*>(&a.part.rec[part * kQRows + row])[2 + PP] =
+        (uint32_t)(exj[0] & 0xffff) | ((uint32_t)exj[1] << 16);
   };
   if (P == 0) store(std::integral_constant<int, 0>{}); else store(std::integral_constant<int, 1>{});
-  if (P == 0 && h == 0) {
-    a.part.pm[part * kQRows + row] = bad ? __builtin_nanf("") : M;
-    a.part.pl[part * kQRows + row] = L;
-  }
+  if (P == 0 && h == 0)
+    *reinterpret_cast<float2*>(&a.part.rec[part * kQRows + row]) = float2{bad ? __builtin_nanf("") : M, L};
   report_expired(a.part.status, expired, lane);
 }
 
@@ -606,31 +649,37 @@ __global__ __launch_bounds__(kSThreads, 1) void k_attn_split(SplitArgs a) {
 // float16 partial times 2^(its quarter's exponent). One wave per output row (kv head g, folded
 // row r), the splits taken 16 at a time: lane 16 dt + k holds split c0 + k's (m, l) and its
 // exponent for quarter dt; lane l then sums columns 2 l, 2 l + 1 over the splits in a fixed
-// order, rescaling between groups of 16 with the running max.
+// order, rescaling between groups of 16 with the running max. Columns 2 l, 2 l + 1 are elements
+// e, e + 1 (e = 2 (l & 1)) of group q = (l & 15) >> 2 of lane n + 32 h (h = (l >> 1) & 1) in the
+// split's 2 KB piece (hp, T, dt = l >> 4): one 4-byte load per split.
 // Workgroup w: head w % 8 (the XCD whose L2 took the head's partials), rows 4 (w / 8) .. +3.
 __global__ __launch_bounds__(256) void k_attn_combine(WsLayout p, uint16_t* out, int n_split) {
   const int lane = threadIdx.x & 63;
   const int g = blockIdx.x % kHkv;
   const int r = 4 * (blockIdx.x / kHkv) + (threadIdx.x >> 6);
+  const int dt = lane >> 4;
   const long long head = (long long)g * n_split;
+  const int grp = ((r >> 5) * 4 + dt);  // (hp * 2 + T) * 4 + dt, with r = 64 hp + 32 T + n
+  const int word = (((r & 31) + 32 * ((lane >> 1) & 1)) * 32 + 8 * ((lane & 15) >> 2) + 4 * (lane & 1)) / 4;
+  const uint32_t* pw = reinterpret_cast<const uint32_t*>(p.po) + (head * 16 + grp) * 512 + word;
   float M = -INFINITY, L = 0.f, acc0 = 0.f, acc1 = 0.f;
   for (int c0 = 0; c0 < n_split; c0 += 16) {
     const int cs = c0 + (lane & 15);
     const bool valid = cs < n_split;
     const int cl = valid ? cs : c0;  // lanes past n_split repeat split c0, weighted 0 below
-    const float mc = p.pm[(head + cl) * kQRows + r];
-    const float lc = p.pl[(head + cl) * kQRows + r];
-    const int ec = p.pe[((head + cl) * kQRows + r) * 4 + (lane >> 4)];
+    const f32x4 rv = *reinterpret_cast<const f32x4*>(p.rec + (head + cl) * kQRows + r);
+    const uint32_t ew = __float_as_uint(rv[2 + (dt >> 1)]);
+    const int ec = (dt & 1) ? (int)(int16_t)(ew >> 16) : (int)(int16_t)(ew & 0xffff);
     float2 ov[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int ck = c0 + k < n_split ? c0 + k : c0;
-      const uint32_t bits = *reinterpret_cast<const uint32_t*>(p.po + ((head + ck) * kQRows + r) * kD + 2 * lane);
+      const uint32_t bits = pw[(long long)ck * 16 * 512];
       const _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(bits & 0xffffu));
       const _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(bits >> 16));
       ov[k] = float2{(float)lo, (float)hi};
     }
-    float Mg = valid ? mc : -INFINITY;
+    float Mg = valid ? rv[0] : -INFINITY;
     Mg = fmaxf(Mg, row_ror<8>(Mg));
     Mg = fmaxf(Mg, row_ror<4>(Mg));
     Mg = fmaxf(Mg, row_ror<2>(Mg));
@@ -641,8 +690,8 @@ __global__ __launch_bounds__(256) void k_attn_combine(WsLayout p, uint16_t* out,
     acc1 *= rs;
     L *= rs;
     M = Mn;
-    const float w = valid ? __builtin_amdgcn_exp2f(mc - M) : 0.f;
-    float wl = w * lc;
+    const float w = valid ? __builtin_amdgcn_exp2f(rv[0] - M) : 0.f;
+    float wl = w * rv[1];
     wl += row_ror<8>(wl);
     wl += row_ror<4>(wl);
     wl += row_ror<2>(wl);
@@ -682,7 +731,7 @@ static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t attn_partials_bytes(const AttnPlan& p) {
   const size_t rows = (size_t)kHkv * p.n_split * kQRows;
-  return kStatusBytes + align256(rows * kD * 2) + 2 * align256(rows * 4) + align256(rows * 4 * 4);
+  return kStatusBytes + align256(rows * kD * 2) + align256(rows * sizeof(PartRec));
 }
 
 WsLayout ws_layout(const AttnPlan& plan, const void* ws) {
@@ -693,11 +742,7 @@ WsLayout ws_layout(const AttnPlan& plan, const void* ws) {
   w += kStatusBytes;
   l.po = reinterpret_cast<uint16_t*>(w);
   w += align256(rows * kD * 2);
-  l.pm = reinterpret_cast<float*>(w);
-  w += align256(rows * 4);
-  l.pl = reinterpret_cast<float*>(w);
-  w += align256(rows * 4);
-  l.pe = reinterpret_cast<int*>(w);
+  l.rec = reinterpret_cast<PartRec*>(w);
   return l;
 }
 

@@ -42,16 +42,21 @@ AttnPlan attn_plan_f8(int S, int Smax);  // fp8 cache (longer splits: a block is
 constexpr int kDefaultWaitLimit = 1 << 20;
 int wait_limit();
 
-// bf16 partials inside the workspace, after the status word (the first 256 bytes): one row per
-// (kv head, key range, folded query row): O [8][n_split][128][128] float16 scaled by 2^-e per
-// (row, 32-column quarter), m and l [8][n_split][128] float, e [8][n_split][128][4] int; each
-// 256-byte aligned.
+// bf16 partials inside the workspace, after the status word (the first 256 bytes), per (kv head
+// g, key range c) = part g * n_split + c: O in float16, scaled by 2^-e per (row, 32-column quarter
+// dt), in 2 KB groups (part, q head parity hp, row tile T, dt) of 64 lanes x 32 bytes (lane (n, h):
+// row 64 hp + 32 T + n, columns 32 dt + 8 q + 4 h .. +3 at byte 32 lane + 8 q); then one 16-byte
+// record per (part, folded row): float m, float l, int16 e[4]. Both regions 256-byte aligned.
+struct PartRec {
+  float m;
+  float l;
+  int16_t e[4];
+};
+static_assert(sizeof(PartRec) == 16, "one 16-byte load per record");
 struct WsLayout {
   int* status;
   uint16_t* po;
-  float* pm;
-  float* pl;
-  int* pe;
+  PartRec* rec;
 };
 size_t attn_partials_bytes(const AttnPlan& p);
 WsLayout ws_layout(const AttnPlan& plan, const void* ws);

@@ -7,13 +7,15 @@
 // op the arithmetic is float32.
 //
 // gfx950 mapping
+// - Weights are packed once (k_pack_w64) so that each 1 KB block holds, lane by lane, exactly the
+//   16-byte W^T operand a lane hands v_mfma_f32_32x32x16_bf16 for one (32-column block, 16-row
+//   step).
 // - k_gemm64: C[64, N] = A[64, K] W[K, N] for the 64 token rows. The weights are the stream
-//   (M = 64 is far below the ridge), so the grid is (N / 64 column tiles) x (K / KC splits) and
-//   each workgroup moves one KC x 64 weight tile and the matching 64 x KC slice of A into LDS
-//   with direct-to-LDS loads, then four waves each make one 32 x 32 tile of C^T = W^T A^T on
-//   v_mfma_f32_32x32x16_bf16: W^T comes from the row-major weight tile through
-//   ds_read_tr16_b64 (as V^T in the attention kernel), A^T straight from A's rows. The split's
-//   float32 partial goes to the workspace.
+//   (M = 64 is far below the ridge), so the grid is (N / (32 NB) column tiles) x (K / KC splits).
+//   Each wave loads its weight operands straight into registers (one plain 16-byte load per
+//   lane and step, non-temporal) while the workgroup's 64 x KC slice of A goes through LDS; the
+//   waves then run one 32 x 32 tile of C^T = W^T A^T each, the KW waves of a column block add
+//   their tiles through LDS, and the split's float32 partial goes to the workspace.
 // - k_gemm_reduce: sums the splits in a fixed order and applies the op's epilogue: the head
 //   split of qkv into q/k/v [heads][64][128], the residual add (o + x, d + x2), or SiLU(g) * u.
 // - k_rmsnorm_rows: one workgroup per token row; k_reduce_residual_norm: the o projection's

@@ -188,7 +188,7 @@ int ax_expert_layer_attn(const uint16_t* q_in, const uint16_t* k_in, const uint1
  * argument, and no allocation of any kind. The partials live in a static
  * 16 MiB device array of the library, one per GPU, held until the process
  * ends, so (S, Smax) whose ax_expert_attn_workspace_bytes exceeds 16 MiB
- * (S > 18240) are AX_E_WORKSPACE. Nothing in that array needs to start at
+ * (S > 18880) are AX_E_WORKSPACE. Nothing in that array needs to start at
  * zero: each call writes every partial it reads; its status word is not
  * reported (a wait that gives up still leaves NaN in the output). All calls on
  * one GPU share the array, so calls that overlap on one GPU (on different

@@ -3,14 +3,16 @@
 Test infrastructure only: imported by ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py``; the product path never touches it.
 
-The op sequence is the one page ``code/alpamayo_tt/EXPERT_NOTES.md`` lists per layer (section
-"Layouts": rms_norm -> linear(wqkv) -> nlp_create_qkv_heads -> q/k norms -> RoPE -> fill_cache ->
-attention -> nlp_concat_heads -> linear(wo) -> add -> rms_norm -> linear(w1, silu), linear(w3) ->
-mul -> linear(w2) -> add), with the shapes of its table: residual [64, 1536]; wqkv [1536, 4096]
-holding q heads 0..15, then k heads 0..7, then v heads 0..7 in its columns; wo [2048, 1536];
-w1 and w3 [1536, 6144]; w2 [6144, 1536]; all weights stored input-major ([in, out], the
-transpose of the HF layout, as the table says). Page ``code/alpamayo_tt/expert.py``,
-``TTExpert.layer``, is the same sequence in code.
+What it computes follows page ``code/alpamayo_tt/EXPERT_NOTES.md``, section "Layouts" (the
+per-layer op list and the weight-shape table), and page ``code/alpamayo_tt/expert.py``,
+``TTExpert.layer``: the residual x is RMS-normed and projected to q, k and v heads (16 + 8 + 8 of
+width 128, in that column order of the fused weight); the attention step of ``expert_attn_layer``
+runs on them; its heads are concatenated, projected back to the residual width and added to x;
+that sum is RMS-normed again and goes through the SwiGLU MLP (silu of one projection times
+another, then the down projection), whose result is added once more. Shapes: residual
+[64, 1536]; the fused qkv weight [1536, 4096]; the output projection [2048, 1536]; the two MLP
+up projections [1536, 6144] and the down projection [6144, 1536]; every weight is stored
+input-major ([in, out], the transpose of the HF layout), as the pages keep them.
 
 Reading (also in the design notes): every op hands a bf16 tensor to the next, as ttnn ops do
 (the pages' activations are bf16 throughout), so the oracle rounds to bf16 at each op boundary

@@ -146,9 +146,9 @@ def test_fp8_workspace_bytes():
 
 def test_bf16_workspace_holds_one_partial_row_per_range_and_query_row():
     # the 256-byte status word block, then, with 15 cache key ranges of 10 blocks + the own-token
-    # range at S = 4700, per (kv head, range, folded query row): 128 float16 of O, m and l (float32)
-    # and 4 exponents (int32)
-    per_row = 128 * 2 + 4 + 4 + 4 * 4
+    # range at S = 4700, per (kv head, range, folded query row): 128 float16 of O and a 16-byte
+    # record (m and l in float32, 4 exponents in int16)
+    per_row = 128 * 2 + 16
     assert ax.expert_attn_workspace_bytes(4700, 8192) == 256 + 16 * 8 * 128 * per_row
     assert ax.expert_attn_workspace_bytes(4700, 5120) == 256 + 16 * 8 * 128 * per_row   # rows read, not Smax
     assert ax.expert_attn_workspace_bytes(0, 64) == 256 + 1 * 8 * 128 * per_row         # the own range alone

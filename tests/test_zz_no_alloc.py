@@ -42,12 +42,13 @@ def test_noalloc_equals_workspace_entry_point(ax):
 def test_noalloc_rejects_shapes_beyond_its_scratch(ax):
     inp = synth.layer_inputs(256, 128, seed=603)
     b = Layer(inp, ax)
-    # S = 18240 fits (58 key ranges), S = 18241 needs a 59th: rejected on the host, nothing launched
-    fits = ax.expert_attn_workspace_bytes(18240, 20480)
-    over = ax.expert_attn_workspace_bytes(18241, 20480)
+    # S = 18880 fits (59 cache key ranges + the own one), S = 18881 needs one more: rejected on
+    # the host, nothing launched
+    fits = ax.expert_attn_workspace_bytes(18880, 20480)
+    over = ax.expert_attn_workspace_bytes(18881, 20480)
     assert fits <= 16 << 20 < over
     code = ax.lib.ax_expert_layer_attn_noalloc(b.q.data_ptr(), b.k.data_ptr(), b.v.data_ptr(), b.gq.data_ptr(),
                                                b.gk.data_ptr(), b.cos.data_ptr(), b.sin.data_ptr(), 1e-6,
-                                               b.Kc.data_ptr(), b.Vc.data_ptr(), 18241, 20480, b.out.data_ptr(),
+                                               b.Kc.data_ptr(), b.Vc.data_ptr(), 18881, 20480, b.out.data_ptr(),
                                                None)
     assert code == ax.AX_E_WORKSPACE
