@@ -212,6 +212,75 @@ __device__ __forceinline__ f32x16 splat16(float x) {
   return r;
 }
 
+// Norm + RoPE in place of query rows row0 .. row0 + 7 (two passes of 4 rows, 16 lanes per row:
+// the arithmetic of the stand-alone norm/RoPE kernel, so the bits are the same) and, in the own
+// range, of the own k rows of the same tokens (same RoPE rows, gamma k). The 64 rows are split
+// between the compute and the loader waves, two waves per SIMD, since a single wave issues vector
+// instructions at only half of a SIMD's rate. Within a pass every LDS read comes first, then the
+// arithmetic, then the stores, so that the rows' dependency chains interleave.
+__device__ __forceinline__ void norm_rows(const SplitArgs& a, const SplitCtx& c, const int row0) {
+  const int lane = c.lane, j16 = lane & 15, r4 = lane >> 4;
+  lds_u8* ring = AX_LDS(sRing);
+  float g8[8];
+  unpack_pair(lds_ld<uint2>(AX_LDS(sGam) + 8 * j16), lds_ld<uint2>(AX_LDS(sGam) + 128 + 8 * j16), g8);
+  uint2 lo[2], hi[2];
+  float cc[2][4], ss[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = row0 + 4 * i + r4;  // query row = token
+    lo[i] = lds_ld<uint2>(AX_LDS(sQ) + r * 256 + pair_off_lo(j16, qswz(r)));
+    hi[i] = lds_ld<uint2>(AX_LDS(sQ) + r * 256 + pair_off_hi(j16, qswz(r)));
+    const f32x4 cs = lds_ld<f32x4>(AX_LDS(sRope) + (row0 + 4 * i) * 256 + 16 * lane);
+    const f32x4 sn = lds_ld<f32x4>(AX_LDS(sRope) + kT * 256 + (row0 + 4 * i) * 256 + 16 * lane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      cc[i][e] = cs[e];
+      ss[i][e] = sn[e];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    float x[8], A[8], B[8];
+    unpack_pair(lo[i], hi[i], x);
+    rope_coef_pair(g8, cc[i], ss[i], A, B);
+    norm_rope_pair(x, A, B, a.eps);
+    pack_pair(x, lo[i], hi[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = row0 + 4 * i + r4;
+    lds_st(AX_LDS(sQ) + r * 256 + pair_off_lo(j16, qswz(r)), lo[i]);
+    lds_st(AX_LDS(sQ) + r * 256 + pair_off_hi(j16, qswz(r)), hi[i]);
+  }
+  if (c.own) {
+    float gk8[8];
+    unpack_pair(lds_ld<uint2>(AX_LDS(sGam) + 256 + 8 * j16), lds_ld<uint2>(AX_LDS(sGam) + 384 + 8 * j16), gk8);
+    uint2 klo[2], khi[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int tr = (row0 + 4 * i + r4) & (kBlk - 1);
+      const lds_u8* krow = ring + ((row0 + 4 * i) >> 5) * kSTile + tr * 256;
+      klo[i] = lds_ld<uint2>(krow + pair_off_lo(j16, kswz2(tr)));
+      khi[i] = lds_ld<uint2>(krow + pair_off_hi(j16, kswz2(tr)));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      float y[8], kA[8], kB[8];
+      rope_coef_pair(gk8, cc[i], ss[i], kA, kB);
+      unpack_pair(klo[i], khi[i], y);
+      norm_rope_pair(y, kA, kB, a.eps);
+      pack_pair(y, klo[i], khi[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int tr = (row0 + 4 * i + r4) & (kBlk - 1);
+      lds_u8* krow = ring + ((row0 + 4 * i) >> 5) * kSTile + tr * 256;
+      lds_st(krow + pair_off_lo(j16, kswz2(tr)), klo[i]);
+      lds_st(krow + pair_off_hi(j16, kswz2(tr)), khi[i]);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------- loaders
 template <bool NORM>
 __device__ __forceinline__ void split_loader(const SplitArgs& a, const SplitCtx& c, int L) {
@@ -259,6 +328,10 @@ __device__ __forceinline__ void split_loader(const SplitArgs& a, const SplitCtx&
   if (c.own) {
     vm_wait<0>();
     arrive(&sCnt[kCPro + L], lane);
+    if constexpr (NORM) {
+      norm_rows(a, c, 16 * L + 8);
+      arrive(&sCnt[kCNorm], lane);
+    }
     return;
   }
   // 2. blocks: kSDepth in flight; block b goes to tile b % kSRing once both uses of the tile's
@@ -269,10 +342,23 @@ __device__ __forceinline__ void split_loader(const SplitArgs& a, const SplitCtx&
     dma_block_share(kc, vc, c, L, b, ring + (b % kSRing) * kSTile);
   };
   const int d0 = nb < kSDepth ? nb : kSDepth;
-  for (int b = 0; b < d0; ++b) issue(b);
-  // the prologue, issued first, has landed once at most the d0 blocks' loads are outstanding
-  if (d0 == 3) vm_wait<12>(); else if (d0 == 2) vm_wait<8>(); else vm_wait<4>();
+  // blocks 0 and 1, then the prologue's hand-off (it was issued first: it has landed once at most
+  // their 8 loads are outstanding), this wave's share of the norm, then the next block: issuing
+  // loads takes the wave long enough that announcing the prologue after all of them would hold
+  // up the norm
+  issue(0);
+  if (d0 > 1) {
+    issue(1);
+    vm_wait<8>();
+  } else {
+    vm_wait<4>();
+  }
   arrive(&sCnt[kCPro + L], lane);
+  if constexpr (NORM) {
+    norm_rows(a, c, 16 * L + 8);
+    arrive(&sCnt[kCNorm], lane);
+  }
+  for (int b = 2; b < d0; ++b) issue(b);
   for (int b = 0; b < nb; ++b) {
     const int later = (b + kSDepth - 1 < nb ? b + kSDepth - 1 : nb - 1) - b;  // blocks issued after b
     if (later >= 2) vm_wait<8>(); else if (later == 1) vm_wait<4>(); else vm_wait<0>();
@@ -297,74 +383,13 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
   bool expired = false;
   lds_barrier();  // counters cleared
 
-  // 1. Norm + RoPE of query rows 16 W .. 16 W + 15 in place (the arithmetic of the stand-alone
-  //    norm/RoPE kernel, so the bits are the same); in the own range also the own k rows of the
-  //    same tokens (same RoPE rows, gamma k). Roped q arrives ready.
+  // 1. Norm + RoPE of query rows 16 W .. 16 W + 7 in place (rows 16 W + 8 .. + 15 are loader W's);
+  //    in the own range also the own k rows of the same tokens. Roped q arrives ready.
   await_cnt(kCPro + W, 1, a.spin_limit, expired);
-  if constexpr (NORM) {
-    // the four query rows in one branch-free pass (all LDS reads, then the arithmetic, then the
-    // stores, so that the rows' dependency chains interleave); the own k rows in a second pass
-    float g8[8];
-    unpack_pair(lds_ld<uint2>(AX_LDS(sGam) + 8 * j16), lds_ld<uint2>(AX_LDS(sGam) + 128 + 8 * j16), g8);
-    uint2 lo[4], hi[4];
-    float cc[4][4], ss[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * W + 4 * i + r4;  // query row = token
-      lo[i] = lds_ld<uint2>(AX_LDS(sQ) + r * 256 + pair_off_lo(j16, qswz(r)));
-      hi[i] = lds_ld<uint2>(AX_LDS(sQ) + r * 256 + pair_off_hi(j16, qswz(r)));
-      const f32x4 cs = lds_ld<f32x4>(AX_LDS(sRope) + (16 * W + 4 * i) * 256 + 16 * lane);
-      const f32x4 sn = lds_ld<f32x4>(AX_LDS(sRope) + kT * 256 + (16 * W + 4 * i) * 256 + 16 * lane);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        cc[i][e] = cs[e];
-        ss[i][e] = sn[e];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x[8], A[8], B[8];
-      unpack_pair(lo[i], hi[i], x);
-      rope_coef_pair(g8, cc[i], ss[i], A, B);
-      norm_rope_pair(x, A, B, a.eps);
-      pack_pair(x, lo[i], hi[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * W + 4 * i + r4;
-      lds_st(AX_LDS(sQ) + r * 256 + pair_off_lo(j16, qswz(r)), lo[i]);
-      lds_st(AX_LDS(sQ) + r * 256 + pair_off_hi(j16, qswz(r)), hi[i]);
-    }
-    if (c.own) {
-      float gk8[8];
-      unpack_pair(lds_ld<uint2>(AX_LDS(sGam) + 256 + 8 * j16), lds_ld<uint2>(AX_LDS(sGam) + 384 + 8 * j16), gk8);
-      uint2 klo[4], khi[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tr = (16 * W + 4 * i + r4) & (kBlk - 1);
-        const lds_u8* krow = ring + ((16 * W + 4 * i) >> 5) * kSTile + tr * 256;
-        klo[i] = lds_ld<uint2>(krow + pair_off_lo(j16, kswz2(tr)));
-        khi[i] = lds_ld<uint2>(krow + pair_off_hi(j16, kswz2(tr)));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float y[8], kA[8], kB[8];
-        rope_coef_pair(gk8, cc[i], ss[i], kA, kB);
-        unpack_pair(klo[i], khi[i], y);
-        norm_rope_pair(y, kA, kB, a.eps);
-        pack_pair(y, klo[i], khi[i]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tr = (16 * W + 4 * i + r4) & (kBlk - 1);
-        lds_u8* krow = ring + ((16 * W + 4 * i) >> 5) * kSTile + tr * 256;
-        lds_st(krow + pair_off_lo(j16, kswz2(tr)), klo[i]);
-        lds_st(krow + pair_off_hi(j16, kswz2(tr)), khi[i]);
-      }
-    }
-  }
+  if constexpr (NORM) norm_rows(a, c, 16 * W);
   arrive(&sCnt[kCNorm], lane);
-  await_cnt(kCNorm, kSC, a.spin_limit, expired);  // all 64 query rows (and in the own range the own k rows) ready
+  // all 64 query rows (and in the own range the own k rows) ready: eight waves norm them
+  await_cnt(kCNorm, NORM ? kSC + kSL : kSC, a.spin_limit, expired);
 
   // 2. The query rows of row tile T as MFMA B operands (k-step kk).
   const int n = lane & 31;
