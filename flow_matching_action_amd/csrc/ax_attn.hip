@@ -14,25 +14,26 @@
 // softmax), and m_c any reference at or near the split's maximum.
 //
 // gfx950 mapping (k_attn_split)
-// - One workgroup of 8 waves per (kv head g, key range, q head 2g + hp): 64 query rows. Workgroup
+// - One workgroup of 12 waves per (kv head g, key range, q head 2g + hp): 64 query rows. Workgroup
 //   id w has head w % 8, which the dispatcher places on XCD w % 8, and the two q heads of a key
 //   range are consecutive ids, so the second read of the range's K/V comes from that XCD's L2.
 //   The cache keys [0, S) are cut into at most 15 ranges of whole 32-key blocks (at most 10
 //   blocks each); the 64 own tokens form one more range of 2 blocks.
-// - Waves 0..3 (loaders, one per SIMD) only issue direct-to-LDS loads (global_load_lds, 16 bytes
-//   per lane): first the query prologue (16 query rows, their RoPE rows and the gammas for the
-//   compute wave on the same SIMD), then the blocks a few ahead into a ring of 6 tiles, and count
-//   each landed block in LDS. A wave whose loads wait for room in the CU's memory pipeline stalls
-//   at issue, so the loads are kept away from the arithmetic.
-// - Waves 4..7 (compute) norm and rope 16 query rows each in LDS (16 lanes per row), then wave
-//   4 + w takes row tile t = w & 1 (rows 32 t .. 32 t + 31) over the blocks of parity p = w >> 1. Per
-//   block S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows, B = Q^T), so each lane holds one
-//   query row's scores, and O^T += V^T P^T with V^T read by ds_read_b64_tr_b16 and P^T taken from
-//   the S^T accumulator (inside a block MFMA row m reads key pi(m), bits 2 and 3 swapped, which
-//   makes the 8 keys a lane supplies to one PV step consecutive). The blocks are software-
-//   pipelined: the scores of block b run on the matrix cores while the exponentials of the
-//   previous block run on the vector ALU, and the PV of the previous block beside the row max
-//   of block b.
+// - Waves 0..3 (loaders, one per SIMD) issue direct-to-LDS loads (global_load_lds, 16 bytes per
+//   lane): first the query prologue (16 query rows, their RoPE rows and the gammas for the row
+//   tile on the same SIMD), then the blocks a few ahead into a ring of 6 tiles, and count each
+//   landed block in LDS. A wave whose loads wait for room in the CU's memory pipeline stalls at
+//   issue, so the loads are kept away from the arithmetic.
+// - Waves 4..11 (compute): wave 4 + w takes row tile t = w & 3 (rows 16 t .. 16 t + 15) over the
+//   blocks of parity p = w >> 2, so each SIMD runs one loader and the two compute
+//   waves of one row tile: a single wave issues vector instructions at only a fraction of a SIMD's
+//   rate, and the per-block exponentials are the larger part of the work. Per block S^T = K Q^T on
+//   v_mfma_f32_16x16x32_bf16 (A = K rows, B = Q^T) and O^T += V^T P^T with V^T read by
+//   ds_read_b64_tr_b16 and P^T taken straight from the S^T accumulators. The blocks are
+//   software-pipelined: the scores of block b run on the matrix cores while the exponentials of
+//   the previous block run on the vector ALU, and the PV of the previous block beside the row
+//   max of block b.
+// - The three waves of a SIMD norm and rope their row tile's 16 query rows in LDS first.
 // - The two parity waves of a row tile merge (m, l, O) through LDS, each finalising half of the
 //   columns, and store the range's partial: O in float16 with a power-of-two exponent per (row,
 //   32-column quarter), m and l in float32.
@@ -43,7 +44,7 @@
 
 namespace ax {
 
-constexpr int kSC = 4;                          // compute waves
+constexpr int kSC = 8;                          // compute waves: 4 row tiles x 2 block parities
 constexpr int kSL = 4;                          // loader waves
 constexpr int kSThreads = 64 * (kSC + kSL);
 constexpr int kSTile = 2 * kBlk * kD * 2;       // 16 KB: the K rows, then the V rows of a 32-key block
@@ -54,10 +55,10 @@ constexpr int kSDepth = 3;                      // blocks in flight per loader w
 constexpr int kSCacheRanges = 15;               // cache key ranges per kv head, at most
 constexpr float kSRescale = 16.0f;              // lazy-rescale threshold (log2 units)
 constexpr float kScoreScale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
-// LDS hand-off counters: prologue of compute wave w landed, query rows normed, query fragments
-// read, block b landed, uses of tile r finished, merge data of row tile t written
+// LDS hand-off counters: prologue of row tile t landed, query rows normed, query fragments read,
+// block b landed, uses of tile r finished, merge data of row tile t written
 constexpr int kCPro = 0, kCNorm = 4, kCFrag = 5, kCLand = 6, kCDone = kCLand + kSMaxNB, kCMrg = kCDone + kSRing,
-              kCN = kCMrg + 2;
+              kCN = kCMrg + 4;
 
 struct SplitArgs {
   const uint16_t* q;       // [16][64][128]: raw q (NORM) or already roped q
@@ -159,14 +160,13 @@ __device__ __forceinline__ void await_cnt(int i, int n, int limit, bool& expired
 // Chunk swizzles of the ring's 256-byte K and V rows (16 chunks of 16 bytes). LDS serves a
 // ds_read_b128 for 16 lanes per cycle and a ds_read_b64_tr_b16 for 32, all 64 banks at once, so
 // those lanes must hit 16 distinct chunks; the swizzles also keep 8-lane (b128) and 16-lane (tr)
-// halves on 8 distinct chunks of the same 128-byte half as those of the other half.
-// K: lanes 0..15 read rows perm_key(0..15) = {0..3, 8..11, 4..7, 12..15} at one chunk c: rows
-// 0..3 and 8..11 go to c ^ 0..7, rows 4..7 and 12..15 to c ^ 8..15.
-__device__ __forceinline__ int kswz2(int r) { return (r & 3) | ((r >> 1) & 4) | ((r << 1) & 8); }
-// V: the 32 lanes of two 16-lane transpose groups read rows 4t .. 4t + 3 at chunks {c, c + 1} and
-// {c + 2, c + 3} (c even): 2 (r & 3) spreads a group over 8 chunks, 8 (r & 1) moves odd rows to the
-// other half of the row's chunks, so the two groups together take all 16.
-__device__ __forceinline__ int vswz2(int r) { return (2 * (r & 3)) ^ (8 * (r & 1)); }
+// halves on 8 distinct chunks of one 128-byte half, the other half taking the other 8.
+// K: lanes 0..15 read rows 0..15 (or 16..31) at one chunk c: row r's chunk c sits at c ^ (r & 15).
+__device__ __forceinline__ int kswz16(int r) { return r & 15; }
+// V: the 32 lanes of two 16-lane transpose groups read rows 0..7 (mod 16) at chunks 2 dt and
+// 2 dt + 1: 2 (r & 7) moves the pair to 2 (dt ^ (r & 7)), a distinct pair per row, with rows 0..3
+// in one half and rows 4..7 in the other.
+__device__ __forceinline__ int vswz16(int r) { return 2 * (r & 7); }
 
 // Per-workgroup facts every wave shares.
 struct SplitCtx {
@@ -186,47 +186,47 @@ __device__ __forceinline__ void dma_block_share(const uint16_t* kc, const uint16
     const int r = r0 + (c.lane >> 4);
     int v = c.k_begin + kBlk * b + r;
     v = v < c.k_end ? v : c.k_begin;
-    dma_x4(kc + (long long)v * kD + 8 * ((c.lane & 15) ^ kswz2(r)), tile + r0 * 256);
-    dma_x4(vc + (long long)v * kD + 8 * ((c.lane & 15) ^ vswz2(r)), tile + kSV + r0 * 256);
+    dma_x4(kc + (long long)v * kD + 8 * ((c.lane & 15) ^ kswz16(r)), tile + r0 * 256);
+    dma_x4(vc + (long long)v * kD + 8 * ((c.lane & 15) ^ vswz16(r)), tile + kSV + r0 * 256);
   }
 }
 
-// Row max of a 32x32 score tile over both lane halves (the row's 32 keys). The IEEE maximum
-// (v_maximum3_f32 on gfx950) needs no quieting of its inputs, unlike fmaxf on MFMA results.
 __device__ __forceinline__ float fmax_(float a, float b) { return __builtin_elementwise_maximum(a, b); }
-__device__ __forceinline__ float tile_rowmax(const f32x16& s) {
-  const float a = fmax_(fmax_(s[0], s[1]), s[2]);
-  const float b = fmax_(fmax_(s[3], s[4]), s[5]);
-  const float c = fmax_(fmax_(s[6], s[7]), s[8]);
-  const float d = fmax_(fmax_(s[9], s[10]), s[11]);
-  const float e = fmax_(fmax_(s[12], s[13]), s[14]);
-  const float m = fmax_(fmax_(fmax_(a, b), c), fmax_(fmax_(d, e), s[15]));
-  const float2 pr = pair32(m);
-  return fmax_(pr.x, pr.y);
+// A lane's value and that of lane ^ 16, in either order (v_permlane16_swap, as pair32 for 32).
+__device__ __forceinline__ float2 pair16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return float2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+// The lane's largest score of a block (its 8 keys), and the max over the four lanes l & 15 + 16 i
+// that hold one query row. The IEEE maximum (v_maximum3_f32 on gfx950) needs no quieting of its
+// inputs, unlike fmaxf on MFMA results.
+__device__ __forceinline__ float lane_max8(const f32x4* s) {
+  return fmax_(fmax_(fmax_(s[0][0], s[0][1]), fmax_(s[0][2], s[0][3])),
+               fmax_(fmax_(s[1][0], s[1][1]), fmax_(s[1][2], s[1][3])));
+}
+__device__ __forceinline__ float row_max4(float x) {
+  float2 p = pair16(x);
+  x = fmax_(p.x, p.y);
+  p = pair32(x);
+  return fmax_(p.x, p.y);
 }
 
-__device__ __forceinline__ f32x16 splat16(float x) {
-  f32x16 r;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) r[i] = x;
-  return r;
-}
-
-// Norm + RoPE in place of query rows row0 .. row0 + 7 (two passes of 4 rows, 16 lanes per row:
-// the arithmetic of the stand-alone norm/RoPE kernel, so the bits are the same) and, in the own
-// range, of the own k rows of the same tokens (same RoPE rows, gamma k). The 64 rows are split
-// between the compute and the loader waves, two waves per SIMD, since a single wave issues vector
-// instructions at only half of a SIMD's rate. Within a pass every LDS read comes first, then the
-// arithmetic, then the stores, so that the rows' dependency chains interleave.
+// Norm + RoPE in place of query rows row0 .. row0 + 4 NP - 1 (NP passes of 4 rows, 16 lanes per
+// row: the arithmetic of the stand-alone norm/RoPE kernel, so the bits are the same) and, in the
+// own range, of the own k rows of the same tokens (same RoPE rows, gamma k). The 16 rows of a row
+// tile are split between the three waves of its SIMD (4 + 4 + 8), since a single wave issues
+// vector instructions at only half of a SIMD's rate. Within a pass every LDS read comes first,
+// then the arithmetic, then the stores, so that the rows' dependency chains interleave.
+template <int NP>
 __device__ __forceinline__ void norm_rows(const SplitArgs& a, const SplitCtx& c, const int row0) {
   const int lane = c.lane, j16 = lane & 15, r4 = lane >> 4;
   lds_u8* ring = AX_LDS(sRing);
   float g8[8];
   unpack_pair(lds_ld<uint2>(AX_LDS(sGam) + 8 * j16), lds_ld<uint2>(AX_LDS(sGam) + 128 + 8 * j16), g8);
-  uint2 lo[2], hi[2];
-  float cc[2][4], ss[2][4];
+  uint2 lo[NP], hi[NP];
+  float cc[NP][4], ss[NP][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < NP; ++i) {
     const int r = row0 + 4 * i + r4;  // query row = token
     lo[i] = lds_ld<uint2>(AX_LDS(sQ) + r * 256 + pair_off_lo(j16, qswz(r)));
     hi[i] = lds_ld<uint2>(AX_LDS(sQ) + r * 256 + pair_off_hi(j16, qswz(r)));
@@ -239,7 +239,7 @@ __device__ __forceinline__ void norm_rows(const SplitArgs& a, const SplitCtx& c,
     }
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < NP; ++i) {
     float x[8], A[8], B[8];
     unpack_pair(lo[i], hi[i], x);
     rope_coef_pair(g8, cc[i], ss[i], A, B);
@@ -247,7 +247,7 @@ __device__ __forceinline__ void norm_rows(const SplitArgs& a, const SplitCtx& c,
     pack_pair(x, lo[i], hi[i]);
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < NP; ++i) {
     const int r = row0 + 4 * i + r4;
     lds_st(AX_LDS(sQ) + r * 256 + pair_off_lo(j16, qswz(r)), lo[i]);
     lds_st(AX_LDS(sQ) + r * 256 + pair_off_hi(j16, qswz(r)), hi[i]);
@@ -255,16 +255,16 @@ __device__ __forceinline__ void norm_rows(const SplitArgs& a, const SplitCtx& c,
   if (c.own) {
     float gk8[8];
     unpack_pair(lds_ld<uint2>(AX_LDS(sGam) + 256 + 8 * j16), lds_ld<uint2>(AX_LDS(sGam) + 384 + 8 * j16), gk8);
-    uint2 klo[2], khi[2];
+    uint2 klo[NP], khi[NP];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NP; ++i) {
       const int tr = (row0 + 4 * i + r4) & (kBlk - 1);
       const lds_u8* krow = ring + ((row0 + 4 * i) >> 5) * kSTile + tr * 256;
-      klo[i] = lds_ld<uint2>(krow + pair_off_lo(j16, kswz2(tr)));
-      khi[i] = lds_ld<uint2>(krow + pair_off_hi(j16, kswz2(tr)));
+      klo[i] = lds_ld<uint2>(krow + pair_off_lo(j16, kswz16(tr)));
+      khi[i] = lds_ld<uint2>(krow + pair_off_hi(j16, kswz16(tr)));
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NP; ++i) {
       float y[8], kA[8], kB[8];
       rope_coef_pair(gk8, cc[i], ss[i], kA, kB);
       unpack_pair(klo[i], khi[i], y);
@@ -272,11 +272,11 @@ __device__ __forceinline__ void norm_rows(const SplitArgs& a, const SplitCtx& c,
       pack_pair(y, klo[i], khi[i]);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < NP; ++i) {
       const int tr = (row0 + 4 * i + r4) & (kBlk - 1);
       lds_u8* krow = ring + ((row0 + 4 * i) >> 5) * kSTile + tr * 256;
-      lds_st(krow + pair_off_lo(j16, kswz2(tr)), klo[i]);
-      lds_st(krow + pair_off_hi(j16, kswz2(tr)), khi[i]);
+      lds_st(krow + pair_off_lo(j16, kswz16(tr)), klo[i]);
+      lds_st(krow + pair_off_hi(j16, kswz16(tr)), khi[i]);
     }
   }
 }
@@ -289,8 +289,9 @@ __device__ __forceinline__ void split_loader(const SplitArgs& a, const SplitCtx&
   const uint16_t* kc = a.Kc + head_off;
   const uint16_t* vc = a.Vc + head_off;
   lds_u8* ring = AX_LDS(sRing);
-  // 1. the prologue of compute wave L: query rows 16 L + 4 i + r4 (lane l lands at 16 l of each
-  //    1 KB, so it fetches the chunk the row's swizzle puts there), their RoPE rows, the gammas;
+  // 1. the prologue of row tile L (the two compute waves on this SIMD): query rows 16 L + 4 i + r4
+  //    (lane l lands at 16 l of each 1 KB, so it fetches the chunk the row's swizzle puts there),
+  //    their RoPE rows, the gammas;
   //    in the own range also own k/v rows 16 L .. 16 L + 15 (blocks 0, 1 in tiles 0, 1)
   const uint16_t* qh = a.q + (long long)(2 * c.g + c.hp) * kT * kD;
 #pragma unroll
@@ -305,8 +306,8 @@ __device__ __forceinline__ void split_loader(const SplitArgs& a, const SplitCtx&
       dma_x4(a.cos_t + tok * 64 + 4 * j16, AX_LDS(sRope) + (16 * L + 4 * i) * 256);
       dma_x4(a.sin_t + tok * 64 + 4 * j16, AX_LDS(sRope) + kT * 256 + (16 * L + 4 * i) * 256);
     }
-    // every loader brings both gamma vectors (the same bytes), so that compute wave L needs no
-    // other loader's count
+    // every loader brings both gamma vectors (the same bytes), so that row tile L's compute
+    // waves need no other loader's count
     dma_x1(a.gq + 2 * lane, AX_LDS(sGam));
     dma_x1(a.gk + 2 * lane, AX_LDS(sGam) + 256);
   }
@@ -319,8 +320,8 @@ __device__ __forceinline__ void split_loader(const SplitArgs& a, const SplitCtx&
       const int tr0 = 16 * (L & 1) + 4 * i;
       const int tr = tr0 + r4;
       const int tok = 16 * L + 4 * i + r4;
-      dma_x4(kt + (long long)tok * kD + 8 * (j16 ^ kswz2(tr)), ot + tr0 * 256);
-      dma_x4(vt + (long long)tok * kD + 8 * (j16 ^ vswz2(tr)), ot + kSV + tr0 * 256);
+      dma_x4(kt + (long long)tok * kD + 8 * (j16 ^ kswz16(tr)), ot + tr0 * 256);
+      dma_x4(vt + (long long)tok * kD + 8 * (j16 ^ vswz16(tr)), ot + kSV + tr0 * 256);
     }
   }
   lds_barrier();  // counters cleared (the workgroup's only barrier)
@@ -329,16 +330,16 @@ __device__ __forceinline__ void split_loader(const SplitArgs& a, const SplitCtx&
     vm_wait<0>();
     arrive(&sCnt[kCPro + L], lane);
     if constexpr (NORM) {
-      norm_rows(a, c, 16 * L + 8);
+      norm_rows<2>(a, c, 16 * L + 8);
       arrive(&sCnt[kCNorm], lane);
     }
     return;
   }
-  // 2. blocks: kSDepth in flight; block b goes to tile b % kSRing once both uses of the tile's
-  //    previous block are finished. Each block is 4 loads of this wave.
+  // 2. blocks: kSDepth in flight; block b goes to tile b % kSRing once all four uses of the
+  //    tile's previous block (one per row tile) are finished. Each block is 4 loads of this wave.
   const int nb = c.nb;
   auto issue = [&](int b) {
-    if (b >= kSRing) await_cnt(kCDone + b % kSRing, 2 * (b / kSRing), a.spin_limit, expired);
+    if (b >= kSRing) await_cnt(kCDone + b % kSRing, (kSC / 2) * (b / kSRing), a.spin_limit, expired);
     dma_block_share(kc, vc, c, L, b, ring + (b % kSRing) * kSTile);
   };
   const int d0 = nb < kSDepth ? nb : kSDepth;
@@ -355,7 +356,7 @@ __device__ __forceinline__ void split_loader(const SplitArgs& a, const SplitCtx&
   }
   arrive(&sCnt[kCPro + L], lane);
   if constexpr (NORM) {
-    norm_rows(a, c, 16 * L + 8);
+    norm_rows<2>(a, c, 16 * L + 8);
     arrive(&sCnt[kCNorm], lane);
   }
   for (int b = 2; b < d0; ++b) issue(b);
@@ -369,120 +370,129 @@ __device__ __forceinline__ void split_loader(const SplitArgs& a, const SplitCtx&
 }
 
 // ---------------------------------------------------------------------------------- compute
-// Compute wave W (0..3) takes row tile T = W & 1 over the blocks of parity P = W >> 1. T, P and
-// the block count are run-time values and the block loop is rolled, so that the four compute waves
-// run one short copy of the code: unrolled per (T, P, block count) the copies outgrow the
-// instruction cache.
+// Compute wave W (0..7) takes row tile T = W & 3 (query rows 16 T .. 16 T + 15) over the blocks of
+// parity P = W >> 2; both waves of row tile T share SIMD T with loader T. T, P and the block
+// count are run-time values and the block loop is rolled, so that the eight compute waves run
+// one short copy of the code.
+//
+// MFMA layouts (v_mfma_f32_16x16x32_bf16, D = A B + C with A 16 x 32, B 32 x 16): lane l holds
+// A[l & 15][8 (l >> 4) + 0..7], B[8 (l >> 4) + 0..7][l & 15] and D[4 (l >> 4) + i][l & 15].
+// - Scores S^T = K Q^T per 16-key half t of a block: A = K rows 16 t .. 16 t + 15, B = Q^T, so
+//   lane l holds query row l & 15 against keys 16 t + 4 (l >> 4) + i.
+// - O^T += V^T P^T per 16-column tile dt of the head dim: B = P^T straight from the two score
+//   accumulators (lane slots 0..3 = keys 4 (l >> 4) + i, slots 4..7 = keys 16 + 4 (l >> 4) + i),
+//   A = V^T read in the same key order by two ds_read_b64_tr_b16; lane l then holds
+//   O[query row l & 15][16 dt + 4 (l >> 4) + i].
 template <bool NORM>
 __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx& c, const int W) {
-  const int T = W & 1, P = W >> 1;
+  const int T = W & 3, P = W >> 2;
   const int NB = c.nb > P ? (c.nb - P + 1) / 2 : 0;  // blocks P, P + 2, ... below nb
-  const int lane = c.lane, j16 = lane & 15, r4 = lane >> 4;
+  const int lane = c.lane, j16 = lane & 15, g4 = lane >> 4;
   const long long head_off = (long long)c.g * a.Smax * kD;
   lds_u8* ring = AX_LDS(sRing);
   bool expired = false;
   lds_barrier();  // counters cleared
 
-  // 1. Norm + RoPE of query rows 16 W .. 16 W + 7 in place (rows 16 W + 8 .. + 15 are loader W's);
-  //    in the own range also the own k rows of the same tokens. Roped q arrives ready.
-  await_cnt(kCPro + W, 1, a.spin_limit, expired);
-  if constexpr (NORM) norm_rows(a, c, 16 * W);
+  // 1. Norm + RoPE of query rows 16 T + 4 P .. + 3 in place (rows 16 T + 8 .. + 15 are loader T's,
+  //    the other four the partner wave's); in the own range also the own k rows of the same
+  //    tokens. Roped q arrives ready.
+  await_cnt(kCPro + T, 1, a.spin_limit, expired);
+  if constexpr (NORM) norm_rows<1>(a, c, 16 * T + 4 * P);
   arrive(&sCnt[kCNorm], lane);
-  // all 64 query rows (and in the own range the own k rows) ready: eight waves norm them
+  // all 64 query rows (and in the own range the own k rows) ready: twelve waves norm them
   await_cnt(kCNorm, NORM ? kSC + kSL : kSC, a.spin_limit, expired);
 
-  // 2. The query rows of row tile T as MFMA B operands (k-step kk).
-  const int n = lane & 31;
-  const int h = lane >> 5;
-  bf16x8 qf[8];
+  // 2. The query rows of row tile T as MFMA B operands (k-step kk: columns 32 kk .. 32 kk + 31).
+  bf16x8 qf[4];
   {
-    const int r = 32 * T + n;
+    const int r = 16 * T + j16;
     const lds_u8* qrow = AX_LDS(sQ) + r * 256;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qf[kk] = lds_ld<bf16x8>(qrow + 16 * ((dcol(kk, h) >> 3) ^ qswz(r)));
+    for (int kk = 0; kk < 4; ++kk) qf[kk] = lds_ld<bf16x8>(qrow + 16 * ((4 * kk + g4) ^ qswz(r)));
   }
-  arrive(&sCnt[kCFrag], lane);  // (the exchange of step 4 reuses the RoPE rows once all four have read)
+  arrive(&sCnt[kCFrag], lane);  // (the exchange of step 5 reuses the RoPE rows once all eight have read)
 
   // 3. The blocks P, P + 2, ..., software-pipelined one block deep.
-  const int krow = perm_key(n);
+  // K: key row 16 t + j16, chunk 4 kk + g4; the second half of the keys is 4 KB further on.
   int koff[4];
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) koff[jj] = krow * 256 + 16 * ((4 * h + jj) ^ kswz2(krow));
-  const int G = lane >> 4, li = lane & 15;
-  const int vrow0 = 8 * (G >> 1) + (li >> 2);
-  const int vx = 2 * (G & 1) + ((li & 3) >> 1);
-  const int voff[2] = {vrow0 * 256 + 16 * (vx ^ vswz2(vrow0)) + 8 * (li & 1),
-                       vrow0 * 256 + 16 * ((4 + vx) ^ vswz2(vrow0)) + 8 * (li & 1)};
-  f32x16 o[4];
+  for (int kk = 0; kk < 4; ++kk) koff[kk] = j16 * 256 + 16 * ((4 * kk + g4) ^ kswz16(j16));
+  // V: lane j16 of 16-lane group g4 supplies key row 4 g4 + (j16 >> 2) (+ 16 for the second read),
+  // columns 16 dt + 4 (j16 & 3) .. + 3: half j16 & 1 of chunk 2 dt + ((j16 & 3) >> 1)
+  const int vr = 4 * g4 + (j16 >> 2);
+  int voff[8];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) o[dt] = splat16(0.f);
-  float m = -INFINITY;  // exponent reference of the lane's row (log2 units)
+  for (int dt = 0; dt < 8; ++dt)
+    voff[dt] = kSV + vr * 256 + 16 * ((2 * dt + ((j16 & 3) >> 1)) ^ vswz16(vr)) + 8 * (j16 & 1);
+  f32x4 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY;  // exponent reference of the lane's row (log2 units), the same in its 4 lanes
   float l = 0.f;        // this lane's share of the row sum
-  f32x16 s;             // raw scores q . k of the block being exponentiated
-  bf16x8 kf[8];
-  v4i16 vt[2][4][2];
-  bf16x8 pb[2];
+  f32x4 s[2];           // raw scores q . k of the block being exponentiated
+  bf16x8 kf[2][4];
+  v4i16 vt[8][2];
+  bf16x8 pb;
   const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
   auto tile_of = [&](int b) { return ring + (b % kSRing) * kSTile; };  // (b uniform: scalar ops)
-  // (the chunks of columns 64 .. 127 are those of columns 0 .. 63 with bit 3 flipped: the
-  // tiles are 16 KB aligned, so the XOR acts on the offset alone)
   auto read_k = [&](const lds_u8* base) {
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) kf[kk] = lds_ld<bf16x8>(base + (koff[kk & 3] ^ (128 * (kk >> 2))));
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) kf[t][kk] = lds_ld<bf16x8>(base + koff[kk] + 4096 * t);
   };
   auto read_v = [&](const lds_u8* base) {
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
+    for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-          vt[kh][dt][hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16*)(base + kSV + (16 * kh + 4 * hf) * 256 + (voff[dt & 1] ^ (128 * (dt >> 1)))));
+      for (int hf = 0; hf < 2; ++hf)
+        vt[dt][hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + voff[dt] + 4096 * hf));
   };
-  auto qk = [&](f32x16& sd) {
-    sd = splat16(0.f);
+  auto qk = [&](f32x4* sd) {
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) sd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], sd, 0, 0, 0);
+    for (int t = 0; t < 2; ++t) {
+      sd[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) sd[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][kk], qf[kk], sd[t], 0, 0, 0);
+    }
   };
   // p = 2^(s log2(e) / sqrt(128) - m) (v_exp_f32 directly: the arguments are at most kSRescale, or
   // -inf), their bf16 pairs (the PV operand) and the row sum of the same rounded values, so every
   // output row is an exact convex combination of V rows
   auto softmax = [&]() {
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    float ps[2] = {0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i], kScoreScale, -m));
-      const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * i + 1], kScoreScale, -m));
-      const bf16x2_t pr = {(__bf16)e0, (__bf16)e1};
-      pb[i >> 2][2 * (i & 3)] = pr[0];
-      pb[i >> 2][2 * (i & 3) + 1] = pr[1];
-      ps[i & 3] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ps[i & 3], false);
-    }
-    l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][2 * i], kScoreScale, -m));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][2 * i + 1], kScoreScale, -m));
+        const bf16x2_t pr = {(__bf16)e0, (__bf16)e1};
+        pb[4 * t + 2 * i] = pr[0];
+        pb[4 * t + 2 * i + 1] = pr[1];
+        ps[i] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ps[i], false);
+      }
+    l += ps[0] + ps[1];
   };
   auto pv = [&]() {
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const v4i16 both[2] = {vt[kh][dt][0], vt[kh][dt][1]};
-        bf16x8 vf;
-        __builtin_memcpy(&vf, both, 16);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kh], o[dt], 0, 0, 0);
-      }
-  };
-  // Keys of the range's last block past k_end get p = 0. Accumulator element i of lane half h is
-  // key perm_key(8 (i >> 2) + 4 h + (i & 3)) = 8 h + kofs(i).
-  auto mask_tail = [&](f32x16& sd, int b) {
-    const int lim = c.k_end - (c.k_begin + kBlk * b) - 8 * h;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kofs = 16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3);
-      sd[i] = (kofs < lim) ? sd[i] : -INFINITY;
+    for (int dt = 0; dt < 8; ++dt) {
+      const v4i16 both[2] = {vt[dt][0], vt[dt][1]};
+      bf16x8 vf;
+      __builtin_memcpy(&vf, both, 16);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb, o[dt], 0, 0, 0);
     }
   };
-  // Release of block b's tile (both row tiles count here) right after its V reads are issued,
+  // Keys of the range's last block past k_end get p = 0 (after the row max: such rows reload the
+  // range's first key, a visible one).
+  auto mask_tail = [&](f32x4* sd, int b) {
+    const int lim = c.k_end - (c.k_begin + kBlk * b) - 4 * g4;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sd[t][i] = (16 * t + i < lim) ? sd[t][i] : -INFINITY;
+  };
+  // Release of block b's tile (all four row tiles count here) right after its V reads are issued,
   // without waiting for them: a wave's LDS operations execute in order, so the increment cannot
   // pass the reads, and a loader that sees it only then starts loads that land far later.
   auto release = [&](int b) {
@@ -502,12 +512,14 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
   // K of block b + 2 is read at the end of iteration b, and its landed count is read early in
   // the iteration (before the V reads), so that neither the poll nor the K reads wait behind
   // this block's V reads; only a block not yet landed takes the blocking poll.
+  // (The blocks go to the two waves by parity, not first come first served, so that every
+  // partial sum, and with it the result, is the same from run to run.)
   if (NB > 0) {
     landed(P);
     read_k(tile_of(P));
     qk(s);
     read_v(tile_of(P));
-    m = tile_rowmax(s) * kScoreScale;  // finite: the block holds a visible key
+    m = row_max4(lane_max8(s)) * kScoreScale;  // finite: the block holds a visible key
     if (c.partial && P == c.nb - 1) mask_tail(s, P);
     release(P);
     if (NB > 1) {
@@ -523,27 +535,29 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
                             ? __hip_atomic_load(&sCnt[kCLand + b + 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
                             : kSL;
       // (A) scores of block b beside the exponentials of block b - 2
-      f32x16 sn;
+      f32x4 sn[2];
       qk(sn);
       softmax();
-      // (B) PV of block b - 2 beside the row max of block b
+      // (B) PV of block b - 2 beside the lane's share of the row max of block b
       pv();
-      const float bm = tile_rowmax(sn) * kScoreScale;
+      const float bm = lane_max8(sn) * kScoreScale;
       read_v(tile_of(b));
       // the reference moves only when the row's block max exceeds it by more than kSRescale:
-      // p stays below 2^kSRescale and the O rescale is rare
+      // p stays below 2^kSRescale and the O rescale is rare; a lane's share of the row max
+      // decides whether any row needs it, and only then are the row's four lanes combined
       if (__builtin_amdgcn_ballot_w64(bm > m + kSRescale) != 0) {
-        const float mn = fmax_(m, bm);
+        const float mn = fmax_(m, row_max4(bm));
         const float alpha = __builtin_amdgcn_exp2f(m - mn);
         m = mn;
         l *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+        for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+          for (int i = 0; i < 4; ++i) o[dt][i] *= alpha;
       }
       if (c.partial && b == c.nb - 1) mask_tail(sn, b);
-      s = sn;
+      s[0] = sn[0];
+      s[1] = sn[1];
       release(b);
       if (more) {
         if (__builtin_amdgcn_readfirstlane(early) < kSL) landed(b + 2);
@@ -554,42 +568,41 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
     pv();
   }
 
-  // 4. Own range, q head parity 0: the roped own k rows and the own v rows of tokens 16 W .. +15
-  //    to the cache tail (after the loaders' last use of those tiles; the reads are done).
+  // 4. Own range, q head parity 0: the roped own k rows and the own v rows of tokens 16 T + 8 P ..
+  //    + 7 to the cache tail (the loaders load nothing into the own range's tiles).
   if (c.own && a.own_tail && c.hp == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = 16 * W + 4 * i + r4;
+    for (int i = 0; i < 2; ++i) {
+      const int tok = 16 * T + 8 * P + 4 * i + g4;
       const int tr = tok & (kBlk - 1);
       const lds_u8* ot = ring + (tok >> 5) * kSTile;
       const long long dst = head_off + (long long)(a.Smax - kT + tok) * kD + 8 * j16;
-      *reinterpret_cast<u32x4*>(a.Kc + dst) = lds_ld<u32x4>(ot + tr * 256 + 16 * (j16 ^ kswz2(tr)));
-      *reinterpret_cast<u32x4*>(a.Vc + dst) = lds_ld<u32x4>(ot + kSV + tr * 256 + 16 * (j16 ^ vswz2(tr)));
+      *reinterpret_cast<u32x4*>(a.Kc + dst) = lds_ld<u32x4>(ot + tr * 256 + 16 * (j16 ^ kswz16(tr)));
+      *reinterpret_cast<u32x4*>(a.Vc + dst) = lds_ld<u32x4>(ot + kSV + tr * 256 + 16 * (j16 ^ vswz16(tr)));
     }
   }
 
   // 5. Merge of the two parity waves of row tile T through the RoPE rows' LDS (free once every
-  //    compute wave has read its query fragments): wave (T, P) keeps d-tiles 2P, 2P + 1 and hands
-  //    over the other two (4 KB each; piece q holds floats 4q .. 4q + 3 of each lane) with its m
-  //    and row total l.
-  const float2 lp = pair32(l);
-  const float lt = lp.x + lp.y;
+  //    compute wave has read its query fragments): wave (T, P) keeps column tiles 4 P .. 4 P + 3
+  //    and hands over the other four (1 KB each) with its m and row total l.
+  float lt = l;  // the row's total: its four lanes' shares
+  {
+    float2 pr = pair16(lt);
+    lt = pr.x + pr.y;
+    pr = pair32(lt);
+    lt = pr.x + pr.y;
+  }
   await_cnt(kCFrag, kSC, a.spin_limit, expired);
-  lds_u8* xw = AX_LDS(sRope) + (2 * T + P) * 8192;  // written by this wave
-  lds_u8* xr = AX_LDS(sRope) + (2 * T + (1 - P)) * 8192;  // written by the partner
-  lds_u8* mw = AX_LDS(sQ) + (2 * T + P) * 512;        // this wave's m, then row total l, per lane
-  lds_u8* mr = AX_LDS(sQ) + (2 * T + (1 - P)) * 512;  // the partner's
+  lds_u8* xw = AX_LDS(sRope) + (2 * T + P) * 4096;        // written by this wave
+  lds_u8* xr = AX_LDS(sRope) + (2 * T + (1 - P)) * 4096;  // written by the partner
+  lds_u8* mw = AX_LDS(sQ) + (2 * T + P) * 512;            // this wave's m, then row total l, per lane
+  lds_u8* mr = AX_LDS(sQ) + (2 * T + (1 - P)) * 512;      // the partner's
   // o[] is indexed with constants only (a run-time index would move the accumulators through
   // memory): the two parities take two copies of the hand-over and the store
   auto hand_over = [&](auto pc) {
     constexpr int PP = decltype(pc)::value;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int dt = 2 * (1 - PP) + j;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      lds_st(xw + j * 4096 + q * 1024 + 16 * lane, f32x4{o[dt][4 * q], o[dt][4 * q + 1], o[dt][4 * q + 2], o[dt][4 * q + 3]});
-  }
+    for (int j = 0; j < 4; ++j) lds_st(xw + j * 1024 + 16 * lane, o[4 * (1 - PP) + j]);
   };
   if (P == 0) hand_over(std::integral_constant<int, 0>{}); else hand_over(std::integral_constant<int, 1>{});
   lds_st(mw + 4 * lane, m);
@@ -604,45 +617,49 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
   const float L = aw * lt + ao * lo_;  // stored by parity 0
   const bool bad = __builtin_amdgcn_ballot_w64(expired) != 0;
   const long long part = (long long)c.g * a.n_split + c.split;
-  const int row = 64 * c.hp + 32 * T + n;  // folded row of head g
+  const int row = 64 * c.hp + 16 * T + j16;  // folded row of head g
+  // Quarter qd = 2 PP + qq of the row (columns 32 qd .. 32 qd + 31) is column tiles 2 qd and
+  // 2 qd + 1; in float16 with a power-of-two exponent per (row, quarter): the largest |value|
+  // maps into [0.5, 1) and ldexp scales each element exactly, with no intermediate overflow.
+  // Group (part, hp, T, qd) holds the quarter's 16 rows row-major (64 bytes a row), so that the
+  // combine reads a row's quarter as one contiguous run; the two stores of a quarter fill its 1 KB.
   auto store = [&](auto pc) {
     constexpr int PP = decltype(pc)::value;
-    int exj[2];
+    int exq[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int dt = 2 * PP + j;
-    f32x16 acc;
+    for (int qq = 0; qq < 2; ++qq) {
+      f32x4 acc[2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 x = lds_ld<f32x4>(xr + j * 4096 + q * 1024 + 16 * lane);
+      for (int jj = 0; jj < 2; ++jj) {
+        const f32x4 x = lds_ld<f32x4>(xr + (2 * qq + jj) * 1024 + 16 * lane);
+        const f32x4& mine = o[4 * PP + 2 * qq + jj];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[4 * q + e] = __builtin_fmaf(ao, x[e], aw * o[dt][4 * q + e]);
+        for (int e = 0; e < 4; ++e) acc[jj][e] = __builtin_fmaf(ao, x[e], aw * mine[e]);
+      }
+      float mx = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmax_(mx, fabsf(acc[jj][e]));
+      mx = row_max4(mx);
+      const int ex = __builtin_amdgcn_frexp_expf(mx);  // 0 for an all-zero quarter
+      exq[qq] = ex;
+      u32x2 v[2];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        v[jj] = pack_f16x4(__builtin_ldexpf(acc[jj][0], -ex), __builtin_ldexpf(acc[jj][1], -ex),
+                           __builtin_ldexpf(acc[jj][2], -ex), __builtin_ldexpf(acc[jj][3], -ex));
+      u32x2* po = reinterpret_cast<u32x2*>(a.part.po) + (((part * 2 + c.hp) * 4 + T) * 4 + 2 * PP + qq) * 128 + 8 * j16 + g4;
+      po[0] = v[0];  // columns 4 g4 .. 4 g4 + 3 of the quarter
+      po[4] = v[1];  // columns 16 + 4 g4 .. 16 + 4 g4 + 3
     }
-    // float16 with a power-of-two exponent per (row, quarter): the largest |value| maps into
-    // [0.5, 1); ldexp scales each element exactly, with no intermediate overflow
-    float mx = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmax_(mx, fabsf(acc[i]));
-    const float2 mp = pair32(mx);
-    const int ex = __builtin_amdgcn_frexp_expf(fmax_(mp.x, mp.y));  // 0 for an all-zero quarter
-    exj[j] = ex;
-    // lane-native groups: each store writes 1 KB of contiguous bytes
-    u32x2 v[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      v[q] = pack_f16x4(__builtin_ldexpf(acc[4 * q], -ex), __builtin_ldexpf(acc[4 * q + 1], -ex),
-                        __builtin_ldexpf(acc[4 * q + 2], -ex), __builtin_ldexpf(acc[4 * q + 3], -ex));
-    u32x4* po = reinterpret_cast<u32x4*>(a.part.po) + ((((part * 2 + c.hp) * 2 + T) * 4 + dt) * 64 + lane) * 2;
-    po[0] = u32x4{v[0][0], v[0][1], v[1][0], v[1][1]};
-    po[1] = u32x4{v[2][0], v[2][1], v[3][0], v[3][1]};
-  }
-  // the two quarters' exponents as one word of the row's record (e[2 PP], e[2 PP + 1])
-  if (h == 0)
-    reinterpret_cast<uint32_t*>(&a.part.rec[part * kQRows + row])[2 + PP] =
-        (uint32_t)(exj[0] & 0xffff) | ((uint32_t)exj[1] << 16);
+    // the two quarters' exponents as one word of the row's record (e[2 PP], e[2 PP + 1])
+    if (g4 == 0)
+      reinterpret_cast<uint32_t*>(&a.part.rec[part * kQRows + row])[2 + PP] =
+          (uint32_t)(exq[0] & 0xffff) | ((uint32_t)exq[1] << 16);
   };
   if (P == 0) store(std::integral_constant<int, 0>{}); else store(std::integral_constant<int, 1>{});
-  if (P == 0 && h == 0)
+  if (P == 0 && g4 == 0)
     *reinterpret_cast<float2*>(&a.part.rec[part * kQRows + row]) = float2{bad ? __builtin_nanf("") : M, L};
   report_expired(a.part.status, expired, lane);
 }
@@ -672,21 +689,21 @@ __global__ __launch_bounds__(kSThreads, 1) void k_attn_split(SplitArgs a) {
 
 // Combine: out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c, M = max_c m_c, with O_c the
 // float16 partial times 2^(its quarter's exponent). One wave per output row (kv head g, folded
-// row r), the splits taken 16 at a time: lane 16 dt + k holds split c0 + k's (m, l) and its
-// exponent for quarter dt; lane l then sums columns 2 l, 2 l + 1 over the splits in a fixed
-// order, rescaling between groups of 16 with the running max. Columns 2 l, 2 l + 1 are elements
-// e, e + 1 (e = 2 (l & 1)) of group q = (l & 15) >> 2 of lane n + 32 h (h = (l >> 1) & 1) in the
-// split's 2 KB piece (hp, T, dt = l >> 4): one 4-byte load per split.
+// row r = 64 hp + 16 T + j), the splits taken 16 at a time: lane 16 qd + k holds split c0 + k's
+// (m, l) and its exponent for quarter qd; lane l then sums columns 2 l, 2 l + 1 over the splits in
+// a fixed order, rescaling between groups of 16 with the running max. Columns 2 l, 2 l + 1 are
+// word l & 15 of row j in the split's 1 KB group (hp, T, qd = l >> 4): one 4-byte load per split,
+// 64 contiguous bytes per 16 lanes.
 // Workgroup w: head w % 8 (the XCD whose L2 took the head's partials), rows 4 (w / 8) .. +3.
 __global__ __launch_bounds__(256) void k_attn_combine(WsLayout p, uint16_t* out, int n_split) {
   const int lane = threadIdx.x & 63;
   const int g = blockIdx.x % kHkv;
   const int r = 4 * (blockIdx.x / kHkv) + (threadIdx.x >> 6);
-  const int dt = lane >> 4;
+  const int dt = lane >> 4;  // the quarter qd of the lane's columns
   const long long head = (long long)g * n_split;
-  const int grp = ((r >> 5) * 4 + dt);  // (hp * 2 + T) * 4 + dt, with r = 64 hp + 32 T + n
-  const int word = (((r & 31) + 32 * ((lane >> 1) & 1)) * 32 + 8 * ((lane & 15) >> 2) + 4 * (lane & 1)) / 4;
-  const uint32_t* pw = reinterpret_cast<const uint32_t*>(p.po) + (head * 16 + grp) * 512 + word;
+  const int grp = (r >> 4) * 4 + dt;  // (hp * 4 + T) * 4 + qd
+  const int word = 16 * (r & 15) + (lane & 15);
+  const uint32_t* pw = reinterpret_cast<const uint32_t*>(p.po) + (head * 32 + grp) * 256 + word;
   float M = -INFINITY, L = 0.f, acc0 = 0.f, acc1 = 0.f;
   for (int c0 = 0; c0 < n_split; c0 += 16) {
     const int cs = c0 + (lane & 15);
@@ -699,7 +716,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(WsLayout p, uint16_t* out,
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const int ck = c0 + k < n_split ? c0 + k : c0;
-      const uint32_t bits = pw[(long long)ck * 16 * 512];
+      const uint32_t bits = pw[(long long)ck * 32 * 256];
       const _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(bits & 0xffffu));
       const _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(bits >> 16));
       ov[k] = float2{(float)lo, (float)hi};
