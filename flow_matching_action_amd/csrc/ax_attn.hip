@@ -49,15 +49,24 @@ constexpr int kSL = 4;                          // loader waves
 constexpr int kSThreads = 64 * (kSC + kSL);
 constexpr int kSTile = 2 * kBlk * kD * 2;       // 16 KB: the K rows, then the V rows of a 32-key block
 constexpr int kSV = kBlk * kD * 2;              // offset of the V rows in a tile
-constexpr int kSRing = 6;                       // tiles; block b uses tile b % kSRing
-constexpr int kSMaxNB = 10;                     // blocks per key range
+constexpr int kSRing = 6;                       // tiles; block b uses tile b % kSRing (bf16 cache)
+constexpr int kSMaxNB = 10;                     // blocks per key range (bf16 cache)
+// fp8 cache: the ring's first four tiles take the bf16 blocks the loaders convert (block b in tile
+// b % 4), the rest four raw tiles of codes (32 rows of 128 bytes for K, then for V; block b in raw
+// tile b % 4)
+constexpr int kSRing8 = 4;
+constexpr int kSRaw8 = 4;
+constexpr int kSRawTile = 2 * kBlk * kD;
+constexpr int kSRawBase = kSRing8 * kSTile;
+static_assert(kSRawBase + kSRaw8 * kSRawTile <= kSRing * kSTile, "fp8 rings inside the bf16 ring");
+constexpr int kSMaxNB8 = 17;                    // blocks per key range (fp8 cache)
 constexpr int kSDepth = 3;                      // blocks in flight per loader wave
 constexpr int kSCacheRanges = 15;               // cache key ranges per kv head, at most
 constexpr float kSRescale = 16.0f;              // lazy-rescale threshold (log2 units)
 constexpr float kScoreScale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
 // LDS hand-off counters: prologue of row tile t landed, query rows normed, query fragments read,
 // block b landed, uses of tile r finished, merge data of row tile t written
-constexpr int kCPro = 0, kCNorm = 4, kCFrag = 5, kCLand = 6, kCDone = kCLand + kSMaxNB, kCMrg = kCDone + kSRing,
+constexpr int kCPro = 0, kCNorm = 4, kCFrag = 5, kCLand = 6, kCDone = kCLand + kSMaxNB8, kCMrg = kCDone + kSRing,
               kCN = kCMrg + 4;
 
 struct SplitArgs {
@@ -75,6 +84,12 @@ struct SplitArgs {
   int own_tail;            // own rows come from k/v tensors; q head parity 0 writes them to the cache tail
   uint16_t* Kc;
   uint16_t* Vc;
+  // fp8 cache (F8): codes [8][Smax][128] e4m3 and float32 row scales [8][Smax]; own rows, when
+  // given, are quantised here into the cache tail (kt_base / vt_base are then the own k / v)
+  uint8_t* Kc8;
+  uint8_t* Vc8;
+  float* Ks;
+  float* Vs;
   WsLayout part;            // the status word and the partials
   int spin_limit;           // polls before a wait gives up
   int S, Smax, n_split, kps;
@@ -136,6 +151,9 @@ __shared__ __attribute__((aligned(16))) uint8_t sQ[kT * 256];
 __shared__ __attribute__((aligned(16))) uint8_t sRope[2 * kT * 256];
 __shared__ __attribute__((aligned(16))) uint8_t sGam[2 * 256];
 __shared__ int sCnt[kCN];
+// fp8 cache: the row scales of block b, 16 per loader share L: K scales of rows 8 L .. 8 L + 7 at
+// [16 L .. 16 L + 7], V scales at [16 L + 8 .. 16 L + 15] (never reused within a launch)
+__shared__ __attribute__((aligned(16))) float sScl8[kSMaxNB8][64];
 
 // Bounded waits on the counters: a wave whose wait runs out (by default about 30 ms; thousands of
 // times any real wait) carries on and remembers it; its partial is then marked NaN and the
@@ -172,6 +190,7 @@ __device__ __forceinline__ int vswz16(int r) { return 2 * (r & 7); }
 struct SplitCtx {
   int g, hp, split, k_begin, k_end, nb, lane;
   bool own;                // the range of the 64 own tokens
+  bool pre;                // its blocks are filled in the prologue (own rows given, or the bf16 tail)
   bool partial;            // the last block of the range has keys past k_end
 };
 
@@ -189,6 +208,41 @@ __device__ __forceinline__ void dma_block_share(const uint16_t* kc, const uint16
     dma_x4(kc + (long long)v * kD + 8 * ((c.lane & 15) ^ kswz16(r)), tile + r0 * 256);
     dma_x4(vc + (long long)v * kD + 8 * ((c.lane & 15) ^ vswz16(r)), tile + kSV + r0 * 256);
   }
+}
+
+// fp8 cache: a loader's share of block b (keys k_begin + 32 b + r, rows r = 8 L .. 8 L + 7) into
+// raw tile b % 4: one 1 KB load for the K codes, one for the V codes, row-major 128 bytes a row,
+// and (lanes 0..15) the rows' K and V scales into the block's scale record. Keys past the tail
+// start are the cache tail's rows; rows past k_end reload the range's first key.
+__device__ __forceinline__ long long cache_row8(const SplitArgs& a, const SplitCtx& c, int v) {
+  v = v < c.k_end ? v : c.k_begin;
+  return (long long)c.g * a.Smax + (v < a.S ? v : a.Smax - kT + (v - a.S));
+}
+__device__ __forceinline__ void dma_block_f8(const SplitArgs& a, const SplitCtx& c, int L, int b) {
+  lds_u8* raw = AX_LDS(sRing) + kSRawBase + (b % kSRaw8) * kSRawTile;
+  const long long row = cache_row8(a, c, c.k_begin + kBlk * b + 8 * L + (c.lane >> 3));
+  dma_x4(a.Kc8 + row * kD + 16 * (c.lane & 7), raw + 8 * L * kD);
+  dma_x4(a.Vc8 + row * kD + 16 * (c.lane & 7), raw + kBlk * kD + 8 * L * kD);
+  if (c.lane < 16) {
+    const long long srow = cache_row8(a, c, c.k_begin + kBlk * b + 8 * L + (c.lane & 7));
+    dma_x1((c.lane < 8 ? a.Ks : a.Vs) + srow, AX_LDS(sScl8) + b * 256 + 64 * L);
+  }
+}
+// ... and, once landed, the same rows converted exactly (every e4m3 value is a bf16 value) into
+// the block's bf16 tile b % 4 with the bf16 tiles' swizzles: code chunk c8 of a row (16 bytes) is
+// bf16 chunks 2 c8 and 2 c8 + 1. The scales are applied in float32 by the compute waves. (Scaling
+// V here instead, rounded to bf16, made the launch 4% slower: the loaders share the SIMDs with
+// the compute waves.)
+__device__ __forceinline__ void convert_block_f8(const SplitCtx& c, int L, int b) {
+  const lds_u8* raw = AX_LDS(sRing) + kSRawBase + (b % kSRaw8) * kSRawTile;
+  lds_u8* tile = AX_LDS(sRing) + (b % kSRing8) * kSTile;
+  const int r = 8 * L + (c.lane >> 3), c8 = c.lane & 7;
+  const u32x4 kw = lds_ld<u32x4>(raw + r * kD + 16 * c8);
+  const u32x4 vw = lds_ld<u32x4>(raw + kBlk * kD + r * kD + 16 * c8);
+  lds_st(tile + r * 256 + 16 * ((2 * c8) ^ kswz16(r)), e4m3x8_to_bf16(kw[0], kw[1]));
+  lds_st(tile + r * 256 + 16 * ((2 * c8 + 1) ^ kswz16(r)), e4m3x8_to_bf16(kw[2], kw[3]));
+  lds_st(tile + kSV + r * 256 + 16 * ((2 * c8) ^ vswz16(r)), e4m3x8_to_bf16(vw[0], vw[1]));
+  lds_st(tile + kSV + r * 256 + 16 * ((2 * c8 + 1) ^ vswz16(r)), e4m3x8_to_bf16(vw[2], vw[3]));
 }
 
 __device__ __forceinline__ float fmax_(float a, float b) { return __builtin_elementwise_maximum(a, b); }
@@ -281,18 +335,56 @@ __device__ __forceinline__ void norm_rows(const SplitArgs& a, const SplitCtx& c,
   }
 }
 
+// fp8 cache, own range: the own k rows (normed and roped, or given roped) and the own v rows of
+// tokens row0 .. row0 + 4 NP - 1 quantised per row in place (16 lanes per row: quant_row16, the
+// definition of the cache format), the tiles then holding the codes' e4m3 values in bf16 and the
+// block's scale record the row scales, as for a block the loaders convert; the codes and scales
+// go to the cache tail here (q head parity 0), while they are at hand.
+template <int NP>
+__device__ __forceinline__ void quant_own_rows(const SplitArgs& a, const SplitCtx& c, const int row0) {
+  const int j16 = c.lane & 15, r4 = c.lane >> 4;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int tok = row0 + 4 * i + r4;
+    const int tr = tok & (kBlk - 1), blk = tok >> 5;
+    lds_u8* krow = AX_LDS(sRing) + blk * kSTile + tr * 256 + 16 * (j16 ^ kswz16(tr));
+    lds_u8* vrow = AX_LDS(sRing) + blk * kSTile + kSV + tr * 256 + 16 * (j16 ^ vswz16(tr));
+    float x[8], y[8], sk, sv;
+    unpack8v(lds_ld<u32x4>(krow), x);
+    unpack8v(lds_ld<u32x4>(vrow), y);
+    const uint2 ck = quant_row16(x, sk);
+    const uint2 cv = quant_row16(y, sv);
+    lds_st(krow, e4m3x8_to_bf16(ck.x, ck.y));
+    lds_st(vrow, e4m3x8_to_bf16(cv.x, cv.y));
+    if (j16 == 0) {
+      sScl8[blk][16 * (tr >> 3) + (tr & 7)] = sk;
+      sScl8[blk][16 * (tr >> 3) + 8 + (tr & 7)] = sv;
+    }
+    if (c.hp == 0) {
+      const long long crow = (long long)c.g * a.Smax + a.Smax - kT + tok;
+      *reinterpret_cast<uint2*>(a.Kc8 + crow * kD + 8 * j16) = ck;
+      *reinterpret_cast<uint2*>(a.Vc8 + crow * kD + 8 * j16) = cv;
+      if (j16 == 0) {
+        a.Ks[crow] = sk;
+        a.Vs[crow] = sv;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------- loaders
-template <bool NORM>
+template <bool NORM, bool F8>
 __device__ __forceinline__ void split_loader(const SplitArgs& a, const SplitCtx& c, int L) {
   const int lane = c.lane, j16 = lane & 15, r4 = lane >> 4;
   const long long head_off = (long long)c.g * a.Smax * kD;
-  const uint16_t* kc = a.Kc + head_off;
-  const uint16_t* vc = a.Vc + head_off;
+  const uint16_t* kc = F8 ? nullptr : a.Kc + head_off;
+  const uint16_t* vc = F8 ? nullptr : a.Vc + head_off;
   lds_u8* ring = AX_LDS(sRing);
   // 1. the prologue of row tile L (the two compute waves on this SIMD): query rows 16 L + 4 i + r4
   //    (lane l lands at 16 l of each 1 KB, so it fetches the chunk the row's swizzle puts there),
   //    their RoPE rows, the gammas;
-  //    in the own range also own k/v rows 16 L .. 16 L + 15 (blocks 0, 1 in tiles 0, 1)
+  //    in the own range also own k/v rows 16 L .. 16 L + 15 (blocks 0, 1 in tiles 0, 1; with the
+  //    fp8 cache only when the own rows are given, else that range is streamed like any other)
   const uint16_t* qh = a.q + (long long)(2 * c.g + c.hp) * kT * kD;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -311,7 +403,7 @@ __device__ __forceinline__ void split_loader(const SplitArgs& a, const SplitCtx&
     dma_x1(a.gq + 2 * lane, AX_LDS(sGam));
     dma_x1(a.gk + 2 * lane, AX_LDS(sGam) + 256);
   }
-  if (c.own) {
+  if (c.pre) {
     const uint16_t* kt = a.kt_base + c.g * a.tail_stride;
     const uint16_t* vt = a.vt_base + c.g * a.tail_stride;
     lds_u8* ot = ring + (L >> 1) * kSTile;  // tokens 0..31 in tile 0, 32..63 in tile 1
@@ -326,33 +418,39 @@ __device__ __forceinline__ void split_loader(const SplitArgs& a, const SplitCtx&
   }
   lds_barrier();  // counters cleared (the workgroup's only barrier)
   bool expired = false;
-  if (c.own) {
+  if (c.pre) {
     vm_wait<0>();
     arrive(&sCnt[kCPro + L], lane);
-    if constexpr (NORM) {
-      norm_rows<2>(a, c, 16 * L + 8);
-      arrive(&sCnt[kCNorm], lane);
-    }
+    if constexpr (NORM) norm_rows<2>(a, c, 16 * L + 8);
+    if constexpr (F8) quant_own_rows<2>(a, c, 16 * L + 8);
+    if constexpr (NORM || F8) arrive(&sCnt[kCNorm], lane);
     return;
   }
-  // 2. blocks: kSDepth in flight; block b goes to tile b % kSRing once all four uses of the
-  //    tile's previous block (one per row tile) are finished. Each block is 4 loads of this wave.
+  // 2. blocks: kSDepth in flight. bf16: block b goes to tile b % kSRing once all four uses of the
+  //    tile's previous block (one per row tile) are finished; 4 loads of this wave. fp8: block b
+  //    goes to raw tile b % 4 at once (this wave converted its previous block), 3 loads; once
+  //    landed, and once the bf16 tile b % 4 is free, this wave converts its rows into it.
+  constexpr int LPB = F8 ? 3 : 4;  // loads per block
   const int nb = c.nb;
   auto issue = [&](int b) {
-    if (b >= kSRing) await_cnt(kCDone + b % kSRing, (kSC / 2) * (b / kSRing), a.spin_limit, expired);
-    dma_block_share(kc, vc, c, L, b, ring + (b % kSRing) * kSTile);
+    if constexpr (F8) {
+      dma_block_f8(a, c, L, b);
+    } else {
+      if (b >= kSRing) await_cnt(kCDone + b % kSRing, (kSC / 2) * (b / kSRing), a.spin_limit, expired);
+      dma_block_share(kc, vc, c, L, b, ring + (b % kSRing) * kSTile);
+    }
   };
   const int d0 = nb < kSDepth ? nb : kSDepth;
   // blocks 0 and 1, then the prologue's hand-off (it was issued first: it has landed once at most
-  // their 8 loads are outstanding), this wave's share of the norm, then the next block: issuing
+  // their loads are outstanding), this wave's share of the norm, then the next block: issuing
   // loads takes the wave long enough that announcing the prologue after all of them would hold
   // up the norm
   issue(0);
   if (d0 > 1) {
     issue(1);
-    vm_wait<8>();
+    vm_wait<2 * LPB>();
   } else {
-    vm_wait<4>();
+    vm_wait<LPB>();
   }
   arrive(&sCnt[kCPro + L], lane);
   if constexpr (NORM) {
@@ -362,7 +460,11 @@ __device__ __forceinline__ void split_loader(const SplitArgs& a, const SplitCtx&
   for (int b = 2; b < d0; ++b) issue(b);
   for (int b = 0; b < nb; ++b) {
     const int later = (b + kSDepth - 1 < nb ? b + kSDepth - 1 : nb - 1) - b;  // blocks issued after b
-    if (later >= 2) vm_wait<8>(); else if (later == 1) vm_wait<4>(); else vm_wait<0>();
+    if (later >= 2) vm_wait<2 * LPB>(); else if (later == 1) vm_wait<LPB>(); else vm_wait<0>();
+    if constexpr (F8) {
+      if (b >= kSRing8) await_cnt(kCDone + b % kSRing8, (kSC / 2) * (b / kSRing8), a.spin_limit, expired);
+      convert_block_f8(c, L, b);
+    }
     arrive(&sCnt[kCLand + b], lane);
     if (b + kSDepth < nb) issue(b + kSDepth);
   }
@@ -383,7 +485,7 @@ __device__ __forceinline__ void split_loader(const SplitArgs& a, const SplitCtx&
 //   accumulators (lane slots 0..3 = keys 4 (l >> 4) + i, slots 4..7 = keys 16 + 4 (l >> 4) + i),
 //   A = V^T read in the same key order by two ds_read_b64_tr_b16; lane l then holds
 //   O[query row l & 15][16 dt + 4 (l >> 4) + i].
-template <bool NORM>
+template <bool NORM, bool F8>
 __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx& c, const int W) {
   const int T = W & 3, P = W >> 2;
   const int NB = c.nb > P ? (c.nb - P + 1) / 2 : 0;  // blocks P, P + 2, ... below nb
@@ -395,12 +497,15 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
 
   // 1. Norm + RoPE of query rows 16 T + 4 P .. + 3 in place (rows 16 T + 8 .. + 15 are loader T's,
   //    the other four the partner wave's); in the own range also the own k rows of the same
-  //    tokens. Roped q arrives ready.
+  //    tokens, and with the fp8 cache the own k and v rows quantised. Roped q arrives ready.
   await_cnt(kCPro + T, 1, a.spin_limit, expired);
   if constexpr (NORM) norm_rows<1>(a, c, 16 * T + 4 * P);
+  if constexpr (F8) {
+    if (c.pre) quant_own_rows<1>(a, c, 16 * T + 4 * P);
+  }
   arrive(&sCnt[kCNorm], lane);
-  // all 64 query rows (and in the own range the own k rows) ready: twelve waves norm them
-  await_cnt(kCNorm, NORM ? kSC + kSL : kSC, a.spin_limit, expired);
+  // all 64 query rows (and in the own range the own rows) ready: twelve waves norm them
+  await_cnt(kCNorm, (NORM || (F8 && c.pre)) ? kSC + kSL : kSC, a.spin_limit, expired);
 
   // 2. The query rows of row tile T as MFMA B operands (k-step kk: columns 32 kk .. 32 kk + 31).
   bf16x8 qf[4];
@@ -434,7 +539,8 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
   v4i16 vt[8][2];
   bf16x8 pb;
   const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
-  auto tile_of = [&](int b) { return ring + (b % kSRing) * kSTile; };  // (b uniform: scalar ops)
+  constexpr int RS = F8 ? kSRing8 : kSRing;
+  auto tile_of = [&](int b) { return ring + (b % RS) * kSTile; };  // (b uniform: scalar ops)
   auto read_k = [&](const lds_u8* base) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -458,21 +564,50 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
   };
   // p = 2^(s log2(e) / sqrt(128) - m) (v_exp_f32 directly: the arguments are at most kSRescale, or
   // -inf), their bf16 pairs (the PV operand) and the row sum of the same rounded values, so every
-  // output row is an exact convex combination of V rows
-  auto softmax = [&]() {
+  // output row is an exact convex combination of V rows. fp8 cache (block bx): p 2^kF8VShift
+  // from the same exponential, times the key's value scale before the rounding to bf16 (the shift
+  // keeps the products of every float32 scale from the denormals up to 2^25 in bf16's normal
+  // range; O then accumulates in units of 2^-kF8VShift), and the row sum of the float32 p
+  // 2^kF8VShift.
+  auto softmax = [&](int bx) {
     float ps[2] = {0.f, 0.f};
+    f32x4 vs[2];
+    if constexpr (F8) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        vs[t] = lds_ld<f32x4>(AX_LDS(sScl8) + bx * 256 + 64 * (2 * t + (g4 >> 1)) + 16 * (g4 & 1) + 32);
+    }
+    const float mo = F8 ? (float)kF8VShift - m : -m;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][2 * i], kScoreScale, -m));
-        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][2 * i + 1], kScoreScale, -m));
-        const bf16x2_t pr = {(__bf16)e0, (__bf16)e1};
-        pb[4 * t + 2 * i] = pr[0];
-        pb[4 * t + 2 * i + 1] = pr[1];
-        ps[i] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ps[i], false);
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][2 * i], kScoreScale, mo));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][2 * i + 1], kScoreScale, mo));
+        if constexpr (F8) {
+          const bf16x2_t pr = {(__bf16)(e0 * vs[t][2 * i]), (__bf16)(e1 * vs[t][2 * i + 1])};
+          pb[4 * t + 2 * i] = pr[0];
+          pb[4 * t + 2 * i + 1] = pr[1];
+          ps[i] += e0 + e1;
+        } else {
+          const bf16x2_t pr = {(__bf16)e0, (__bf16)e1};
+          pb[4 * t + 2 * i] = pr[0];
+          pb[4 * t + 2 * i + 1] = pr[1];
+          ps[i] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ps[i], false);
+        }
       }
     l += ps[0] + ps[1];
+  };
+  // fp8 cache: the scores of block bx times their keys' scales (the lane's keys 16 t + 4 g4 + i)
+  auto kscale = [&](f32x4* sd, int bx) {
+    if constexpr (F8) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const f32x4 ks = lds_ld<f32x4>(AX_LDS(sScl8) + bx * 256 + 64 * (2 * t + (g4 >> 1)) + 16 * (g4 & 1));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sd[t][i] *= ks[i];
+      }
+    }
   };
   auto pv = [&]() {
 #pragma unroll
@@ -496,16 +631,16 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
   // without waiting for them: a wave's LDS operations execute in order, so the increment cannot
   // pass the reads, and a loader that sees it only then starts loads that land far later.
   auto release = [&](int b) {
-    if (c.own) return;
+    if (c.pre) return;
     __builtin_amdgcn_sched_barrier(0);
     if (lane == 0) {
-      const unsigned off = (unsigned)(uintptr_t)(lds_int*)&sCnt[kCDone + b % kSRing];
+      const unsigned off = (unsigned)(uintptr_t)(lds_int*)&sCnt[kCDone + b % RS];
       asm volatile("ds_add_u32 %0, %1" ::"v"(off), "v"(1) : "memory");
     }
     __builtin_amdgcn_sched_barrier(0);
   };
   auto landed = [&](int b) {
-    if (c.own) return;  // the own blocks are ready with the normed query rows
+    if (c.pre) return;  // the own blocks are ready with the normed query rows
     await_cnt(kCLand + b, kSL, a.spin_limit, expired);
   };
 
@@ -518,6 +653,7 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
     landed(P);
     read_k(tile_of(P));
     qk(s);
+    kscale(s, P);
     read_v(tile_of(P));
     m = row_max4(lane_max8(s)) * kScoreScale;  // finite: the block holds a visible key
     if (c.partial && P == c.nb - 1) mask_tail(s, P);
@@ -531,13 +667,14 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
       const int b = P + 2 * k;
       const bool more = k + 1 < NB;
       // (the count is read behind this block's K reads, which the scores need first anyway)
-      const int early = (more && !c.own)
+      const int early = (more && !c.pre)
                             ? __hip_atomic_load(&sCnt[kCLand + b + 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
                             : kSL;
       // (A) scores of block b beside the exponentials of block b - 2
       f32x4 sn[2];
       qk(sn);
-      softmax();
+      softmax(b - 2);
+      kscale(sn, b);
       // (B) PV of block b - 2 beside the lane's share of the row max of block b
       pv();
       const float bm = lane_max8(sn) * kScoreScale;
@@ -564,21 +701,24 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
         read_k(tile_of(b + 2));
       }
     }
-    softmax();
+    softmax(P + 2 * (NB - 1));
     pv();
   }
 
   // 4. Own range, q head parity 0: the roped own k rows and the own v rows of tokens 16 T + 8 P ..
-  //    + 7 to the cache tail (the loaders load nothing into the own range's tiles).
-  if (c.own && a.own_tail && c.hp == 0) {
+  //    + 7 to the cache tail (the loaders load nothing into the own range's tiles). (The fp8 cache's
+  //    tail was written with the quantisation.)
+  if constexpr (!F8) {
+    if (c.own && a.own_tail && c.hp == 0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int tok = 16 * T + 8 * P + 4 * i + g4;
-      const int tr = tok & (kBlk - 1);
-      const lds_u8* ot = ring + (tok >> 5) * kSTile;
-      const long long dst = head_off + (long long)(a.Smax - kT + tok) * kD + 8 * j16;
-      *reinterpret_cast<u32x4*>(a.Kc + dst) = lds_ld<u32x4>(ot + tr * 256 + 16 * (j16 ^ kswz16(tr)));
-      *reinterpret_cast<u32x4*>(a.Vc + dst) = lds_ld<u32x4>(ot + kSV + tr * 256 + 16 * (j16 ^ vswz16(tr)));
+      for (int i = 0; i < 2; ++i) {
+        const int tok = 16 * T + 8 * P + 4 * i + g4;
+        const int tr = tok & (kBlk - 1);
+        const lds_u8* ot = ring + (tok >> 5) * kSTile;
+        const long long dst = head_off + (long long)(a.Smax - kT + tok) * kD + 8 * j16;
+        *reinterpret_cast<u32x4*>(a.Kc + dst) = lds_ld<u32x4>(ot + tr * 256 + 16 * (j16 ^ kswz16(tr)));
+        *reinterpret_cast<u32x4*>(a.Vc + dst) = lds_ld<u32x4>(ot + kSV + tr * 256 + 16 * (j16 ^ vswz16(tr)));
+      }
     }
   }
 
@@ -643,7 +783,7 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
         for (int e = 0; e < 4; ++e) mx = fmax_(mx, fabsf(acc[jj][e]));
       mx = row_max4(mx);
       const int ex = __builtin_amdgcn_frexp_expf(mx);  // 0 for an all-zero quarter
-      exq[qq] = ex;
+      exq[qq] = F8 ? ex - kF8VShift : ex;  // (fp8: O in units of 2^-kF8VShift)
       u32x2 v[2];
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
@@ -660,13 +800,14 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
   };
   if (P == 0) store(std::integral_constant<int, 0>{}); else store(std::integral_constant<int, 1>{});
   if (P == 0 && g4 == 0)
-    *reinterpret_cast<float2*>(&a.part.rec[part * kQRows + row]) = float2{bad ? __builtin_nanf("") : M, L};
+    *reinterpret_cast<float2*>(&a.part.rec[part * kQRows + row]) =
+        float2{bad ? __builtin_nanf("") : M, F8 ? L * 0x1p-64f : L};  // (fp8: l in units of 2^-kF8VShift)
   report_expired(a.part.status, expired, lane);
 }
 
 // NORM: q and the own k arrive raw and are normed + roped here (the layer step); otherwise both
 // arrive roped (attention only).
-template <bool NORM>
+template <bool NORM, bool F8>
 __global__ __launch_bounds__(kSThreads, 1) void k_attn_split(SplitArgs a) {
   SplitCtx c;
   c.lane = threadIdx.x & 63;
@@ -676,15 +817,16 @@ __global__ __launch_bounds__(kSThreads, 1) void k_attn_split(SplitArgs a) {
   c.split = j >> 1;
   c.hp = j & 1;
   c.own = c.split >= a.n_cache_split;
+  c.pre = c.own && (!F8 || a.own_tail);
   c.k_begin = c.own ? a.S : c.split * a.kps;
   c.k_end = c.own ? a.S + kT : min(c.k_begin + a.kps, a.S);
   c.nb = (c.k_end - c.k_begin + kBlk - 1) / kBlk;
   c.partial = c.nb * kBlk != c.k_end - c.k_begin;
   if (threadIdx.x < kCN) sCnt[threadIdx.x] = 0;  // (wave 0, before its barrier)
   if (wave >= kSL)
-    split_compute<NORM>(a, c, wave - kSL);
+    split_compute<NORM, F8>(a, c, wave - kSL);
   else
-    split_loader<NORM>(a, c, wave);
+    split_loader<NORM, F8>(a, c, wave);
 }
 
 // Combine: out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c, M = max_c m_c, with O_c the
@@ -801,7 +943,7 @@ hipError_t launch_attn(const AttnPlan& plan, const AttnLaunch& p, hipStream_t st
 }
 
 hipError_t launch_attn_split(const AttnPlan& plan, const AttnLaunch& p, hipStream_t st) {
-  SplitArgs a;
+  SplitArgs a{};
   a.q = p.q; a.gq = p.gq; a.gk = p.gk; a.cos_t = p.cos_t; a.sin_t = p.sin_t; a.eps = p.eps;
   a.own_tail = p.k_tail != nullptr;
   if (a.own_tail) {
@@ -817,10 +959,57 @@ hipError_t launch_attn_split(const AttnPlan& plan, const AttnLaunch& p, hipStrea
   a.n_cache_split = plan.n_cache_split;
   const dim3 grid(kHkv * plan.n_split * 2);
   if (p.q_norm)
-    hipLaunchKernelGGL(k_attn_split<true>, grid, dim3(kSThreads), 0, st, a);
+    hipLaunchKernelGGL((k_attn_split<true, false>), grid, dim3(kSThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(k_attn_split<false>, grid, dim3(kSThreads), 0, st, a);
+    hipLaunchKernelGGL((k_attn_split<false, false>), grid, dim3(kSThreads), 0, st, a);
   return hipGetLastError();
+}
+
+// fp8 cache: the same plan with ranges of at most 17 blocks (at S = 8128: 15 ranges of 544 keys,
+// 256 workgroups), the same partials and combine.
+AttnPlan attn_plan_f8(int S, int /*Smax*/) {
+  AttnPlan p;
+  p.n_keys = S + kT;
+  int kps = (S + kSCacheRanges - 1) / kSCacheRanges;
+  kps = (kps + kBlk - 1) / kBlk * kBlk;
+  if (kps < kBlk) kps = kBlk;
+  if (kps > kBlk * kSMaxNB8) kps = kBlk * kSMaxNB8;
+  p.keys_per_split = kps;
+  p.n_cache_split = (S + kps - 1) / kps;
+  p.n_split = p.n_cache_split + 1;
+  p.blocks = kps / kBlk;
+  return p;
+}
+
+size_t attn_partials_bytes_f8(const AttnPlan& p) { return attn_partials_bytes(p); }
+
+hipError_t launch_attn_f8_combine(const AttnPlan& plan, const void* ws, uint16_t* out, hipStream_t st) {
+  return launch_attn_combine(plan, ws, out, st);
+}
+
+hipError_t launch_attn_f8_split(const AttnPlan& plan, const AttnLaunchF8& p, hipStream_t st) {
+  SplitArgs a{};
+  a.q = p.q; a.gq = p.gq; a.gk = p.gk; a.cos_t = p.cos_t; a.sin_t = p.sin_t; a.eps = p.eps;
+  a.own_tail = p.k_own != nullptr;
+  a.kt_base = p.k_own; a.vt_base = p.v_own; a.tail_stride = (long long)kT * kD;
+  a.Kc = nullptr; a.Vc = nullptr;
+  a.Kc8 = p.Kc; a.Vc8 = p.Vc; a.Ks = p.Ks; a.Vs = p.Vs;
+  a.part = ws_layout(plan, p.ws);
+  a.spin_limit = wait_limit();
+  a.S = p.S; a.Smax = p.Smax; a.n_split = plan.n_split; a.kps = plan.keys_per_split;
+  a.n_cache_split = plan.n_cache_split;
+  const dim3 grid(kHkv * plan.n_split * 2);
+  if (p.q_norm)
+    hipLaunchKernelGGL((k_attn_split<true, true>), grid, dim3(kSThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_attn_split<false, true>), grid, dim3(kSThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_f8(const AttnPlan& plan, const AttnLaunchF8& p, hipStream_t st) {
+  const hipError_t e = launch_attn_f8_split(plan, p, st);
+  if (e != hipSuccess) return e;
+  return launch_attn_combine(plan, p.ws, p.out, st);
 }
 
 __global__ __launch_bounds__(256) void k_copy_words(const u32x4* src, u32x4* dst, size_t n) {

@@ -1,21 +1,13 @@
-// Device-side pieces shared by the split-KV attention kernels (bf16 and fp8 caches):
-// launch shape, the LDS hand-off counters, the MFMA operand layouts, and the query
-// norm/RoPE helpers. The kernels themselves are in ax_attn.hip and ax_attn_f8.hip.
+// Device-side pieces shared by the attention kernels (the expert step over bf16 and fp8 caches,
+// ax_attn.hip; the text-model decode step, ax_decode.hip): the LDS hand-off counters and bounded
+// waits, the workspace status word, the decode kernel's MFMA operand layouts, the float16 partial
+// packing and the e4m3 conversions.
 #pragma once
 #include "ax_dev.h"
 
 namespace ax {
 
 constexpr int kBlk = 32;                      // keys per block
-constexpr int kQBytes = kQRows * kD * 2;      // 32 KB: the 128 query rows in bf16
-constexpr int kComputeWaves = 8;
-constexpr int kLoaderWaves = 4;
-constexpr int kThreads = 64 * (kComputeWaves + kLoaderWaves);
-constexpr int kMaxBlocks = 12;                // blocks per split in any kernel variant
-// LDS hand-off counters: queries normed, query fragments read, block b landed, block b
-// consumed, merge data of query group q ready
-constexpr int kCntQNormed = 0, kCntQRead = 1, kCntBlock = 2;
-constexpr int kCntDone = kCntBlock + kMaxBlocks, kCntMerge = kCntDone + kMaxBlocks, kNCnt = kCntMerge + 4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescale = 8.0f;              // lazy-rescale threshold (log2 units)
 constexpr int kNonTemporal = 2;               // cache-policy operand of a load: nt
@@ -24,8 +16,9 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Chunk swizzles (16-byte chunk index within a row: 16 chunks in a bf16 row, 8 in an fp8 row).
-// Query rows are read by consecutive lanes from consecutive rows: all 4 row bits.
+// Chunk swizzles (16-byte chunk index within a 256-byte bf16 row). Query rows are read by
+// consecutive lanes from consecutive rows: all 4 row bits. (kswz, vswz: the decode kernel's
+// 32-row MFMA layout; the expert kernel's 16-row layout has its own.)
 __device__ __forceinline__ int qswz(int r) { return r & 15; }
 // K rows are read by 8-lane groups from rows {0..3, 8..11} + 4j (the MFMA row order pi below):
 // bits 0, 1 and 3 of the row make those 8 rows hit 8 distinct 16-byte bank groups. The
@@ -73,7 +66,7 @@ __device__ __forceinline__ void lds_barrier() {
 // In-workgroup hand-off counters in LDS. A producer wave bumps a counter once its data is
 // in LDS; consumers poll it. Unlike s_barrier this never makes a producer wait for its
 // consumers, so the cache stream runs ahead of the arithmetic as far as the LDS tiles
-// allow (tiles are never reused within a launch, so there is nothing to wait for).
+// allow.
 // The increment is written as inline asm: the compiler cannot tell an LDS atomic from the
 // direct-to-LDS loads still in flight and would drain them all (vmcnt(0)) before it.
 typedef __attribute__((address_space(3))) int lds_int;
@@ -152,153 +145,51 @@ __device__ __forceinline__ u32x4 pack8v(const float* f) {
 }
 
 
-// RMSNorm + RoPE in place in LDS of the query rows 32p + r16 (p = 0..3) that this lane's
-// 16-lane group holds, in the pair layout (columns 4 j16 .. +3 and 64 + 4 j16 .. +3), rows
-// swizzled by qswz. graw: the lane's 8 gammas in that layout; cs[t]: cos, sin of frequencies
-// 4 j16 .. +3 of token set t = p & 1. All rows are read before any is written back.
-__device__ __forceinline__ void norm_rope_query_rows(uint8_t* qlds, const uint2 (&graw)[2], const f32x4 (&cs)[2][2],
-                                                     int j16, int r16, float eps) {
-  float qg[8], A[2][8], B[2][8];
-  unpack_pair(graw[0], graw[1], qg);
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const float c[4] = {cs[t][0][0], cs[t][0][1], cs[t][0][2], cs[t][0][3]};
-    const float sn[4] = {cs[t][1][0], cs[t][1][1], cs[t][1][2], cs[t][1][3]};
-    rope_coef_pair(qg, c, sn, A[t], B[t]);
-  }
-  uint2 lo[4], hi[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int r = 32 * p + r16;
-    lo[p] = *reinterpret_cast<const uint2*>(qlds + r * 256 + pair_off_lo(j16, qswz(r)));
-    hi[p] = *reinterpret_cast<const uint2*>(qlds + r * 256 + pair_off_hi(j16, qswz(r)));
-  }
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    float x[8];
-    unpack_pair(lo[p], hi[p], x);
-    norm_rope_pair(x, A[p & 1], B[p & 1], eps);
-    pack_pair(x, lo[p], hi[p]);
-  }
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int r = 32 * p + r16;
-    *reinterpret_cast<uint2*>(qlds + r * 256 + pair_off_lo(j16, qswz(r))) = lo[p];
-    *reinterpret_cast<uint2*>(qlds + r * 256 + pair_off_hi(j16, qswz(r))) = hi[p];
-  }
-}
-
-
-// Split partials in float16. O is stored as O 2^-e per (split, query row), with 2^e the power of
-// two just above the row's largest |O| (max |O 2^-e| in [0.5, 1)); e is stored beside the row's
-// m and l, which stay float32 and unscaled. The scaling is ldexp, exact for every finite O
-// (denormal ones included: e >= -149 and |O 2^-e| < 1), so nothing overflows whatever the
-// magnitudes; the combine multiplies the row's weight by 2^e. Float16 then keeps 11 significant
-// bits of every element within 2^14 of the row's largest |O| (its normal range), and smaller
-// elements an absolute error below 2^-25 of that largest value.
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+// Four floats to float16 (nearest even) in two 32-bit words.
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x2 pack_f16x4(float a, float b, float c, float d) {
   const f16x4 v = {(_Float16)a, (_Float16)b, (_Float16)c, (_Float16)d};  // nearest even
   return __builtin_bit_cast(u32x2, v);
 }
-__device__ __forceinline__ f32x4 unpack_f16x4(const u32x2& u) {
-  const f16x4 v = __builtin_bit_cast(f16x4, u);
-  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+constexpr float kE4m3Max = 448.0f;
+
+// 8 e4m3 codes (bytes of w0, then w1) -> 8 bf16, exactly.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// The fp8 kernel folds the value scales into P with a fixed factor 2^kF8VShift (the products
-// p * scale * 2^64 stay in bf16's normal range for every float32 scale from the denormals up to
-// 2^25), so its O accumulates in units of 2^-64; the stored exponent takes the factor back out.
+// Per-row e4m3 quantisation of a 128-wide row held by a group of 16 lanes (8 values each):
+// scale = max |x| / 448 (1 for an all-zero row), codes = nearest-even e4m3 of x / scale,
+// saturated to +-448 (v_cvt_pk_fp8_f32 rounds to nearest even and does not saturate, hence
+// the clamp). Divisions are float32, correctly rounded. All 16 lanes must call together.
+__device__ __forceinline__ uint2 quant_row16(const float* x, float& scale) {
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+  m = fmaxf(m, row_ror<8>(m));
+  m = fmaxf(m, row_ror<4>(m));
+  m = fmaxf(m, row_ror<2>(m));
+  m = fmaxf(m, row_ror<1>(m));
+  scale = m > 0.f ? m / kE4m3Max : 1.0f;
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf(x[e] / scale, -kE4m3Max), kE4m3Max);
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
+  return make_uint2((uint32_t)w0, (uint32_t)w1);
+}
+
+// The fp8-cache kernel folds the value scales into P with a fixed factor 2^kF8VShift (the
+// products p * scale * 2^64 stay in bf16's normal range for every float32 scale from the
+// denormals up to 2^25), so its O accumulates in units of 2^-64; the stored exponent takes the
+// factor back out.
 constexpr int kF8VShift = 64;
-
-// Store of one wave's partial for query rows 32 qgrp .. +31 (lane (n, h): row n, the half h of
-// the accumulator layout): O at po + ((part * 4 + qgrp) * 16 + j) * 64 + lane in 8-byte units
-// (slot j = 4t + jj, 4 float16 each, non-temporal: the combine reads it once), m, l and e at
-// pm / pl / pe + part * 128 + query row. l_tot is the row's whole sum (both halves); O is in
-// units of 2^-kF8VShift, so e - kF8VShift is stored.
-__device__ __forceinline__ void store_partial_f16(const f32x16 (&o)[4], float m, float l_tot, int qgrp, int lane,
-                                                  float* po_all, float* pm, float* pl, int* pe, long long part) {
-  const int n = lane & 31;
-  const int h = lane >> 5;
-  float amax = 0.f;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(o[t][i]));
-  const float2 ap = pair32(amax);
-  const int e = __builtin_amdgcn_frexp_expf(fmaxf(ap.x, ap.y));  // 0 for an all-zero row
-  u32x2* po = reinterpret_cast<u32x2*>(po_all) + (part * 4 + qgrp) * (16 * 64) + lane;
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-      __builtin_nontemporal_store(pack_f16x4(__builtin_ldexpf(o[t][4 * jj], -e), __builtin_ldexpf(o[t][4 * jj + 1], -e),
-                                             __builtin_ldexpf(o[t][4 * jj + 2], -e),
-                                             __builtin_ldexpf(o[t][4 * jj + 3], -e)),
-                                  &po[(4 * t + jj) * 64]);
-  if (h == 0) {
-    const int qrow = 32 * qgrp + n;
-    __builtin_nontemporal_store(m, &pm[part * kQRows + qrow]);
-    __builtin_nontemporal_store(l_tot, &pl[part * kQRows + qrow]);
-    __builtin_nontemporal_store(e - kF8VShift, &pe[part * kQRows + qrow]);
-  }
-}
-
-// End of a split: the two parity waves of query group qgrp hold (m, l, O) over disjoint
-// blocks. The odd wave hands its O (16 KB: slot j = 4t + jj of the accumulator layout, 1 KB
-// per slot, slots 0..7 at xlo and 8..15 at xhi) and (m, l) to the even one through LDS, once
-// region_free() says nobody reads those regions any more; the even wave rescales both to
-// the larger m and stores the split's partial (store_partial_f16). With a single block
-// (two_parities false) the odd wave holds nothing.
-template <typename RegionFree>
-__device__ __forceinline__ void merge_and_store_partial(f32x16 (&o)[4], float m_run, float l_run,
-                                                        bool two_parities, int par, int qgrp, int lane,
-                                                        uint8_t* xlo, uint8_t* xhi, RegionFree&& region_free,
-                                                        float (*mlx)[2][32], int* cnt, float* po_all,
-                                                        float* pm, float* pl, int* pe, long long part,
-                                                        int limit, bool& expired) {
-  const int n = lane & 31;
-  const int h = lane >> 5;
-  const float2 l_pair = pair32(l_run);
-  const float l_tot = l_pair.x + l_pair.y;
-  if (!two_parities) {
-    if (par == 1) return;
-    store_partial_f16(o, expired ? __builtin_nanf("") : m_run, l_tot, qgrp, lane, po_all, pm, pl, pe, part);
-    return;
-  }
-  auto slot = [&](int j) { return reinterpret_cast<f32x4*>(j < 8 ? xlo + j * 1024 : xhi + (j - 8) * 1024) + lane; };
-  if (par == 1) {
-    region_free();
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        *slot(4 * t + jj) = f32x4{o[t][4 * jj], o[t][4 * jj + 1], o[t][4 * jj + 2], o[t][4 * jj + 3]};
-    if (h == 0) {
-      mlx[qgrp][0][n] = m_run;
-      mlx[qgrp][1][n] = l_tot;
-    }
-    arrive(&cnt[kCntMerge + qgrp], lane);
-    return;
-  }
-  await(&cnt[kCntMerge + qgrp], 1, limit, expired);
-  const float m_o = mlx[qgrp][0][n];
-  const float l_o = mlx[qgrp][1][n];
-  const float m_new = fmaxf(m_run, m_o);  // m_run is finite: block 0 holds a visible key
-  const float ae = __builtin_amdgcn_exp2f(m_run - m_new);
-  const float ao = __builtin_amdgcn_exp2f(m_o - m_new);  // 0 if the odd wave saw no key
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const f32x4 x = *slot(4 * t + jj);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[t][4 * jj + e] = ae * o[t][4 * jj + e] + ao * x[e];
-    }
-  // an expired wait leaves this row's partial NaN (m), besides the status word
-  store_partial_f16(o, expired ? __builtin_nanf("") : m_new, ae * l_tot + ao * l_o, qgrp, lane, po_all, pm, pl, pe,
-                    part);
-}
 
 }  // namespace ax

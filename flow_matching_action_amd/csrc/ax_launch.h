@@ -35,18 +35,19 @@ struct AttnPlan {
 };
 
 AttnPlan attn_plan(int S, int Smax);     // bf16 cache
-AttnPlan attn_plan_f8(int S, int Smax);  // fp8 cache (longer splits: a block is half the bytes)
+AttnPlan attn_plan_f8(int S, int Smax);  // fp8 cache (longer key ranges: a block is half the bytes)
 
 // Polls a bounded in-workgroup wait makes before it gives up: the default (about 30 ms of
 // polling), or the value set through ax_debug_set_wait_limit.
 constexpr int kDefaultWaitLimit = 1 << 20;
 int wait_limit();
 
-// bf16 partials inside the workspace, after the status word (the first 256 bytes), per (kv head
-// g, key range c) = part g * n_split + c: O in float16, scaled by 2^-e per (row, 32-column quarter
-// dt), in 2 KB groups (part, q head parity hp, row tile T, dt) of 64 lanes x 32 bytes (lane (n, h):
-// row 64 hp + 32 T + n, columns 32 dt + 8 q + 4 h .. +3 at byte 32 lane + 8 q); then one 16-byte
-// record per (part, folded row): float m, float l, int16 e[4]. Both regions 256-byte aligned.
+// Partials inside the workspace (both cache formats), after the status word (the first 256
+// bytes), per (kv head g, key range c) = part g * n_split + c: O in float16, scaled by 2^-e per
+// (row, 32-column quarter qd), in 1 KB groups (part, q head parity hp, row tile T, qd), each the
+// quarter's 16 rows row-major (row 64 hp + 16 T + j at byte 64 j, its column 32 qd + x at
+// 64 j + 2 x); then one 16-byte record per (part, folded row): float m, float l, int16 e[4].
+// Both regions 256-byte aligned.
 struct PartRec {
   float m;
   float l;
@@ -61,18 +62,8 @@ struct WsLayout {
 size_t attn_partials_bytes(const AttnPlan& p);
 WsLayout ws_layout(const AttnPlan& plan, const void* ws);
 
-// fp8-cache partials, after the status word: O [8][n_split][4][16][64] groups of 4 float16
-// (scaled by 2^-e per (split, row)), then m and l [8][n_split][128] float and e
-// [8][n_split][128] int, each 256-byte aligned.
-struct WsLayoutF8 {
-  int* status;
-  float* po;
-  float* pm;
-  float* pl;
-  int* pe;
-};
+// fp8-cache partials: the same layout as the bf16 cache's
 size_t attn_partials_bytes_f8(const AttnPlan& p);
-WsLayoutF8 ws_layout_f8(const AttnPlan& plan, const void* ws);
 
 struct AttnLaunch {
   const uint16_t* q;       // [16][64][128] (== folded [8][128][128]): raw if q_norm, else roped
