@@ -259,8 +259,8 @@ int ax_cache_tail_write_fp8(const uint16_t* k_roped, const uint16_t* v, uint8_t*
  * softmax weights before they are rounded to bf16; value scales from the
  * float32 denormals up to 2^25 keep those products in bf16's normal range.
  * ws: at least ax_expert_attn_fp8_workspace_bytes(S, Smax) bytes, 256-byte
- * aligned (the status word, then partials as for the bf16 cache with one
- * power-of-two scale per row).
+ * aligned (the status word, then partials in the bf16 cache's layout, with
+ * longer key ranges).
  */
 int ax_expert_attn_fp8(const uint16_t* q_roped, const uint16_t* k_own, const uint16_t* v_own,
                        uint8_t* Kc8, float* Ks, uint8_t* Vc8, float* Vs, int S, int Smax,
