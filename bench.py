@@ -265,7 +265,7 @@ class RotatingWorkloadF8:
 # unchanged since the counters were taken.
 KERNEL_SOURCES = {
     "bf16": ("ax_attn.hip", "ax_attn_common.h", "ax_dev.h"),
-    "fp8": ("ax_attn_f8.hip", "ax_attn_common.h", "ax_dev.h"),
+    "fp8": ("ax_attn.hip", "ax_attn_common.h", "ax_dev.h"),
     "decode": ("ax_decode.hip", "ax_attn_common.h", "ax_dev.h"),
     "layer": ("ax_layer.hip", "ax_attn.hip", "ax_attn_common.h", "ax_dev.h"),
 }
@@ -525,7 +525,8 @@ def main() -> int:
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(b8_attn / (us8_attn * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                          "traffic": load_traffic("fp8"),
-                         "kernel": "k_attn_f8 (q/k norm + RoPE + quantised tail write + split attention)",
+                         "kernel": "k_attn_split, fp8 instantiation (q/k norm + RoPE + quantised tail write + split "
+                                   "attention), one launch per step; the step adds k_attn_combine",
                          "kernel_us_per_launch": round(us8_attn, 3),
                          "algorithmic_bytes_per_launch": b8_attn,
                          "algorithmic_flops_per_launch": f8,
