@@ -582,7 +582,7 @@ def main() -> int:
             "roofline": {"bound": "hbm", "achieved": round(bl / (usl * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(bl / (usl * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                          "traffic": load_traffic("layer"),
-                         "kernel": "the whole layer (eleven launches)",
+                         "kernel": "the whole layer (nine launches)",
                          "algorithmic_bytes_per_layer": bl,
                          "algorithmic_flops_per_layer": algorithmic_flops_layer(S)},
             "replays_ms": [round(t, 4) for t in tl],

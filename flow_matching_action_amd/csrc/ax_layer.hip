@@ -10,16 +10,20 @@
 // - Weights are packed once (k_pack_w64) so that each 1 KB block holds, lane by lane, exactly the
 //   16-byte W^T operand a lane hands v_mfma_f32_32x32x16_bf16 for one (32-column block, 16-row
 //   step).
-// - k_gemm64: C[64, N] = A[64, K] W[K, N] for the 64 token rows. The weights are the stream
-//   (M = 64 is far below the ridge), so the grid is (N / (32 NB) column tiles) x (K / KC splits).
-//   Each wave loads its weight operands straight into registers (one plain 16-byte load per
-//   lane and step, non-temporal) while the workgroup's 64 x KC slice of A goes through LDS; the
-//   waves then run one 32 x 32 tile of C^T = W^T A^T each, the KW waves of a column block add
-//   their tiles through LDS, and the split's float32 partial goes to the workspace.
-// - k_gemm_reduce: sums the splits in a fixed order and applies the op's epilogue: the head
-//   split of qkv into q/k/v [heads][64][128], the residual add (o + x, d + x2), or SiLU(g) * u.
-// - k_rmsnorm_rows: one workgroup per token row; k_reduce_residual_norm: the o projection's
-//   split sum and residual add followed by the second norm, in one pass per row.
+// - The weights are the stream (M = 64 is far below the ridge). Each wave loads its weight
+//   operands straight into registers (one plain 16-byte load per lane and step, non-temporal)
+//   while the workgroup's slice of A goes through LDS, runs one 32 x 32 tile of C^T = W^T A^T per
+//   step, and the waves that split K inside the workgroup add their tiles through LDS.
+// - k_gemm32: one 32-row half of the tokens per workgroup, the two halves of a column tile on one
+//   XCD (the second weight read is an L2 hit). With all of K in the workgroup the epilogue runs in
+//   place: qkv's head split into q/k/v [heads][64][128], or SiLU(g) * u with the gate and up
+//   column blocks in the same workgroup, so no partial leaves it. The o projection takes it with
+//   2 splits of K and float32 partials.
+// - k_gemm64: all 64 rows per workgroup, K in splits with float32 partials (the down projection,
+//   whose 6144 rows of K do not fit one workgroup's LDS, and any other shape).
+// - k_gemm_reduce: sums the splits in a fixed order and applies the op's epilogue (plain store,
+//   or the residual add d + x2); k_reduce_residual_norm: the o projection's split sum and residual
+//   add followed by the second norm, in one pass per row; k_rmsnorm_rows: the first norm.
 #include "ax_attn_common.h"
 #include "ax_launch.h"
 
@@ -69,15 +73,12 @@ __device__ __forceinline__ int aswz(int c, int m) { return c ^ (m & 15); }
 // into registers (STEPS 1 KB loads per wave, all issued at the start and consumed in order), while
 // the split's 64 x KC slice of A sits in LDS (loaded first, from L2, through registers: a
 // direct-to-LDS load would make the compiler drain the whole weight stream before the first LDS
-// read). Each wave makes
-// C^T[32 n][64 m] with two matrix-core products per step (m halves); the KW waves of a column block
-// then add their tiles in LDS in kq order and the first stores the float32 partial. W0 holds
-// blocks [0, nblk0), W1 (if not null) the next nblk0, written to partial columns N .. 2N - 1.
-template <int NB, int KW, int STEPS, bool HEADS>
-__global__ __launch_bounds__(64 * NB * KW) void k_gemm64(const uint16_t* A, int lda, const uint16_t* W0,
-                                                       const uint16_t* W1, int K, int N, int n_tiles,
-                                                       float* part) {
-  constexpr int kThreads = 64 * NB * KW;
+// read). Each wave makes C^T[32 n][64 m] with two matrix-core products per step (m halves); the
+// KW waves of a column block then add their tiles in LDS in kq order and the first stores the
+// split's float32 partial, part[split][64][N]. A is row-major [64][K].
+template <int NB, int KW, int STEPS>
+__global__ __launch_bounds__(64 * NB * KW) void k_gemm64(const uint16_t* A, const uint16_t* W, int K, int N,
+                                                       int n_tiles, float* part) {
   constexpr int KC = KW * STEPS * 16;
   constexpr int kCpr = KC / 8;                     // 16-byte chunks per A row
   static_assert(kCpr % 16 == 0, "A rows of at least 16 chunks");
@@ -104,15 +105,12 @@ __global__ __launch_bounds__(64 * NB * KW) void k_gemm64(const uint16_t* A, int 
     const int e = 64 * (j * (NB * KW) + wave) + lane;
     const int m = e / kCpr;
     const int c = aswz(e % kCpr, m);
-    av[j] = *reinterpret_cast<const u32x4*>(a_elem(A, lda, m, k0 + 8 * c, HEADS));
+    av[j] = *reinterpret_cast<const u32x4*>(A + (long long)m * K + k0 + 8 * c);
   }
   __builtin_amdgcn_sched_barrier(0);
   // then every weight operand of this wave, from a wave-uniform base
-  const int nblk0 = W1 ? n_tiles * NB / 2 : n_tiles * NB;
-  const int jb = tile * NB + nb;  // column block over W0 then W1
-  const uint16_t* W = jb < nblk0 ? W0 : W1;
-  const int jl = jb < nblk0 ? jb : jb - nblk0;
-  const u32x4* wsrc = reinterpret_cast<const u32x4*>(W) + ((long long)jl * (K / 16) + k0 / 16 + kq * STEPS) * 64;
+  const int jb = tile * NB + nb;
+  const u32x4* wsrc = reinterpret_cast<const u32x4*>(W) + ((long long)jb * (K / 16) + k0 / 16 + kq * STEPS) * 64;
   u32x4 wv[STEPS];
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) wv[s] = __builtin_nontemporal_load(wsrc + s * 64 + lane);
@@ -167,11 +165,10 @@ __global__ __launch_bounds__(64 * NB * KW) void k_gemm64(const uint16_t* A, int 
         }
   }
   // lane (m = lane % 32, g = lane / 32) holds C rows 32 h + m, columns 32 jb + 8a + 4g + (0..3)
-  const int pld = W1 ? 2 * N : N;
   const int pcol = kNBlk * jb + 4 * (lane >> 5);
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    float* dst = part + ((long long)split * kGemmM + 32 * h + am0) * pld + pcol;
+    float* dst = part + ((long long)split * kGemmM + 32 * h + am0) * N + pcol;
 #pragma unroll
     for (int a = 0; a < 4; ++a)
       __builtin_nontemporal_store(f32x4{acc[h][4 * a], acc[h][4 * a + 1], acc[h][4 * a + 2], acc[h][4 * a + 3]},
@@ -179,91 +176,197 @@ __global__ __launch_bounds__(64 * NB * KW) void k_gemm64(const uint16_t* A, int 
   }
 }
 
-enum GemmEpilogue { kEpiStore = 0, kEpiQkvSplit = 1, kEpiResidual = 2, kEpiSwiGlu = 3 };
+enum GemmEpilogue { kEpiStore = 0, kEpiQkvSplit = 1, kEpiResidual = 2, kEpiSwiGlu = 3, kEpiPartial = 4 };
 
-// Sum of the splits of C[64, N], then the epilogue. A workgroup covers one row and 256 columns: thread (g, q) sums splits g, g + 4, ... of columns 4q .. 4q + 3 (eight loads in
-// flight), and group 0 adds the four group sums in group order, so the result does not depend on
-// timing. kEpiStore: out[m][n] = bf16(C); kEpiQkvSplit: bf16(C) into q / k / v [heads][64][128]
-// (columns 0..2047 q heads, 2048..3071 k heads, 3072..4095 v heads); kEpiResidual: out =
-// bf16(res + bf16(C)); kEpiSwiGlu: partial columns n and N + n are x w1 and x w3, out =
-// bf16(bf16(silu(C1)) * bf16(C3)).
+// One 32-row half of C = A W over the whole of K, with the op's epilogue applied in place, so no
+// float32 partial leaves the workgroup. The workgroup has NB x KW waves; wave (nb, kq) streams
+// column block nb over rows 16 STEPS kq .. 16 STEPS (kq + 1) of K straight into registers (a ring
+// of D 1 KB loads in flight, D = STEPS: all at once) while the half's 32 x K slice of A goes
+// through LDS (as in k_gemm64), and makes one 32 x 32 tile C^T[32 n][32 m] per step. The KW
+// tiles of a column block are then added in kq order through LDS; epilogue item (p, a) (column
+// block or block pair p, columns 8a .. 8a + 7 of it) goes to wave 4p + a.
+// Grid: 16 ids per 8 column tiles, the two halves of a tile 8 ids apart, so both run on one XCD
+// and the second read of the tile's weights is an L2 hit.
+// kEpiQkvSplit: column blocks NB t .. NB t + NB - 1 of W0, bf16(C) into q / k / v
+// [heads][64][128].
+// kEpiSwiGlu: blocks (NB / 2) t + p of W0 (x w1, waves nb = p) and of W1 (x w3, nb = NB / 2 + p),
+// out[m][32 j + c] = bf16(bf16(silu(C1)) * bf16(C3)), the same arithmetic as k_gemm_reduce's
+// SwiGLU epilogue.
+// kEpiPartial: K is cut into n_split splits of KC = 16 KW STEPS rows (blockIdx / (2 n_tiles) is the
+// split); the split's float32 C goes to part[split][64][N] for k_gemm_reduce.
+// HEADS: A is the attention output [16][64][128] read as [64][2048] (a_elem).
+template <int NB, int KW, int STEPS, int EPI, bool HEADS, int D = STEPS>
+__global__ __launch_bounds__(64 * NB * KW) void k_gemm32(const uint16_t* A, const uint16_t* W0, const uint16_t* W1,
+                                                       int N, uint16_t* out, uint16_t* out_k, uint16_t* out_v,
+                                                       int Ktot, float* part) {
+  static_assert(EPI == kEpiQkvSplit || EPI == kEpiSwiGlu || EPI == kEpiPartial, "k_gemm32 epilogue");
+  constexpr bool kPairs = EPI == kEpiSwiGlu;
+  static_assert(!kPairs || NB % 2 == 0, "SwiGLU takes column blocks in pairs");
+  constexpr int kWaves = NB * KW;
+  constexpr int kHalf = kPairs ? NB / 2 : NB;  // column blocks of W0 per tile
+  constexpr int kItems = 4 * kHalf;
+  static_assert(kItems <= kWaves, "one epilogue item per wave");
+  static_assert(D >= 1 && D <= STEPS, "ring depth");
+  constexpr int K = KW * STEPS * 16;                // rows of K per workgroup (all of K unless kEpiPartial)
+  constexpr int kCpr = K / 8;                       // 16-byte chunks per A row
+  static_assert(kCpr % 16 == 0, "A rows of at least 16 chunks");
+  constexpr int kALoads = 32 * kCpr / 64;           // 1 KB loads of the A half
+  static_assert(kALoads % kWaves == 0, "A half split evenly over the waves");
+  constexpr int kRedBytes = kWaves * 4 * 64 * 16;  // every wave's tile, 16 floats per lane
+  constexpr int kLds = 32 * K * 2 > kRedBytes ? 32 * K * 2 : kRedBytes;
+  static_assert(kLds <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int nb = wave % NB;
+  const int kq = wave / NB;
+  const int n_tiles = N / (kNBlk * kHalf);
+  const int split = EPI == kEpiPartial ? blockIdx.x / (2 * n_tiles) : 0;
+  const int b = EPI == kEpiPartial ? blockIdx.x % (2 * n_tiles) : blockIdx.x;
+  const int tile = (b >> 4) * 8 + (b & 7);
+  const int mh = (b >> 3) & 1;
+  const int lda = EPI == kEpiPartial ? Ktot : K;
+  const int k0 = split * K;
+
+  constexpr int kAPer = kALoads / kWaves;
+  u32x4 av[kAPer];
+#pragma unroll
+  for (int j = 0; j < kAPer; ++j) {
+    const int e = 64 * (j * kWaves + wave) + lane;
+    const int m = e / kCpr;
+    const int c = aswz(e % kCpr, m);
+    av[j] = *reinterpret_cast<const u32x4*>(a_elem(A, lda, 32 * mh + m, k0 + 8 * c, HEADS));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const uint16_t* W = (kPairs && nb >= kHalf) ? W1 : W0;
+  const int jb = tile * kHalf + nb % kHalf;
+  const u32x4* wsrc =
+      reinterpret_cast<const u32x4*>(W) + ((long long)jb * (lda / 16) + k0 / 16 + kq * STEPS) * 64;
+  u32x4 wv[D];
+#pragma unroll
+  for (int s = 0; s < D; ++s) wv[s] = __builtin_nontemporal_load(wsrc + s * 64 + lane);
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4* alds = reinterpret_cast<u32x4*>(lds);
+#pragma unroll
+  for (int j = 0; j < kAPer; ++j) alds[64 * (j * kWaves + wave) + lane] = av[j];
+  __syncthreads();
+
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  const int am0 = lane & 31;
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+    const int c = 2 * (kq * STEPS + s) + (lane >> 5);
+    bf16x8 wf;
+    __builtin_memcpy(&wf, &wv[s % D], 16);
+    const bf16x8 af = *reinterpret_cast<const bf16x8*>(lds + am0 * (K * 2) + 16 * aswz(c, am0));
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, af, acc, 0, 0, 0);
+    if (s + D < STEPS) wv[s % D] = __builtin_nontemporal_load(wsrc + (s + D) * 64 + lane);
+  }
+
+  __syncthreads();  // every wave is done with the A half; its LDS now holds the tiles
+  f32x4* red = reinterpret_cast<f32x4*>(lds);
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+    red[(wave * 4 + a) * 64 + lane] = f32x4{acc[4 * a], acc[4 * a + 1], acc[4 * a + 2], acc[4 * a + 3]};
+  __syncthreads();
+  if (wave >= kItems) return;
+  const int a = wave & 3, pi = wave >> 2;
+  // lane (m = lane % 32, g = lane / 32) sums C rows 32 mh + m, columns 32 j + 8a + 4g + (0..3) of
+  // column block pi (and, for SwiGLU, of its partner NB / 2 + pi)
+  constexpr int kSets = kPairs ? 2 : 1;
+  f32x4 sv[kSets];
+#pragma unroll
+  for (int n = 0; n < kSets; ++n) {
+    const int bn = pi + n * kHalf;
+    sv[n] = red[(bn * 4 + a) * 64 + lane];
+#pragma unroll
+    for (int q = 1; q < KW; ++q) {
+      const f32x4 v = red[((q * NB + bn) * 4 + a) * 64 + lane];
+      sv[n][0] += v[0]; sv[n][1] += v[1]; sv[n][2] += v[2]; sv[n][3] += v[3];
+    }
+  }
+  const int m = 32 * mh + am0;
+  const int col = kNBlk * (tile * kHalf + pi) + 8 * a + 4 * (lane >> 5);
+  if constexpr (EPI == kEpiPartial) {
+    __builtin_nontemporal_store(sv[0], reinterpret_cast<f32x4*>(part + ((long long)split * kGemmM + m) * N + col));
+    return;
+  }
+  float r[4];
+  uint16_t* dst;
+  if constexpr (EPI == kEpiSwiGlu) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float gv = bf16_to_f32(f32_to_bf16(sv[0][e] / (1.0f + __expf(-sv[0][e]))));
+      const float uv = bf16_to_f32(f32_to_bf16(sv[1][e]));
+      r[e] = gv * uv;
+    }
+    dst = out + (long long)m * N + col;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = sv[0][e];
+    const int head = col >> 7, d = col & 127;
+    uint16_t* base = head < kHq ? out : head < kHq + kHkv ? out_k : out_v;
+    const int hh = head < kHq ? head : head < kHq + kHkv ? head - kHq : head - kHq - kHkv;
+    dst = base + ((long long)hh * kGemmM + m) * 128 + d;
+  }
+  *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
+}
+
+// Sum of the splits of C[64, N], then the epilogue. A workgroup covers one row and 256 columns:
+// thread (g, q) sums splits g, g + 4, ... of columns 4q .. 4q + 3 (eight loads in flight), and
+// group 0 adds the four group sums in group order, so the result does not depend on timing.
+// kEpiStore: out[m][n] = bf16(C); kEpiResidual: out = bf16(res + bf16(C)).
 constexpr int kRedGroups = 4, kRedBatch = 8;
 
-__device__ __forceinline__ f32x4 split_sum(const f32x4* p, long long stride, int g, int n_split) {
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_reduce(const float* part, int n_split, int N, const uint16_t* res,
+                                                     uint16_t* out) {
+  static_assert(EPI == kEpiStore || EPI == kEpiResidual, "reduce epilogue");
+  __shared__ f32x4 red[kRedGroups - 1][64];
+  const int g = threadIdx.x >> 6;
+  const int q = threadIdx.x & 63;
+  const int m = blockIdx.x % kGemmM;
+  const int n = (blockIdx.x / kGemmM) * 256 + 4 * q;
+  const long long stride = (long long)kGemmM * N / 4;  // float4s per split
+  const bool live = n < N;  // the last block of a width that is not a multiple of 256
+  const f32x4* p = reinterpret_cast<const f32x4*>(part + (long long)m * N + (live ? n : 0));
+  const int ns = live ? n_split : 0;
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = g; c0 < n_split; c0 += kRedGroups * kRedBatch) {
+  for (int c0 = g; c0 < ns; c0 += kRedGroups * kRedBatch) {
     f32x4 v[kRedBatch];
 #pragma unroll
     for (int b = 0; b < kRedBatch; ++b) {
       const int c = c0 + kRedGroups * b;
-      v[b] = c < n_split ? p[c * stride] : f32x4{0.f, 0.f, 0.f, 0.f};
+      v[b] = c < ns ? p[c * stride] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int b = 0; b < kRedBatch; ++b) {
       s[0] += v[b][0]; s[1] += v[b][1]; s[2] += v[b][2]; s[3] += v[b][3];
     }
   }
-  return s;
-}
-
-template <int EPI>
-__global__ __launch_bounds__(256) void k_gemm_reduce(const float* part, int n_split, int N, const uint16_t* res,
-                                                     uint16_t* out, uint16_t* out_k, uint16_t* out_v) {
-  constexpr int kSets = EPI == kEpiSwiGlu ? 2 : 1;
-  __shared__ f32x4 red[kSets][kRedGroups - 1][64];
-  const int g = threadIdx.x >> 6;
-  const int q = threadIdx.x & 63;
-  const int m = blockIdx.x % kGemmM;
-  const int n = (blockIdx.x / kGemmM) * 256 + 4 * q;
-  const int pld = kSets * N;
-  const long long stride = (long long)kGemmM * pld / 4;  // float4s per split
-  const bool live = n < N;  // the last block of a width that is not a multiple of 256
-  const f32x4* p = reinterpret_cast<const f32x4*>(part + (long long)m * pld + (live ? n : 0));
-  f32x4 s[kSets];
-  s[0] = split_sum(p, stride, g, live ? n_split : 0);
-  if constexpr (kSets == 2) s[1] = split_sum(p + N / 4, stride, g, live ? n_split : 0);
-  if (g > 0) {
-#pragma unroll
-    for (int j = 0; j < kSets; ++j) red[j][g - 1][q] = s[j];
-  }
+  if (g > 0) red[g - 1][q] = s;
   __syncthreads();
   if (g > 0 || !live) return;
 #pragma unroll
-  for (int j = 0; j < kSets; ++j)
-#pragma unroll
-    for (int k = 0; k < kRedGroups - 1; ++k) {
-      const f32x4 v = red[j][k][q];
-      s[j][0] += v[0]; s[j][1] += v[1]; s[j][2] += v[2]; s[j][3] += v[3];
-    }
+  for (int k = 0; k < kRedGroups - 1; ++k) {
+    const f32x4 v = red[k][q];
+    s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
+  }
   float r[4];
-  if constexpr (EPI == kEpiSwiGlu) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float gv = bf16_to_f32(f32_to_bf16(s[0][e] / (1.0f + __expf(-s[0][e]))));
-      const float uv = bf16_to_f32(f32_to_bf16(s[1][e]));
-      r[e] = gv * uv;
-    }
-  } else if constexpr (EPI == kEpiResidual) {
+  if constexpr (EPI == kEpiResidual) {
     const uint2 rr = *reinterpret_cast<const uint2*>(res + (long long)m * N + n);
     const float x[4] = {bf16_to_f32(rr.x & 0xffffu), bf16_to_f32(rr.x >> 16), bf16_to_f32(rr.y & 0xffffu),
                         bf16_to_f32(rr.y >> 16)};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] = x[e] + bf16_to_f32(f32_to_bf16(s[0][e]));
+    for (int e = 0; e < 4; ++e) r[e] = x[e] + bf16_to_f32(f32_to_bf16(s[e]));
   } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] = s[0][e];
+    for (int e = 0; e < 4; ++e) r[e] = s[e];
   }
-  const uint2 o2 = make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
-  uint16_t* dst;
-  if constexpr (EPI == kEpiQkvSplit) {
-    const int head = n >> 7, d = n & 127;
-    uint16_t* base = head < kHq ? out : head < kHq + kHkv ? out_k : out_v;
-    const int hh = head < kHq ? head : head < kHq + kHkv ? head - kHq : head - kHq - kHkv;
-    dst = base + ((long long)hh * kGemmM + m) * 128 + d;
-  } else {
-    dst = out + (long long)m * N + n;
-  }
-  *reinterpret_cast<uint2*>(dst) = o2;
+  *reinterpret_cast<uint2*>(out + (long long)m * N + n) = make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
 }
 
 // Residual RMSNorm: out[m] = bf16(gamma * x[m] / sqrt(mean(x[m]^2) + eps)), one workgroup per row,
@@ -350,12 +453,23 @@ __global__ __launch_bounds__(256) void k_reduce_residual_norm(const float* part,
 // Projection shapes. A configuration is (NB column blocks, KW waves along k, STEPS 16-row steps per
 // wave); a split then covers KC = 16 KW STEPS rows and the grid is (N / (32 NB)) x (K / KC).
 struct GemmCfg {
-  int nb, kw, steps;
+  int nb, kw, steps, depth = 0;  // depth: weight loads in flight per wave (k_gemm32; 0 = all)
 };
 // the layer's four projections, each the fastest of a sweep over configurations on the cold-weight
 // workload: qkv 64 x 4 = 256 workgroups of 2 waves, o 48 x 4 = 192 of 4, gate/up 96 x 2 = 192 of 8,
 // down 24 x 8 = 192 of 4
-constexpr GemmCfg kCfgQkv{2, 1, 24}, kCfgO{1, 4, 8}, kCfgGateUp{4, 2, 24}, kCfgDown{2, 2, 24};
+constexpr GemmCfg kCfgDown{2, 2, 24};
+constexpr int kDownSplits = kLayerMlp / (16 * kCfgDown.kw * kCfgDown.steps);
+// the o projection in the 32-row form with 2 splits of K (2 x 48 x 2 = 192 workgroups of 8 waves)
+constexpr GemmCfg kCfgO32{1, 8, 8, 8};
+constexpr int kOSplits = kHq * 128 / (16 * kCfgO32.kw * kCfgO32.steps);
+// qkv and gate/up take the whole of K per 32-row half (k_gemm32): qkv 2 x 128 = 256 workgroups,
+// gate/up 2 x 192 = 384
+constexpr GemmCfg kCfgQkv32{1, 8, 12, 12}, kCfgGateUp32{4, 2, 48, 16};
+static_assert(16 * kCfgQkv32.kw * kCfgQkv32.steps == kLayerHidden, "qkv takes the whole of K");
+static_assert(16 * kCfgGateUp32.kw * kCfgGateUp32.steps == kLayerHidden, "gate/up take the whole of K");
+static_assert((kLayerQkv / kNBlk / kCfgQkv32.nb) % 8 == 0 && (kLayerMlp / kNBlk / (kCfgGateUp32.nb / 2)) % 8 == 0,
+              "tiles in groups of 8");
 // any other shape: 4 waves along k over one column block, the most rows per wave that still gives
 // 256 workgroups (else the fewest)
 static GemmCfg gemm_cfg_generic(int K, int N) {
@@ -377,13 +491,12 @@ size_t gemm64_partials_bytes(int K, int N) {
   return (size_t)gemm_splits(c, K) * kGemmM * N * 4;
 }
 
-template <int NB, int KW, int STEPS, bool HEADS>
-static void launch_gemm_cfg(const uint16_t* A, int lda, const uint16_t* W0, const uint16_t* W1, int K, int N,
-                            float* part, hipStream_t st) {
-  const int tiles = (W1 ? 2 : 1) * (N / kNBlk) / NB;
+template <int NB, int KW, int STEPS>
+static void launch_gemm_cfg(const uint16_t* A, const uint16_t* W, int K, int N, float* part, hipStream_t st) {
+  const int tiles = (N / kNBlk) / NB;
   const int splits = K / (16 * KW * STEPS);
-  hipLaunchKernelGGL((k_gemm64<NB, KW, STEPS, HEADS>), dim3(tiles * splits), dim3(64 * NB * KW), 0, st, A, lda, W0,
-                     W1, K, N, tiles, part);
+  hipLaunchKernelGGL((k_gemm64<NB, KW, STEPS>), dim3(tiles * splits), dim3(64 * NB * KW), 0, st, A, W, K, N, tiles,
+                     part);
 }
 
 static hipError_t launch_gemm_generic(const uint16_t* A, const uint16_t* W, int K, int N, float* part,
@@ -391,11 +504,11 @@ static hipError_t launch_gemm_generic(const uint16_t* A, const uint16_t* W, int 
   const GemmCfg c = gemm_cfg_generic(K, N);
   *n_split = gemm_splits(c, K);
   switch (c.steps) {
-    case 12: launch_gemm_cfg<1, 4, 12, false>(A, K, W, nullptr, K, N, part, st); break;
-    case 8: launch_gemm_cfg<1, 4, 8, false>(A, K, W, nullptr, K, N, part, st); break;
-    case 6: launch_gemm_cfg<1, 4, 6, false>(A, K, W, nullptr, K, N, part, st); break;
-    case 4: launch_gemm_cfg<1, 4, 4, false>(A, K, W, nullptr, K, N, part, st); break;
-    case 2: launch_gemm_cfg<1, 4, 2, false>(A, K, W, nullptr, K, N, part, st); break;
+    case 12: launch_gemm_cfg<1, 4, 12>(A, W, K, N, part, st); break;
+    case 8: launch_gemm_cfg<1, 4, 8>(A, W, K, N, part, st); break;
+    case 6: launch_gemm_cfg<1, 4, 6>(A, W, K, N, part, st); break;
+    case 4: launch_gemm_cfg<1, 4, 4>(A, W, K, N, part, st); break;
+    case 2: launch_gemm_cfg<1, 4, 2>(A, W, K, N, part, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -403,9 +516,9 @@ static hipError_t launch_gemm_generic(const uint16_t* A, const uint16_t* W, int 
 
 template <int EPI>
 static hipError_t launch_reduce(const float* part, int n_split, int N, const uint16_t* res, uint16_t* out,
-                                uint16_t* out_k, uint16_t* out_v, hipStream_t st) {
-  hipLaunchKernelGGL((k_gemm_reduce<EPI>), dim3(kGemmM * ((N + 255) / 256)), dim3(256), 0, st, part, n_split, N, res, out,
-                     out_k, out_v);
+                                hipStream_t st) {
+  hipLaunchKernelGGL((k_gemm_reduce<EPI>), dim3(kGemmM * ((N + 255) / 256)), dim3(256), 0, st, part, n_split, N, res,
+                     out);
   return hipGetLastError();
 }
 
@@ -420,7 +533,7 @@ hipError_t launch_linear64(const uint16_t* A, const uint16_t* W, int K, int N, u
   int ns = 0;
   hipError_t e = launch_gemm_generic(A, W, K, N, static_cast<float*>(ws), st, &ns);
   if (e != hipSuccess) return e;
-  return launch_reduce<kEpiStore>(static_cast<float*>(ws), ns, N, nullptr, C, nullptr, nullptr, st);
+  return launch_reduce<kEpiStore>(static_cast<float*>(ws), ns, N, nullptr, C, st);
 }
 
 // Layer workspace: activations, then the attention workspace, then the GEMM partials (the
@@ -450,12 +563,9 @@ static size_t layer_ws_layout(const AttnPlan& plan, void* ws, LayerWs* l) {
   uint16_t* x2 = reinterpret_cast<uint16_t*>(take(act));
   uint16_t* n2 = reinterpret_cast<uint16_t*>(take(act));
   uint16_t* mlp = reinterpret_cast<uint16_t*>(take((size_t)kGemmM * kLayerMlp * 2));
-  // float32 partials of the largest projection (gate and up share one launch: rows of 2 x 6144)
+  // float32 partials of the larger split projection (qkv and gate/up leave none)
   size_t pmax = 0;
-  for (size_t b : {(size_t)gemm_splits(kCfgQkv, kLayerHidden) * kGemmM * kLayerQkv * 4,
-                   (size_t)gemm_splits(kCfgO, kHq * 128) * kGemmM * kLayerHidden * 4,
-                   (size_t)gemm_splits(kCfgGateUp, kLayerHidden) * kGemmM * 2 * kLayerMlp * 4,
-                   (size_t)gemm_splits(kCfgDown, kLayerMlp) * kGemmM * kLayerHidden * 4})
+  for (size_t b : {(size_t)kOSplits * kGemmM * kLayerHidden * 4, (size_t)kDownSplits * kGemmM * kLayerHidden * 4})
     pmax = b > pmax ? b : pmax;
   float* part = reinterpret_cast<float*>(take(pmax));
   if (l) *l = LayerWs{n1, q, k, v, attn, x2, n2, mlp, attn_ws, part};
@@ -469,7 +579,6 @@ hipError_t launch_layer(const LayerLaunch& p, hipStream_t st) {
   LayerWs l;
   layer_ws_layout(plan, p.ws, &l);
   hipError_t e;
-  int ns = 0;
 #define AX_TRY(x)                \
   do {                           \
     e = (x);                     \
@@ -478,31 +587,28 @@ hipError_t launch_layer(const LayerLaunch& p, hipStream_t st) {
   hipLaunchKernelGGL(k_rmsnorm_rows, dim3(kGemmM), dim3(kLayerHidden / 8), 0, st, p.x, p.ln1, p.eps, kLayerHidden,
                      l.n1);
   AX_TRY(hipGetLastError());
-  launch_gemm_cfg<kCfgQkv.nb, kCfgQkv.kw, kCfgQkv.steps, false>(l.n1, kLayerHidden, p.wqkv, nullptr, kLayerHidden,
-                                                                kLayerQkv, l.part, st);
+  hipLaunchKernelGGL((k_gemm32<kCfgQkv32.nb, kCfgQkv32.kw, kCfgQkv32.steps, kEpiQkvSplit, false, kCfgQkv32.depth>),
+                     dim3(2 * kLayerQkv / kNBlk / kCfgQkv32.nb), dim3(64 * kCfgQkv32.nb * kCfgQkv32.kw), 0, st, l.n1,
+                     p.wqkv, nullptr, kLayerQkv, l.q, l.k, l.v, kLayerHidden, nullptr);
   AX_TRY(hipGetLastError());
-  AX_TRY(launch_reduce<kEpiQkvSplit>(l.part, gemm_splits(kCfgQkv, kLayerHidden), kLayerQkv, nullptr, l.q, l.k, l.v,
-                                     st));
   AttnLaunch a{l.q, p.qn, p.kn, p.cos_t, p.sin_t, p.eps, l.k, l.v, p.Kc, p.Vc, l.attn, l.attn_ws, p.S, p.Smax,
                /*q_norm=*/1};
   AX_TRY(launch_attn(plan, a, st));
-  launch_gemm_cfg<kCfgO.nb, kCfgO.kw, kCfgO.steps, true>(l.attn, 0, p.wo, nullptr, kHq * 128, kLayerHidden, l.part,
-                                                         st);
+  hipLaunchKernelGGL((k_gemm32<kCfgO32.nb, kCfgO32.kw, kCfgO32.steps, kEpiPartial, true, kCfgO32.depth>),
+                     dim3(2 * kLayerHidden / kNBlk / kCfgO32.nb * kOSplits), dim3(64 * kCfgO32.nb * kCfgO32.kw), 0, st,
+                     l.attn, p.wo, nullptr, kLayerHidden, nullptr, nullptr, nullptr, kHq * 128, l.part);
   AX_TRY(hipGetLastError());
-  static_assert(kHq * 128 / (16 * kCfgO.kw * kCfgO.steps) == 4, "o projection splits");
-  hipLaunchKernelGGL(k_reduce_residual_norm<4>, dim3(kGemmM), dim3(kLayerHidden / 8), 0, st, l.part, p.x, p.ln2,
-                     p.eps, kLayerHidden, l.x2, l.n2);
+  hipLaunchKernelGGL(k_reduce_residual_norm<kOSplits>, dim3(kGemmM), dim3(kLayerHidden / 8), 0, st, l.part, p.x,
+                     p.ln2, p.eps, kLayerHidden, l.x2, l.n2);
   AX_TRY(hipGetLastError());
-  launch_gemm_cfg<kCfgGateUp.nb, kCfgGateUp.kw, kCfgGateUp.steps, false>(l.n2, kLayerHidden, p.w1, p.w3,
-                                                                         kLayerHidden, kLayerMlp, l.part, st);
+  hipLaunchKernelGGL((k_gemm32<kCfgGateUp32.nb, kCfgGateUp32.kw, kCfgGateUp32.steps, kEpiSwiGlu, false,
+                               kCfgGateUp32.depth>),
+                     dim3(2 * kLayerMlp / kNBlk / (kCfgGateUp32.nb / 2)), dim3(64 * kCfgGateUp32.nb * kCfgGateUp32.kw), 0,
+                     st, l.n2, p.w1, p.w3, kLayerMlp, l.mlp, nullptr, nullptr, kLayerHidden, nullptr);
   AX_TRY(hipGetLastError());
-  AX_TRY(launch_reduce<kEpiSwiGlu>(l.part, gemm_splits(kCfgGateUp, kLayerHidden), kLayerMlp, nullptr, l.mlp, nullptr,
-                                   nullptr, st));
-  launch_gemm_cfg<kCfgDown.nb, kCfgDown.kw, kCfgDown.steps, false>(l.mlp, kLayerMlp, p.w2, nullptr, kLayerMlp,
-                                                                   kLayerHidden, l.part, st);
+  launch_gemm_cfg<kCfgDown.nb, kCfgDown.kw, kCfgDown.steps>(l.mlp, p.w2, kLayerMlp, kLayerHidden, l.part, st);
   AX_TRY(hipGetLastError());
-  AX_TRY(launch_reduce<kEpiResidual>(l.part, gemm_splits(kCfgDown, kLayerMlp), kLayerHidden, l.x2, p.x_out, nullptr,
-                                     nullptr, st));
+  AX_TRY(launch_reduce<kEpiResidual>(l.part, kDownSplits, kLayerHidden, l.x2, p.x_out, st));
 #undef AX_TRY
   return hipSuccess;
 }

@@ -326,7 +326,7 @@ int ax_text_decode_attn(const uint16_t* q_in, const uint16_t* k_in, const uint16
  * arithmetic is float32 (products of bf16 on the matrix cores). Updates the
  * cache tail like ax_expert_layer_attn. x_out must not alias x_in. ws: at least
  * ax_expert_layer_workspace_bytes(S, Smax) bytes, 256-byte aligned, starting
- * with the status word. Eleven launches.
+ * with the status word. Nine launches.
  */
 size_t ax_expert_layer_workspace_bytes(int S, int Smax);
 int ax_expert_layer(const uint16_t* x_in, const uint16_t* ln1, const uint16_t* wqkv,

@@ -278,7 +278,7 @@ def test_layer_benchmark_inputs_match_oracle(ax, layer):
 
 
 def test_layer_graph_replay_equals_eager(ax):
-    # the layer's eleven launches captured in one graph, replayed three times with eager work in
+    # the layer's nine launches captured in one graph, replayed three times with eager work in
     # between: every replay equals the eager result bit for bit
     S, Smax = 1000, 2048
     w = synth.layer_weights(41)
