@@ -95,6 +95,9 @@ lib.ax_expert_layer_workspace_bytes.restype = ctypes.c_size_t
 lib.ax_expert_layer_workspace_bytes.argtypes = [_I, _I]
 lib.ax_expert_layer.restype = _I
 lib.ax_expert_layer.argtypes = [_P] * 12 + [ctypes.c_float, _P, _P, _I, _I, _P, _P, ctypes.c_size_t, _P]
+lib.ax_expert_layer_chained.restype = _I
+lib.ax_expert_layer_chained.argtypes = [_P] * 13 + [ctypes.c_float, _P, _P, _I, _I, _P, _P, _P, _P, ctypes.c_size_t,
+                                                    _P]
 lib.ax_pack_weight_m64.restype = _I
 lib.ax_pack_weight_m64.argtypes = [_P, _I, _I, _P, _P]
 lib.ax_linear_m64_workspace_bytes.restype = ctypes.c_size_t
@@ -111,7 +114,7 @@ EXPORTS = ("ax_abi_version", "ax_strerror", "ax_debug_set_wait_limit", "ax_rope_
            "ax_expert_attn_fp8_workspace_bytes", "ax_cache_tail_write_fp8", "ax_expert_attn_fp8",
            "ax_expert_layer_attn_fp8", "ax_expert_layer_attn_fp8_split", "ax_expert_attn_fp8_combine",
            "ax_text_decode_workspace_bytes", "ax_text_decode_attn", "ax_expert_layer_workspace_bytes",
-           "ax_expert_layer", "ax_pack_weight_m64", "ax_linear_m64_workspace_bytes", "ax_linear_m64",
+           "ax_expert_layer", "ax_expert_layer_chained", "ax_pack_weight_m64", "ax_linear_m64_workspace_bytes", "ax_linear_m64",
            "ax_copy_words")
 
 
@@ -283,6 +286,14 @@ def expert_layer(x_in, ln1, wqkv, q_norm_w, k_norm_w, wo, ln2, w1, w3, w2, rope_
         _ptr(x_in), _ptr(ln1), _ptr(wqkv), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(wo), _ptr(ln2), _ptr(w1), _ptr(w3),
         _ptr(w2), _ptr(rope_cos), _ptr(rope_sin), float(eps), _ptr(Kc), _ptr(Vc), int(S), int(Smax), _ptr(x_out),
         _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def expert_layer_chained(x_in, n1_in, ln1, wqkv, q_norm_w, k_norm_w, wo, ln2, w1, w3, w2, rope_cos, rope_sin, eps,
+                         Kc, Vc, S: int, Smax: int, x_out, ln1_next, n1_out, ws, stream=None):
+    _check("ax_expert_layer_chained", lib.ax_expert_layer_chained(
+        _ptr(x_in), _ptr(n1_in), _ptr(ln1), _ptr(wqkv), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(wo), _ptr(ln2),
+        _ptr(w1), _ptr(w3), _ptr(w2), _ptr(rope_cos), _ptr(rope_sin), float(eps), _ptr(Kc), _ptr(Vc), int(S),
+        int(Smax), _ptr(x_out), _ptr(ln1_next), _ptr(n1_out), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def pack_weight_m64(W, K: int, N: int, W_packed, stream=None):

@@ -31,11 +31,11 @@ int check_device() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int check_ptrs(std::initializer_list<const void*> ps) {
+int check_ptrs(std::initializer_list<const void*> ps, bool allow_null = false) {
   for (const void* p : ps)
-    if (p == nullptr) return AX_E_NULL;
+    if (p == nullptr && !allow_null) return AX_E_NULL;
   for (const void* p : ps)
-    if (!aligned16(p)) return AX_E_ALIGN;
+    if (p != nullptr && !aligned16(p)) return AX_E_ALIGN;
   return AX_OK;
 }
 
@@ -399,6 +399,36 @@ int ax_expert_layer(const uint16_t* x_in, const uint16_t* ln1, const uint16_t* w
   if (r != AX_OK) return r;
   ax::LayerLaunch p{x_in, ln1, wqkv, q_norm_w, k_norm_w, wo, ln2, w1, w3, w2, rope_cos, rope_sin, eps, Kc, Vc, S, Smax,
                     x_out, ws};
+  return status(ax::launch_layer(p, as_stream(stream)));
+}
+
+static bool overlap(const void* a, const void* b, size_t n) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return a && b && (x < y ? y - x < n : x - y < n);
+}
+
+int ax_expert_layer_chained(const uint16_t* x_in, const uint16_t* n1_in, const uint16_t* ln1, const uint16_t* wqkv,
+                            const uint16_t* q_norm_w, const uint16_t* k_norm_w, const uint16_t* wo,
+                            const uint16_t* ln2, const uint16_t* w1, const uint16_t* w3, const uint16_t* w2,
+                            const float* rope_cos, const float* rope_sin, float eps, uint16_t* Kc, uint16_t* Vc,
+                            int S, int Smax, uint16_t* x_out, const uint16_t* ln1_next, uint16_t* n1_out, void* ws,
+                            size_t ws_bytes, void* stream) {
+  int r = check_ptrs({x_in, wqkv, q_norm_w, k_norm_w, wo, ln2, w1, w3, w2, rope_cos, rope_sin, Kc, Vc, x_out, ws});
+  if (r == AX_OK && n1_in == nullptr && ln1 == nullptr) r = AX_E_NULL;  // the first norm needs ln1
+  if (r == AX_OK && (ln1_next == nullptr) != (n1_out == nullptr)) r = AX_E_NULL;
+  if (r == AX_OK) r = check_ptrs({n1_in, ln1, ln1_next, n1_out}, /*allow_null=*/true);
+  if (r == AX_OK) r = check_shape(S, Smax);
+  if (r == AX_OK) r = check_eps(eps);
+  const size_t act = (size_t)AX_N_TOK * 1536 * 2;
+  if (r == AX_OK && (overlap(x_in, x_out, act) || overlap(n1_out, x_in, act) || overlap(n1_out, x_out, act) ||
+                     overlap(n1_out, n1_in, act)))
+    r = AX_E_ARG;
+  if (r == AX_OK && ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || ws_bytes < ax_expert_layer_workspace_bytes(S, Smax)))
+    r = AX_E_WORKSPACE;
+  if (r == AX_OK) r = check_device();
+  if (r != AX_OK) return r;
+  ax::LayerLaunch p{x_in, ln1, wqkv, q_norm_w, k_norm_w, wo, ln2, w1, w3, w2, rope_cos, rope_sin, eps, Kc, Vc, S, Smax,
+                    x_out, ws, n1_in, ln1_next, n1_out};
   return status(ax::launch_layer(p, as_stream(stream)));
 }
 

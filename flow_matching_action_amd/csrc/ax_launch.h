@@ -155,6 +155,12 @@ struct LayerLaunch {
   int S, Smax;
   uint16_t* x_out;        // [64][1536]
   void* ws;
+  // a chained layer: n1_in (if not null) is RMSNorm(x; ln1), made by the previous layer's last
+  // launch, and the first norm is skipped; with ln1_next, the last launch also writes n1_out =
+  // RMSNorm(x_out; ln1_next) for the next layer
+  const uint16_t* n1_in = nullptr;
+  const uint16_t* ln1_next = nullptr;
+  uint16_t* n1_out = nullptr;
 };
 size_t layer_workspace_bytes(int S, int Smax);
 hipError_t launch_layer(const LayerLaunch& p, hipStream_t st);

@@ -21,9 +21,9 @@
 //   2 splits of K and float32 partials.
 // - k_gemm64: all 64 rows per workgroup, K in splits with float32 partials (the down projection,
 //   whose 6144 rows of K do not fit one workgroup's LDS, and any other shape).
-// - k_gemm_reduce: sums the splits in a fixed order and applies the op's epilogue (plain store,
-//   or the residual add d + x2); k_reduce_residual_norm: the o projection's split sum and residual
-//   add followed by the second norm, in one pass per row; k_rmsnorm_rows: the first norm.
+// - k_reduce_residual_norm: a split sum, the residual add and the norm that follows, in one pass
+//   per row (o: x2 and n2; down: x_out and, for a chained layer, the next layer's first norm);
+//   k_rmsnorm_rows: the first norm; k_gemm_reduce: the plain split sum of a stand-alone product.
 #include "ax_attn_common.h"
 #include "ax_launch.h"
 
@@ -78,7 +78,7 @@ __device__ __forceinline__ int aswz(int c, int m) { return c ^ (m & 15); }
 // split's float32 partial, part[split][64][N]. A is row-major [64][K].
 template <int NB, int KW, int STEPS>
 __global__ __launch_bounds__(64 * NB * KW) void k_gemm64(const uint16_t* A, const uint16_t* W, int K, int N,
-                                                       int n_tiles, float* part) {
+                                                       float* part) {
   constexpr int KC = KW * STEPS * 16;
   constexpr int kCpr = KC / 8;                     // 16-byte chunks per A row
   static_assert(kCpr % 16 == 0, "A rows of at least 16 chunks");
@@ -92,8 +92,11 @@ __global__ __launch_bounds__(64 * NB * KW) void k_gemm64(const uint16_t* A, cons
   const int lane = tid & 63;
   const int nb = wave % NB;
   const int kq = wave / NB;
-  const int tile = blockIdx.x % n_tiles;
-  const int split = blockIdx.x / n_tiles;
+  // consecutive ids take consecutive splits, so (ids landing on XCD id % 8) an XCD holds the same
+  // splits of every column tile and reads only their slices of A
+  const int n_split = K / KC;
+  const int split = blockIdx.x % n_split;
+  const int tile = blockIdx.x / n_split;
   const int k0 = split * KC;
 
   // the A slice first (plain loads into registers; stored to LDS once the weight loads are out):
@@ -176,7 +179,7 @@ __global__ __launch_bounds__(64 * NB * KW) void k_gemm64(const uint16_t* A, cons
   }
 }
 
-enum GemmEpilogue { kEpiStore = 0, kEpiQkvSplit = 1, kEpiResidual = 2, kEpiSwiGlu = 3, kEpiPartial = 4 };
+enum GemmEpilogue { kEpiQkvSplit = 1, kEpiSwiGlu = 3, kEpiPartial = 4 };
 
 // One 32-row half of C = A W over the whole of K, with the op's epilogue applied in place, so no
 // float32 partial leaves the workgroup. The workgroup has NB x KW waves; wave (nb, kq) streams
@@ -318,13 +321,10 @@ __global__ __launch_bounds__(64 * NB * KW) void k_gemm32(const uint16_t* A, cons
 // Sum of the splits of C[64, N], then the epilogue. A workgroup covers one row and 256 columns:
 // thread (g, q) sums splits g, g + 4, ... of columns 4q .. 4q + 3 (eight loads in flight), and
 // group 0 adds the four group sums in group order, so the result does not depend on timing.
-// kEpiStore: out[m][n] = bf16(C); kEpiResidual: out = bf16(res + bf16(C)).
+// out[m][n] = bf16(C).
 constexpr int kRedGroups = 4, kRedBatch = 8;
 
-template <int EPI>
-__global__ __launch_bounds__(256) void k_gemm_reduce(const float* part, int n_split, int N, const uint16_t* res,
-                                                     uint16_t* out) {
-  static_assert(EPI == kEpiStore || EPI == kEpiResidual, "reduce epilogue");
+__global__ __launch_bounds__(256) void k_gemm_reduce(const float* part, int n_split, int N, uint16_t* out) {
   __shared__ f32x4 red[kRedGroups - 1][64];
   const int g = threadIdx.x >> 6;
   const int q = threadIdx.x & 63;
@@ -355,18 +355,7 @@ __global__ __launch_bounds__(256) void k_gemm_reduce(const float* part, int n_sp
     const f32x4 v = red[k][q];
     s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
   }
-  float r[4];
-  if constexpr (EPI == kEpiResidual) {
-    const uint2 rr = *reinterpret_cast<const uint2*>(res + (long long)m * N + n);
-    const float x[4] = {bf16_to_f32(rr.x & 0xffffu), bf16_to_f32(rr.x >> 16), bf16_to_f32(rr.y & 0xffffu),
-                        bf16_to_f32(rr.y >> 16)};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] = x[e] + bf16_to_f32(f32_to_bf16(s[e]));
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] = s[e];
-  }
-  *reinterpret_cast<uint2*>(out + (long long)m * N + n) = make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
+  *reinterpret_cast<uint2*>(out + (long long)m * N + n) = make_uint2(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]));
 }
 
 // Residual RMSNorm: out[m] = bf16(gamma * x[m] / sqrt(mean(x[m]^2) + eps)), one workgroup per row,
@@ -402,15 +391,17 @@ __global__ __launch_bounds__(256) void k_rmsnorm_rows(const uint16_t* x, const u
   *reinterpret_cast<u32x4*>(out + (long long)m * width + 8 * t) = pack8v(o);
 }
 
-// The o projection's epilogue and the second residual norm in one pass, one workgroup per row:
-// x2[m] = bf16(x[m] + bf16(sum of the splits of C[m])) and n2[m] = bf16(gamma * x2[m] /
-// sqrt(mean(x2[m]^2) + eps)) (the same arithmetic as k_gemm_reduce's residual epilogue followed by
-// k_rmsnorm_rows). 8 columns per thread, width = 8 x blockDim; all split loads of a thread are
-// issued before any is added.
+// A split sum, the residual add and the next norm in one pass, one workgroup per row:
+// y[m] = bf16(x[m] + bf16(sum of the splits of C[m])) and, if gamma is not null, n[m] =
+// bf16(gamma * y[m] / sqrt(mean(y[m]^2) + eps)), the same arithmetic and summation order as
+// k_rmsnorm_rows on y. Used for the o projection (y = x2, n = n2) and the down projection (y =
+// x_out, and for a chained layer n = the next layer's first norm). 8 columns per thread, width = 8
+// x blockDim; the splits are added in order 0, 1, ..., all loads of a thread issued before any is
+// added.
 template <int NSPLIT>
 __global__ __launch_bounds__(256) void k_reduce_residual_norm(const float* part, const uint16_t* x,
                                                               const uint16_t* gamma, float eps, int width,
-                                                              uint16_t* x2, uint16_t* n2) {
+                                                              uint16_t* y, uint16_t* n) {
   __shared__ float red[8];
   const int m = blockIdx.x;
   const int t = threadIdx.x;
@@ -423,19 +414,21 @@ __global__ __launch_bounds__(256) void k_reduce_residual_norm(const float* part,
     v[c][0] = p[c * stride];
     v[c][1] = p[c * stride + 1];
   }
-  float xr[8], g[8], o[8];
+  float xr[8], o[8];
   unpack8v(*reinterpret_cast<const u32x4*>(x + row), xr);
-  unpack8v(*reinterpret_cast<const u32x4*>(gamma + 8 * t), g);
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     float sum = v[0][e >> 2][e & 3];
 #pragma unroll
     for (int c = 1; c < NSPLIT; ++c) sum += v[c][e >> 2][e & 3];
-    o[e] = bf16_to_f32(f32_to_bf16(xr[e] + bf16_to_f32(f32_to_bf16(sum))));  // x2, as stored
+    o[e] = bf16_to_f32(f32_to_bf16(xr[e] + bf16_to_f32(f32_to_bf16(sum))));  // y, as stored
     ss += o[e] * o[e];
   }
-  *reinterpret_cast<u32x4*>(x2 + row) = pack8v(o);
+  *reinterpret_cast<u32x4*>(y + row) = pack8v(o);
+  if (gamma == nullptr) return;
+  float g[8];
+  unpack8v(*reinterpret_cast<const u32x4*>(gamma + 8 * t), g);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
   if ((t & 63) == 0) red[t >> 6] = ss;
@@ -445,7 +438,7 @@ __global__ __launch_bounds__(256) void k_reduce_residual_norm(const float* part,
   const float inv = 1.0f / sqrtf(tot / (float)width + eps);
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = o[e] * inv * g[e];
-  *reinterpret_cast<u32x4*>(n2 + row) = pack8v(o);
+  *reinterpret_cast<u32x4*>(n + row) = pack8v(o);
 }
 
 // ---- host side -----------------------------------------------------------------------------------
@@ -495,8 +488,7 @@ template <int NB, int KW, int STEPS>
 static void launch_gemm_cfg(const uint16_t* A, const uint16_t* W, int K, int N, float* part, hipStream_t st) {
   const int tiles = (N / kNBlk) / NB;
   const int splits = K / (16 * KW * STEPS);
-  hipLaunchKernelGGL((k_gemm64<NB, KW, STEPS>), dim3(tiles * splits), dim3(64 * NB * KW), 0, st, A, W, K, N, tiles,
-                     part);
+  hipLaunchKernelGGL((k_gemm64<NB, KW, STEPS>), dim3(tiles * splits), dim3(64 * NB * KW), 0, st, A, W, K, N, part);
 }
 
 static hipError_t launch_gemm_generic(const uint16_t* A, const uint16_t* W, int K, int N, float* part,
@@ -514,11 +506,8 @@ static hipError_t launch_gemm_generic(const uint16_t* A, const uint16_t* W, int 
   return hipGetLastError();
 }
 
-template <int EPI>
-static hipError_t launch_reduce(const float* part, int n_split, int N, const uint16_t* res, uint16_t* out,
-                                hipStream_t st) {
-  hipLaunchKernelGGL((k_gemm_reduce<EPI>), dim3(kGemmM * ((N + 255) / 256)), dim3(256), 0, st, part, n_split, N, res,
-                     out);
+static hipError_t launch_reduce(const float* part, int n_split, int N, uint16_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_gemm_reduce, dim3(kGemmM * ((N + 255) / 256)), dim3(256), 0, st, part, n_split, N, out);
   return hipGetLastError();
 }
 
@@ -533,7 +522,7 @@ hipError_t launch_linear64(const uint16_t* A, const uint16_t* W, int K, int N, u
   int ns = 0;
   hipError_t e = launch_gemm_generic(A, W, K, N, static_cast<float*>(ws), st, &ns);
   if (e != hipSuccess) return e;
-  return launch_reduce<kEpiStore>(static_cast<float*>(ws), ns, N, nullptr, C, st);
+  return launch_reduce(static_cast<float*>(ws), ns, N, C, st);
 }
 
 // Layer workspace: activations, then the attention workspace, then the GEMM partials (the
@@ -584,11 +573,16 @@ hipError_t launch_layer(const LayerLaunch& p, hipStream_t st) {
     e = (x);                     \
     if (e != hipSuccess) return e; \
   } while (0)
-  hipLaunchKernelGGL(k_rmsnorm_rows, dim3(kGemmM), dim3(kLayerHidden / 8), 0, st, p.x, p.ln1, p.eps, kLayerHidden,
-                     l.n1);
-  AX_TRY(hipGetLastError());
+  // the first norm, unless the previous layer's last launch made it (a chained layer)
+  const uint16_t* n1 = p.n1_in;
+  if (n1 == nullptr) {
+    hipLaunchKernelGGL(k_rmsnorm_rows, dim3(kGemmM), dim3(kLayerHidden / 8), 0, st, p.x, p.ln1, p.eps, kLayerHidden,
+                       l.n1);
+    AX_TRY(hipGetLastError());
+    n1 = l.n1;
+  }
   hipLaunchKernelGGL((k_gemm32<kCfgQkv32.nb, kCfgQkv32.kw, kCfgQkv32.steps, kEpiQkvSplit, false, kCfgQkv32.depth>),
-                     dim3(2 * kLayerQkv / kNBlk / kCfgQkv32.nb), dim3(64 * kCfgQkv32.nb * kCfgQkv32.kw), 0, st, l.n1,
+                     dim3(2 * kLayerQkv / kNBlk / kCfgQkv32.nb), dim3(64 * kCfgQkv32.nb * kCfgQkv32.kw), 0, st, n1,
                      p.wqkv, nullptr, kLayerQkv, l.q, l.k, l.v, kLayerHidden, nullptr);
   AX_TRY(hipGetLastError());
   AttnLaunch a{l.q, p.qn, p.kn, p.cos_t, p.sin_t, p.eps, l.k, l.v, p.Kc, p.Vc, l.attn, l.attn_ws, p.S, p.Smax,
@@ -608,7 +602,10 @@ hipError_t launch_layer(const LayerLaunch& p, hipStream_t st) {
   AX_TRY(hipGetLastError());
   launch_gemm_cfg<kCfgDown.nb, kCfgDown.kw, kCfgDown.steps>(l.mlp, p.w2, kLayerMlp, kLayerHidden, l.part, st);
   AX_TRY(hipGetLastError());
-  AX_TRY(launch_reduce<kEpiResidual>(l.part, kDownSplits, kLayerHidden, l.x2, p.x_out, st));
+  // the split sum + residual, and for a chained layer the next layer's first norm
+  hipLaunchKernelGGL(k_reduce_residual_norm<kDownSplits>, dim3(kGemmM), dim3(kLayerHidden / 8), 0, st, l.part, l.x2,
+                     p.ln1_next, p.eps, kLayerHidden, p.x_out, p.n1_out);
+  AX_TRY(hipGetLastError());
 #undef AX_TRY
   return hipSuccess;
 }

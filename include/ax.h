@@ -336,6 +336,33 @@ int ax_expert_layer(const uint16_t* x_in, const uint16_t* ln1, const uint16_t* w
                     int S, int Smax, uint16_t* x_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * ax_expert_layer for layers run one after another, the output residual of
+ * one the input of the next (the expert's stack of decoder layers; page
+ * code/alpamayo_tt/expert.py, TTExpert, whose forward calls the layer function
+ * once per layer). The first norm of a layer then runs in the previous
+ * layer's last launch:
+ * - n1_in: NULL, or RMSNorm(x_in; ln1) [64][1536] as the previous call wrote it
+ *   to its n1_out; the first norm is then skipped and ln1 is not read (it may
+ *   be NULL).
+ * - ln1_next, n1_out: both NULL, or the next layer's ln1 [1536] and a
+ *   [64][1536] buffer that receives RMSNorm(x_out; ln1_next), written by the
+ *   launch that writes x_out.
+ * Every other argument as for ax_expert_layer. x_out and n1_out are the bits
+ * ax_expert_layer gives for the same inputs (and n1_out the bits its first
+ * norm gives on x_out). AX_E_NULL if exactly one of ln1_next / n1_out is NULL,
+ * or if n1_in and ln1 are both NULL; AX_E_ARG if n1_out overlaps x_in, x_out or
+ * n1_in, or x_out overlaps x_in. A caller keeps two n1 buffers and alternates
+ * them. Eight launches with n1_in, nine without.
+ */
+int ax_expert_layer_chained(const uint16_t* x_in, const uint16_t* n1_in, const uint16_t* ln1,
+                            const uint16_t* wqkv, const uint16_t* q_norm_w, const uint16_t* k_norm_w,
+                            const uint16_t* wo, const uint16_t* ln2, const uint16_t* w1,
+                            const uint16_t* w3, const uint16_t* w2, const float* rope_cos,
+                            const float* rope_sin, float eps, uint16_t* Kc, uint16_t* Vc, int S,
+                            int Smax, uint16_t* x_out, const uint16_t* ln1_next, uint16_t* n1_out,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Weight packing for the projections: W [K][N] bf16, input-major, into W_packed
  * (same size, a separate buffer) in the layout the projection kernel streams:
  * 4 KB blocks of 32 rows x 64 columns, the blocks of one 64-column tile

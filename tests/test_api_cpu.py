@@ -249,3 +249,32 @@ def test_expert_layer_workspace_and_validation_codes():
         assert layer() == ax.AX_E_UNSUPPORTED
         assert pk(FAKE, 128, 64, FAKE, None) == ax.AX_E_UNSUPPORTED
         assert g(FAKE, FAKE, 128, 64, FAKE, FAKE, big, None) == ax.AX_E_UNSUPPORTED
+
+
+def test_expert_layer_chained_validation_codes():
+    f = ax.lib.ax_expert_layer_chained
+    X, XO, N1, N2 = 0x100000, 0x200000, 0x300000, 0x400000  # aligned, 1 MiB apart, never dereferenced
+
+    def layer(**kw):
+        a = dict(x=X, n1_in=None, ln1=FAKE, wqkv=FAKE, qn=FAKE, kn=FAKE, wo=FAKE, ln2=FAKE, w1=FAKE, w3=FAKE,
+                 w2=FAKE, cos=FAKE, sin=FAKE, eps=1e-6, Kc=FAKE, Vc=FAKE, S=128, Smax=256, out=XO, ln1_next=None,
+                 n1_out=None, ws=FAKE, ws_bytes=1 << 30)
+        a.update(kw)
+        return f(*a.values(), None)
+
+    assert layer(wqkv=None) == ax.AX_E_NULL
+    assert layer(ln1=None) == ax.AX_E_NULL                   # no n1_in: the first norm needs ln1
+    assert layer(ln1_next=FAKE) == ax.AX_E_NULL              # ln1_next without n1_out
+    assert layer(n1_out=N2) == ax.AX_E_NULL                  # n1_out without ln1_next
+    assert layer(n1_in=MIS) == ax.AX_E_ALIGN
+    assert layer(ln1_next=FAKE, n1_out=N2 + 8) == ax.AX_E_ALIGN
+    assert layer(out=X + 4096) == ax.AX_E_ARG                # x_out overlaps x_in
+    assert layer(ln1_next=FAKE, n1_out=XO + 1024) == ax.AX_E_ARG
+    assert layer(ln1_next=FAKE, n1_out=X) == ax.AX_E_ARG
+    assert layer(n1_in=N1, ln1_next=FAKE, n1_out=N1 + 16) == ax.AX_E_ARG
+    assert layer(S=193) == ax.AX_E_SHAPE
+    assert layer(eps=float("nan")) == ax.AX_E_ARG
+    assert layer(ws_bytes=16) == ax.AX_E_WORKSPACE
+    if not _gpu_present():  # valid arguments would launch on the fake pointers where a device exists
+        assert layer() == ax.AX_E_UNSUPPORTED
+        assert layer(n1_in=N1, ln1=None, ln1_next=FAKE, n1_out=N2) == ax.AX_E_UNSUPPORTED

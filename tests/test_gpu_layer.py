@@ -244,6 +244,77 @@ def test_expert_layer_headline_shape(ax):
     assert np.array_equal(down(b.out), first)
 
 
+def test_expert_layer_chained_equals_plain(ax):
+    # three layers run one after another: the chained calls (each layer's first norm made by the
+    # previous call's last launch) give the plain calls' x_out bit for bit, and the first layer
+    # matches the oracle
+    S, Smax = 300, 512
+    ws_ = [synth.layer_weights(700 + i) for i in range(3)]
+    x = synth.residual_inputs(710)
+    caches = [synth.layer_inputs(Smax, S, 720 + i) for i in range(3)]
+    say(f"expert_layer_chained S={S} Smax={Smax}, 3 layers")
+    lay = [LayerBufs(ax, ws_[i], x, caches[i], S, Smax) for i in range(3)]
+    # plain: x -> layer 0 -> layer 1 -> layer 2
+    xs = [up(x)] + [torch.empty((64, 1536), dtype=torch.int16, device=DEV) for _ in range(3)]
+    for i, b in enumerate(lay):
+        w = b.w
+        ax.expert_layer(xs[i], w["ln1"], w["wqkv"], w["qn"], w["kn"], w["wo"], w["ln2"], w["w1"], w["w3"],
+                        w["w2"], b.cos, b.sin, 1e-6, b.Kc, b.Vc, S, Smax, xs[i + 1], b.ws)
+    torch.cuda.synchronize()
+    plain = [down(t).copy() for t in xs[1:]]
+    # chained, on fresh caches, with guarded outputs and norm buffers
+    lay = [LayerBufs(ax, ws_[i], x, caches[i], S, Smax) for i in range(3)]
+    xg = [Guarded(64 * 1536 * 2) for _ in range(3)]
+    ng = [Guarded(64 * 1536 * 2) for _ in range(2)]
+    xo = [g.t.view(torch.int16).view(64, 1536) for g in xg]
+    n1 = [g.t.view(torch.int16).view(64, 1536) for g in ng]
+    for i, b in enumerate(lay):
+        w = b.w
+        n1_in = None if i == 0 else n1[(i - 1) % 2]
+        ln1 = w["ln1"] if i == 0 else None  # not read when n1_in is given
+        nxt = lay[i + 1].w["ln1"] if i < 2 else None
+        n1_out = n1[i % 2] if i < 2 else None
+        ax.expert_layer_chained(up(x) if i == 0 else xo[i - 1], n1_in, ln1, w["wqkv"], w["qn"], w["kn"], w["wo"],
+                                w["ln2"], w["w1"], w["w3"], w["w2"], b.cos, b.sin, 1e-6, b.Kc, b.Vc, S, Smax, xo[i],
+                                nxt, n1_out, b.ws)
+        torch.cuda.synchronize()
+    for i in range(3):
+        xg[i].check(f"x_out {i}")
+        assert np.array_equal(down(xo[i]), plain[i]), f"layer {i}"
+    for g in ng:
+        g.check("n1")
+    for b in lay:
+        assert_status_clear(ax, b.ws)
+    ref = _ref(ws_[0], x, caches[0], S, Smax)
+    got = bf16_to_f64(plain[0])
+    assert metrics(got, ref["x_out"])["pcc"] >= 0.9999
+    # the norm buffer a chained call hands on is the oracle's norm of its x_out, within a bf16 rounding
+    n1_ref = oracle.rms_norm(bf16_to_f64(plain[1]), bf16_to_f64(ws_[2]["ln1"]), 1e-6)
+    got_n1 = bf16_to_f64(down(n1[1]))
+    assert (np.abs(got_n1 - n1_ref) <= 2.0 ** -8 * np.abs(n1_ref) + 1e-30).all()
+
+
+def test_expert_layer_chained_rejects_bad_arguments(ax):
+    S, Smax = 64, 128
+    b = LayerBufs(ax, synth.layer_weights(730), synth.residual_inputs(731), synth.layer_inputs(Smax, S, 732), S, Smax)
+    w = b.w
+    n = torch.empty((64, 1536), dtype=torch.int16, device=DEV)
+
+    def call(**kw):
+        a = dict(x_in=b.x, n1_in=None, ln1=w["ln1"], ln1_next=None, n1_out=None, x_out=b.out)
+        a.update(kw)
+        ax.expert_layer_chained(a["x_in"], a["n1_in"], a["ln1"], w["wqkv"], w["qn"], w["kn"], w["wo"], w["ln2"],
+                                w["w1"], w["w3"], w["w2"], b.cos, b.sin, 1e-6, b.Kc, b.Vc, S, Smax, a["x_out"],
+                                a["ln1_next"], a["n1_out"], b.ws)
+
+    for kw in (dict(ln1=None), dict(ln1_next=w["ln1"]), dict(n1_out=n), dict(ln1_next=w["ln1"], n1_out=b.x),
+               dict(ln1_next=w["ln1"], n1_out=b.out), dict(x_out=b.x)):
+        with pytest.raises(RuntimeError):
+            call(**kw)
+    call(ln1_next=w["ln1"], n1_out=n)  # valid
+    torch.cuda.synchronize()
+
+
 def _bits(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
