@@ -14,7 +14,7 @@ another, then the down projection), whose result is added once more. Shapes: res
 up projections [1536, 6144] and the down projection [6144, 1536]; every weight is stored
 input-major ([in, out], the transpose of the HF layout), as the pages keep them.
 
-Reading (also in the design notes): every op hands a bf16 tensor to the next, as ttnn ops do
+Reading: every op hands a bf16 tensor to the next, as ttnn ops do
 (the pages' activations are bf16 throughout), so the oracle rounds to bf16 at each op boundary
 of the list above and computes inside each op in float64: the residual inputs of the adds, the
 normed activations, qkv, the attention output, o, g = silu(n2 w1), u = n2 w3, m = g u, d.
