@@ -193,10 +193,9 @@ enum GemmEpilogue { kEpiQkvSplit = 1, kEpiSwiGlu = 3, kEpiPartial = 4 };
 // kEpiQkvSplit: column blocks NB t .. NB t + NB - 1 of W0, bf16(C) into q / k / v
 // [heads][64][128].
 // kEpiSwiGlu: blocks (NB / 2) t + p of W0 (x w1, waves nb = p) and of W1 (x w3, nb = NB / 2 + p),
-// out[m][32 j + c] = bf16(bf16(silu(C1)) * bf16(C3)), the same arithmetic as k_gemm_reduce's
-// SwiGLU epilogue.
+// out[m][32 j + c] = bf16(bf16(silu(C1)) * bf16(C3)), silu(g) = g / (1 + e^-g).
 // kEpiPartial: K is cut into n_split splits of KC = 16 KW STEPS rows (blockIdx / (2 n_tiles) is the
-// split); the split's float32 C goes to part[split][64][N] for k_gemm_reduce.
+// split); the split's float32 C goes to part[split][64][N] (summed by k_reduce_residual_norm).
 // HEADS: A is the attention output [16][64][128] read as [64][2048] (a_elem).
 template <int NB, int KW, int STEPS, int EPI, bool HEADS, int D = STEPS>
 __global__ __launch_bounds__(64 * NB * KW) void k_gemm32(const uint16_t* A, const uint16_t* W0, const uint16_t* W1,
@@ -318,10 +317,9 @@ __global__ __launch_bounds__(64 * NB * KW) void k_gemm32(const uint16_t* A, cons
   *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
 }
 
-// Sum of the splits of C[64, N], then the epilogue. A workgroup covers one row and 256 columns:
+// Sum of the splits of C[64, N], rounded to bf16. A workgroup covers one row and 256 columns:
 // thread (g, q) sums splits g, g + 4, ... of columns 4q .. 4q + 3 (eight loads in flight), and
 // group 0 adds the four group sums in group order, so the result does not depend on timing.
-// out[m][n] = bf16(C).
 constexpr int kRedGroups = 4, kRedBatch = 8;
 
 __global__ __launch_bounds__(256) void k_gemm_reduce(const float* part, int n_split, int N, uint16_t* out) {
