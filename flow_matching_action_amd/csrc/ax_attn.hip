@@ -175,17 +175,6 @@ __device__ __forceinline__ void await_cnt(int i, int n, int limit, bool& expired
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Chunk swizzles of the ring's 256-byte K and V rows (16 chunks of 16 bytes). LDS serves a
-// ds_read_b128 for 16 lanes per cycle and a ds_read_b64_tr_b16 for 32, all 64 banks at once, so
-// those lanes must hit 16 distinct chunks; the swizzles also keep 8-lane (b128) and 16-lane (tr)
-// halves on 8 distinct chunks of one 128-byte half, the other half taking the other 8.
-// K: lanes 0..15 read rows 0..15 (or 16..31) at one chunk c: row r's chunk c sits at c ^ (r & 15).
-__device__ __forceinline__ int kswz16(int r) { return r & 15; }
-// V: the 32 lanes of two 16-lane transpose groups read rows 0..7 (mod 16) at chunks 2 dt and
-// 2 dt + 1: 2 (r & 7) moves the pair to 2 (dt ^ (r & 7)), a distinct pair per row, with rows 0..3
-// in one half and rows 4..7 in the other.
-__device__ __forceinline__ int vswz16(int r) { return 2 * (r & 7); }
-
 // Per-workgroup facts every wave shares.
 struct SplitCtx {
   int g, hp, split, k_begin, k_end, nb, lane;

@@ -1,7 +1,7 @@
 // Device-side pieces shared by the attention kernels (the expert step over bf16 and fp8 caches,
-// ax_attn.hip; the text-model decode step, ax_decode.hip): the LDS hand-off counters and bounded
-// waits, the workspace status word, the decode kernel's MFMA operand layouts, the float16 partial
-// packing and the e4m3 conversions.
+// ax_attn.hip; the text-model decode step, ax_decode.hip): the block tiles' swizzles, the LDS
+// hand-off counters and bounded waits, the workspace status word, the float16 partial packing and
+// the e4m3 conversions.
 #pragma once
 #include "ax_dev.h"
 
@@ -17,17 +17,18 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Chunk swizzles (16-byte chunk index within a 256-byte bf16 row). Query rows are read by
-// consecutive lanes from consecutive rows: all 4 row bits. (kswz, vswz: the decode kernel's
-// 32-row MFMA layout; the expert kernel's 16-row layout has its own.)
+// consecutive lanes from consecutive rows: all 4 row bits.
 __device__ __forceinline__ int qswz(int r) { return r & 15; }
-// K rows are read by 8-lane groups from rows {0..3, 8..11} + 4j (the MFMA row order pi below):
-// bits 0, 1 and 3 of the row make those 8 rows hit 8 distinct 16-byte bank groups. The
-// swizzle stays below 8, so chunks c and c + 8 keep their 128-byte distance.
-__device__ __forceinline__ int kswz(int r) { return (r & 3) | ((r >> 1) & 4); }
-// V rows of a bf16 tile: the swizzle only depends on row & 3, so all transpose reads of a
-// lane share two base addresses (t even / odd) plus immediate offsets, and still spread a
-// 16-lane group over 8 distinct chunks.
-__device__ __forceinline__ int vswz(int r) { return 2 * (r & 3); }
+// K and V rows of a 32-key block tile (16 chunks of 16 bytes a row). LDS serves a ds_read_b128
+// for 16 lanes per cycle and a ds_read_b64_tr_b16 for 32, all 64 banks at once, so those lanes
+// must hit 16 distinct chunks; the swizzles also keep 8-lane (b128) and 16-lane (tr) halves on 8
+// distinct chunks of one 128-byte half, the other half taking the other 8.
+// K: lanes 0..15 read rows 0..15 (or 16..31) at one chunk c: row r's chunk c sits at c ^ (r & 15).
+__device__ __forceinline__ int kswz16(int r) { return r & 15; }
+// V: the 32 lanes of two 16-lane transpose groups read rows 0..7 (mod 16) at chunks 2 dt and
+// 2 dt + 1: 2 (r & 7) moves the pair to 2 (dt ^ (r & 7)), a distinct pair per row, with rows 0..3
+// in one half and rows 4..7 in the other.
+__device__ __forceinline__ int vswz16(int r) { return 2 * (r & 7); }
 // A lane's value and that of lane ^ 32, in either order: v_permlane32_swap exchanges the upper
 // half of one operand with the lower half of the other, so fed the same value twice, each of
 // its two results holds one of the pair in every lane. A VALU exchange, unlike ds_bpermute.
@@ -35,13 +36,6 @@ __device__ __forceinline__ float2 pair32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return float2{__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
-
-// Row order inside a 32-key block seen by the MFMA: swap bits 2 and 3.
-__device__ __forceinline__ int perm_key(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
-
-// Head-dim chunk (8 columns) used by k-step kk in lane half h: half h holds columns
-// [32h, 32h+32) and [64+32h, 96+32h), so a RoPE pair (j, j+64) stays in one lane.
-__device__ __forceinline__ int dcol(int kk, int h) { return (kk < 4) ? 32 * h + 8 * kk : 64 + 32 * h + 8 * (kk - 4); }
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt bits [3:0]
 // and [15:14], expcnt [6:4], lgkmcnt [11:8]).

@@ -18,10 +18,11 @@
 //   cache; the compute wave that consumes its block norms and ropes that k row in the tile
 //   and writes both rows to cache row pos.
 // - Waves 0..3 (compute): wave 0 norms and ropes the 8 query rows of the kv head into LDS;
-//   wave w consumes blocks w, w + 4. The 8 rows are the first 8 of the 32 rows of the expert
-//   kernel's MFMA layout (S^T = K Q^T on v_mfma_f32_32x32x16_bf16, O^T = V^T P^T with V^T read
-//   by ds_read_tr16_b64); rows 8..31 are zero. The step is bound by the cache stream, which
-//   the unused rows do not touch.
+//   wave w consumes blocks w, w + 4. The 8 rows are the first 8 of the expert kernel's 16-row
+//   MFMA layout and tiles (S^T = K Q^T per 16-key half on v_mfma_f32_16x16x32_bf16, O^T += V^T
+//   P^T with P^T straight from the score accumulators and V^T read by ds_read_b64_tr_b16); rows
+//   8..15 are zero. (On the 32-row layout, with 24 zero rows, the block arithmetic took ~2.2 us
+//   of the step; this layout halves it.)
 // - The compute waves merge their (m, l, O) through LDS; wave 0 stores the split's partial
 //   (8 rows). k_decode_combine then reduces the splits of each of the 64 output rows.
 #include "ax_attn_common.h"
@@ -63,8 +64,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void k_decode_attn(DecArgs a) {
   static_assert(NB >= 1 && NB <= kDecMaxNB, "blocks per split");
   __shared__ __attribute__((aligned(16))) uint8_t tiles[NB][kDecTile];
   __shared__ __attribute__((aligned(16))) uint8_t qlds[kDecRows * 256];
-  // merge hand-off of compute waves 1..3: O of rows 0..7 (slot j, lane (row, half)), m and l
-  __shared__ f32x4 mo[kDecCompute - 1][16][16];
+  // merge hand-off of compute waves 1..3: O of rows 0..7 (column tile dt, slot (row, group)), m and l
+  __shared__ f32x4 mo[kDecCompute - 1][8][32];
   __shared__ float mml[kDecCompute - 1][2][kDecRows];
   __shared__ int cnt[kDcN];
   const int tid = threadIdx.x;
@@ -97,9 +98,9 @@ __global__ __launch_bounds__(kDecThreads, 1) void k_decode_attn(DecArgs a) {
         const uint16_t* ks = is_new ? a.k + (long long)g * kD : a.Kc + (head_row + kk) * kD;
         const uint16_t* vs = is_new ? a.v + (long long)g * kD : a.Vc + (head_row + kk) * kD;
         // non-temporal: the decode step measured 5% faster than with ordinary reads
-        __builtin_amdgcn_global_load_lds(ks + 8 * ((lane & 15) ^ kswz(r)), (lds_void*)(tile + (8 * w + 4 * i) * 256),
+        __builtin_amdgcn_global_load_lds(ks + 8 * ((lane & 15) ^ kswz16(r)), (lds_void*)(tile + (8 * w + 4 * i) * 256),
                                          16, 0, kNonTemporal);
-        __builtin_amdgcn_global_load_lds(vs + 8 * ((lane & 15) ^ vswz(r)),
+        __builtin_amdgcn_global_load_lds(vs + 8 * ((lane & 15) ^ vswz16(r)),
                                          (lds_void*)(tile + kDecTile / 2 + (8 * w + 4 * i) * 256), 16, 0, kNonTemporal);
       });
     };
@@ -159,35 +160,36 @@ __global__ __launch_bounds__(kDecThreads, 1) void k_decode_attn(DecArgs a) {
   }
   await(&cnt[kDcQ], 1, a.spin_limit, expired);
 
-  const int n = lane & 31;
-  const int h = lane >> 5;
-  bf16x8 qf[8];
+  // The query rows as MFMA B operands (16 rows of the 16-row layout; rows 8..15 are zero): k-step
+  // kk takes columns 32 kk .. 32 kk + 31; lane l holds row l & 15, columns 32 kk + 8 (l >> 4) ..
+  const int g4 = lane >> 4;
+  bf16x8 qf[4];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    if (n < kDecRows) {
-      qf[kk] = *reinterpret_cast<const bf16x8*>(qlds + n * 256 + 16 * ((dcol(kk, h) >> 3) ^ qswz(n)));
+  for (int kk = 0; kk < 4; ++kk) {
+    if (j16 < kDecRows) {
+      qf[kk] = *reinterpret_cast<const bf16x8*>(qlds + j16 * 256 + 16 * ((4 * kk + g4) ^ qswz(j16)));
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) qf[kk][e] = (__bf16)0.f;
     }
   }
 
-  f32x16 o[4];
+  f32x4 o[8];  // O^T: lane l holds O[row l & 15][16 dt + 4 (l >> 4) + i]
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;  // the lane's row; l_run is the lane's share of its sum
   const float sc = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
-  const int krow = perm_key(n);
+  // K: key row 16 t + j16, chunk 4 kk + g4 (the second half of the keys 4 KB further on)
   int koff[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) koff[j] = krow * 256 + 16 * ((4 * h + j) ^ kswz(krow));
-  const int G = lane >> 4, li = lane & 15;
-  const int vrow0 = 8 * (G >> 1) + (li >> 2);
-  const int vx = 2 * (G & 1) + ((li & 3) >> 1);
-  const int voff[2] = {vrow0 * 256 + 16 * (vx ^ vswz(vrow0)) + 8 * (li & 1),
-                       vrow0 * 256 + 16 * ((4 + vx) ^ vswz(vrow0)) + 8 * (li & 1)};
+  for (int kk = 0; kk < 4; ++kk) koff[kk] = j16 * 256 + 16 * ((4 * kk + g4) ^ kswz16(j16));
+  // V^T: lane j16 of group g4 supplies key row 4 g4 + (j16 >> 2) (+ 16 for the second read),
+  // columns 16 dt + 4 (j16 & 3) .. + 3
+  const int vr = 4 * g4 + (j16 >> 2);
+  int voff[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+    voff[dt] = kDecTile / 2 + vr * 256 + 16 * ((2 * dt + ((j16 & 3) >> 1)) ^ vswz16(vr)) + 8 * (j16 & 1);
 
   static_for<NB>([&](auto bc) {
     constexpr int b = decltype(bc)::value;
@@ -200,8 +202,8 @@ __global__ __launch_bounds__(kDecThreads, 1) void k_decode_attn(DecArgs a) {
     if (a.pos >= kb && a.pos < min(kb + kBlk, k_end) && lane < 16) {
       // the new token's k row: norm + RoPE in place, then both rows to cache row pos
       const int r = a.pos - kb;
-      u32x4* kp = reinterpret_cast<u32x4*>(tile + r * 256 + 16 * (j16 ^ kswz(r)));
-      const u32x4 vraw = *reinterpret_cast<const u32x4*>(tile + kDecTile / 2 + r * 256 + 16 * (j16 ^ vswz(r)));
+      u32x4* kp = reinterpret_cast<u32x4*>(tile + r * 256 + 16 * (j16 ^ kswz16(r)));
+      const u32x4 vraw = *reinterpret_cast<const u32x4*>(tile + kDecTile / 2 + r * 256 + 16 * (j16 ^ vswz16(r)));
       float gkv[8], x[8];
       unpack8v(gkraw, gkv);
       rope_coef(gkv, qc, qs, j16, A, B);
@@ -213,28 +215,30 @@ __global__ __launch_bounds__(kDecThreads, 1) void k_decode_attn(DecArgs a) {
       *reinterpret_cast<u32x4*>(a.Kc + dst) = kr;
       *reinterpret_cast<u32x4*>(a.Vc + dst) = vraw;
     }
-    f32x16 s;
-    {
-      bf16x8 kf[8];
+    // S^T = K Q^T per 16-key half t: lane l holds row j16 against keys 16 t + 4 g4 + i
+    f32x4 s[2];
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(tile + koff[kk & 3] + 128 * (kk >> 2));
+    for (int t = 0; t < 2; ++t) {
+      bf16x8 kf[4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] = 0.f;
+      for (int kk = 0; kk < 4; ++kk) kf[kk] = *reinterpret_cast<const bf16x8*>(tile + koff[kk] + 4096 * t);
+      s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
+      for (int kk = 0; kk < 4; ++kk) s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[kk], s[t], 0, 0, 0);
     }
     if (kb + kBlk > k_end) {
-      const int lim = k_end - kb - 8 * h;
+      const int lim = k_end - kb - 4 * g4;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kofs = 16 * (i >> 3) + 4 * ((i >> 2) & 1) + (i & 3);
-        s[i] = (kofs < lim) ? s[i] : -INFINITY;
-      }
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[t][i] = (16 * t + i < lim) ? s[t][i] : -INFINITY;
     }
-    float bmax = s[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) bmax = fmaxf(bmax, s[i]);
+    // the row's block max: the lane's 8 keys, then the four lanes j16 + 16 i of the row
+    float bmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
     {
+      const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(bmax), __float_as_uint(bmax), false, false);
+      bmax = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
       const float2 pr = pair32(bmax);
       bmax = fmaxf(pr.x, pr.y);
     }
@@ -247,59 +251,54 @@ __global__ __launch_bounds__(kDecThreads, 1) void k_decode_attn(DecArgs a) {
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+        for (int i = 0; i < 4; ++i) o[dt][i] *= alpha;
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sc, -m_run));
-    // the row sum adds the same bf16-rounded p that the PV product uses, so each output row is an
-    // exact convex combination of v rows
+    // p as P^T straight from the two score accumulators (slots 0..3: keys 4 g4 + i, 4..7: keys
+    // 16 + 4 g4 + i); the row sum adds the same bf16-rounded p that the PV product uses, so each
+    // output row is an exact convex combination of v rows
     const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
-    float ps[2] = {0.f, 0.f};
-    const uint8_t* tv = tile + kDecTile / 2;
+    bf16x8 pb;
+    float ps = 0.f;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      bf16x8 pb;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)s[8 * c + e];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const bf16x2_t pr = {pb[e], pb[e + 1]};
-        ps[c] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ps[c], false);
+      for (int i = 0; i < 4; i += 2) {
+        const bf16x2_t pr = {(__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], sc, -m_run)),
+                             (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i + 1], sc, -m_run))};
+        pb[4 * t + i] = pr[0];
+        pb[4 * t + i + 1] = pr[1];
+        ps = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ps, false);
       }
-      v4i16 vt[4][2];
+    l_run += ps;
+    // O^T += V^T P^T per 16-column tile dt (V^T in the same key order: two ds_read_b64_tr_b16)
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-          vt[t][hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16*)(tv + (16 * c + 4 * hf) * 256 + 128 * (t >> 1) + voff[t & 1]));
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const v4i16 both[2] = {vt[t][0], vt[t][1]};
-        bf16x8 vf;
-        __builtin_memcpy(&vf, both, 16);
-        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[t], 0, 0, 0);
-      }
+    for (int dt = 0; dt < 8; ++dt) {
+      const v4i16 both[2] = {__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + voff[dt])),
+                             __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + voff[dt] + 4096))};
+      bf16x8 vf;
+      __builtin_memcpy(&vf, both, 16);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb, o[dt], 0, 0, 0);
     }
-    l_run += ps[0] + ps[1];
   });
 
-  // merge of the compute waves (rows 0..7: lanes n < 8 of both halves), then the partial
-  const float2 l_pair = pair32(l_run);
-  const float l_tot = l_pair.x + l_pair.y;
-  const int ml = (lane & 7) + 8 * h;  // merge slot of lane (n, h), n < 8
+  // merge of the compute waves (rows 0..7: lanes j16 < 8), then the partial
+  float l_tot = l_run;  // the row's total: its four lanes' shares
+  {
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(l_tot), __float_as_uint(l_tot), false, false);
+    l_tot = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    const float2 pr = pair32(l_tot);
+    l_tot = pr.x + pr.y;
+  }
+  const int ml = (lane & 7) + 8 * g4;  // merge slot of lane (row j16 < 8, group g4)
   if (wave > 0) {
-    if (n < kDecRows) {
+    if (j16 < kDecRows) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          mo[wave - 1][4 * t + jj][ml] = f32x4{o[t][4 * jj], o[t][4 * jj + 1], o[t][4 * jj + 2], o[t][4 * jj + 3]};
-      if (h == 0) {
-        mml[wave - 1][0][n] = m_run;
-        mml[wave - 1][1][n] = l_tot;
+      for (int dt = 0; dt < 8; ++dt) mo[wave - 1][dt][ml] = o[dt];
+      if (g4 == 0) {
+        mml[wave - 1][0][j16] = m_run;
+        mml[wave - 1][1][j16] = l_tot;
       }
     }
     arrive(&cnt[kDcMerge], lane);
@@ -308,35 +307,30 @@ __global__ __launch_bounds__(kDecThreads, 1) void k_decode_attn(DecArgs a) {
   }
   await(&cnt[kDcMerge], kDecCompute - 1, a.spin_limit, expired);
   report_expired(a.status, expired, lane);
-  if (n >= kDecRows) return;
+  if (j16 >= kDecRows) return;
   float m_all = m_run, l_all = l_tot;  // block 0 holds a visible key: m_run is finite
 #pragma unroll
   for (int w = 0; w < kDecCompute - 1; ++w) {
-    const float m_o = mml[w][0][n];
-    const float l_o = mml[w][1][n];
+    const float m_o = mml[w][0][j16];
+    const float l_o = mml[w][1][j16];
     const float m_new = fmaxf(m_all, m_o);
     const float ae = __builtin_amdgcn_exp2f(m_all - m_new);
     const float ao = __builtin_amdgcn_exp2f(m_o - m_new);  // 0 for a wave without blocks (m = -inf)
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int dt = 0; dt < 8; ++dt) {
+      const f32x4 x = mo[w][dt][ml];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const f32x4 x = mo[w][4 * t + jj][ml];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[t][4 * jj + e] = ae * o[t][4 * jj + e] + ao * x[e];
-      }
+      for (int e = 0; e < 4; ++e) o[dt][e] = ae * o[dt][e] + ao * x[e];
+    }
     l_all = ae * l_all + ao * l_o;
     m_all = m_new;
   }
-  const long long prow = ((long long)g * a.n_split + split) * kDecRows + n;
-  // lane (n, h) holds columns 32 t + 8 jj + 4 h .. +3 of row n
+  const long long prow = ((long long)g * a.n_split + split) * kDecRows + j16;
+  // lane (row j16, group g4) holds columns 16 dt + 4 g4 .. +3 of row j16
   f32x4* po = reinterpret_cast<f32x4*>(a.po + prow * kD);
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
-      po[(32 * t + 8 * jj + 4 * h) / 4] = f32x4{o[t][4 * jj], o[t][4 * jj + 1], o[t][4 * jj + 2], o[t][4 * jj + 3]};
-  if (h == 0) {
+  for (int dt = 0; dt < 8; ++dt) po[4 * dt + g4] = o[dt];
+  if (g4 == 0) {
     a.pm[prow] = expired ? __builtin_nanf("") : m_all;
     a.pl[prow] = l_all;
   }
