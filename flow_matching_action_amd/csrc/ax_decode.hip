@@ -33,7 +33,8 @@ namespace ax {
 constexpr int kDecQHeads = 64;
 constexpr int kDecRows = kDecQHeads / kHkv;   // 8 query rows (heads) per kv head
 constexpr int kDecCompute = 4;                // compute waves
-constexpr int kDecThreads = 64 * 2 * kDecCompute;  // + as many loader waves
+constexpr int kDecLoaders = 4;                // loader waves (8 rows of each block each)
+constexpr int kDecThreads = 64 * (kDecCompute + kDecLoaders);
 constexpr int kDecDepth = 3;                  // blocks in flight per loader wave
 // LDS hand-off counters: query rows normed, block b landed, merge data of the compute waves ready
 constexpr int kDcQ = 0, kDcBlock = 1, kDcMerge = kDcBlock + 8, kDcN = kDcMerge + 1;
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void k_decode_attn(DecArgs a) {
     constexpr int b = decltype(bc)::value;
     if (b % kDecCompute != wave) return;
     const int kb = k_begin + b * kBlk;
-    await(&cnt[kDcBlock + b], kDecCompute, a.spin_limit, expired);
+    await(&cnt[kDcBlock + b], kDecLoaders, a.spin_limit, expired);
     if (kb >= k_end) return;
     uint8_t* tile = &tiles[b][0];
     // (a split's last block can reach past the split's end: key pos must be one of this split's)
