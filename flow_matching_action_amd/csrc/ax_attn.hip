@@ -44,6 +44,7 @@
 
 namespace ax {
 
+constexpr int kSRT = 4;                         // row tiles of 16 query rows (one per SIMD)
 constexpr int kSC = 8;                          // compute waves: 4 row tiles x 2 block parities
 constexpr int kSL = 4;                          // loader waves
 constexpr int kSThreads = 64 * (kSC + kSL);
@@ -51,14 +52,20 @@ constexpr int kSTile = 2 * kBlk * kD * 2;       // 16 KB: the K rows, then the V
 constexpr int kSV = kBlk * kD * 2;              // offset of the V rows in a tile
 constexpr int kSRing = 6;                       // tiles; block b uses tile b % kSRing (bf16 cache)
 constexpr int kSMaxNB = 10;                     // blocks per key range (bf16 cache)
-// fp8 cache: the ring's first four tiles take the bf16 blocks the loaders convert (block b in tile
-// b % 4), the rest four raw tiles of codes (32 rows of 128 bytes for K, then for V; block b in raw
-// tile b % 4)
-constexpr int kSRing8 = 4;
-constexpr int kSRaw8 = 4;
+// fp8 cache: the ring's first 32 KB are four V tiles of the bf16 values the loaders convert (block
+// b in V tile b % 4: 32 rows of 256 bytes, the bf16 tiles' V layout), the rest eight raw tiles of
+// codes (block b in raw tile b % 8: 32 rows of 128 bytes for K, chunk-swizzled, which the matrix
+// cores read as codes, then 32 rows for V). In the own range, blocks 0 and 1 arrive as bf16 rows
+// in two bf16 tiles at kSStage8 (raw tiles 2..5, unused there) and are quantised from there.
+constexpr int kSRing8 = 4;                      // V tiles
+constexpr int kSVTile8 = kBlk * kD * 2;
+constexpr int kSRaw8 = 8;                       // raw tiles
 constexpr int kSRawTile = 2 * kBlk * kD;
-constexpr int kSRawBase = kSRing8 * kSTile;
+constexpr int kSRawBase = kSRing8 * kSVTile8;
+constexpr int kSStage8 = kSRawBase + 2 * kSRawTile;
 static_assert(kSRawBase + kSRaw8 * kSRawTile <= kSRing * kSTile, "fp8 rings inside the bf16 ring");
+static_assert(kSStage8 + 2 * kSTile <= kSRawBase + kSRaw8 * kSRawTile, "own-range staging inside the raw tiles");
+constexpr int kSDoneN = kSRaw8 > kSRing ? kSRaw8 : kSRing;  // tile-use counters
 constexpr int kSMaxNB8 = 17;                    // blocks per key range (fp8 cache)
 constexpr int kSDepth = 3;                      // blocks in flight per loader wave
 constexpr int kSCacheRanges = 15;               // cache key ranges per kv head, at most
@@ -66,7 +73,7 @@ constexpr float kSRescale = 16.0f;              // lazy-rescale threshold (log2 
 constexpr float kScoreScale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
 // LDS hand-off counters: prologue of row tile t landed, query rows normed, query fragments read,
 // block b landed, uses of tile r finished, merge data of row tile t written
-constexpr int kCPro = 0, kCNorm = 4, kCFrag = 5, kCLand = 6, kCDone = kCLand + kSMaxNB8, kCMrg = kCDone + kSRing,
+constexpr int kCPro = 0, kCNorm = 4, kCFrag = 5, kCLand = 6, kCDone = kCLand + kSMaxNB8, kCMrg = kCDone + kSDoneN,
               kCN = kCMrg + 4;
 
 struct SplitArgs {
@@ -207,31 +214,32 @@ __device__ __forceinline__ long long cache_row8(const SplitArgs& a, const SplitC
   v = v < c.k_end ? v : c.k_begin;
   return (long long)c.g * a.Smax + (v < a.S ? v : a.Smax - kT + (v - a.S));
 }
+// K codes: chunk c (16 bytes) of row r at c ^ kswz8(r), so that the 16 rows a 16-lane group reads
+// at one chunk hit all 64 banks once (rows 128 bytes apart share banks two rows apart).
+__device__ __forceinline__ int kswz8(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ void dma_block_f8(const SplitArgs& a, const SplitCtx& c, int L, int b) {
   lds_u8* raw = AX_LDS(sRing) + kSRawBase + (b % kSRaw8) * kSRawTile;
-  const long long row = cache_row8(a, c, c.k_begin + kBlk * b + 8 * L + (c.lane >> 3));
-  dma_x4(a.Kc8 + row * kD + 16 * (c.lane & 7), raw + 8 * L * kD);
+  const int r = 8 * L + (c.lane >> 3);
+  const long long row = cache_row8(a, c, c.k_begin + kBlk * b + r);
+  dma_x4(a.Kc8 + row * kD + 16 * ((c.lane & 7) ^ kswz8(r)), raw + 8 * L * kD);
   dma_x4(a.Vc8 + row * kD + 16 * (c.lane & 7), raw + kBlk * kD + 8 * L * kD);
   if (c.lane < 16) {
     const long long srow = cache_row8(a, c, c.k_begin + kBlk * b + 8 * L + (c.lane & 7));
     dma_x1((c.lane < 8 ? a.Ks : a.Vs) + srow, AX_LDS(sScl8) + b * 256 + 64 * L);
   }
 }
-// ... and, once landed, the same rows converted exactly (every e4m3 value is a bf16 value) into
-// the block's bf16 tile b % 4 with the bf16 tiles' swizzles: code chunk c8 of a row (16 bytes) is
-// bf16 chunks 2 c8 and 2 c8 + 1. The scales are applied in float32 by the compute waves. (Scaling
-// V here instead, rounded to bf16, made the launch 4% slower: the loaders share the SIMDs with
-// the compute waves.)
+// ... and, once landed, the V rows converted exactly (every e4m3 value is a bf16 value) into the
+// block's V tile b % 4 with the bf16 tiles' V swizzle: code chunk c8 of a row (16 bytes) is bf16
+// chunks 2 c8 and 2 c8 + 1. (K stays in codes.) The scales are applied in float32 by the compute
+// waves. (Scaling V here instead, rounded to bf16, made the launch 4% slower: the loaders share the
+// SIMDs with the compute waves.)
 __device__ __forceinline__ void convert_block_f8(const SplitCtx& c, int L, int b) {
   const lds_u8* raw = AX_LDS(sRing) + kSRawBase + (b % kSRaw8) * kSRawTile;
-  lds_u8* tile = AX_LDS(sRing) + (b % kSRing8) * kSTile;
+  lds_u8* vt = AX_LDS(sRing) + (b % kSRing8) * kSVTile8;
   const int r = 8 * L + (c.lane >> 3), c8 = c.lane & 7;
-  const u32x4 kw = lds_ld<u32x4>(raw + r * kD + 16 * c8);
   const u32x4 vw = lds_ld<u32x4>(raw + kBlk * kD + r * kD + 16 * c8);
-  lds_st(tile + r * 256 + 16 * ((2 * c8) ^ kswz16(r)), e4m3x8_to_bf16(kw[0], kw[1]));
-  lds_st(tile + r * 256 + 16 * ((2 * c8 + 1) ^ kswz16(r)), e4m3x8_to_bf16(kw[2], kw[3]));
-  lds_st(tile + kSV + r * 256 + 16 * ((2 * c8) ^ vswz16(r)), e4m3x8_to_bf16(vw[0], vw[1]));
-  lds_st(tile + kSV + r * 256 + 16 * ((2 * c8 + 1) ^ vswz16(r)), e4m3x8_to_bf16(vw[2], vw[3]));
+  lds_st(vt + r * 256 + 16 * ((2 * c8) ^ vswz16(r)), e4m3x8_to_bf16(vw[0], vw[1]));
+  lds_st(vt + r * 256 + 16 * ((2 * c8 + 1) ^ vswz16(r)), e4m3x8_to_bf16(vw[2], vw[3]));
 }
 
 __device__ __forceinline__ float fmax_(float a, float b) { return __builtin_elementwise_maximum(a, b); }
@@ -254,13 +262,20 @@ __device__ __forceinline__ float row_max4(float x) {
   return fmax_(p.x, p.y);
 }
 
+// The bf16 tile holding own block blk (tokens 32 blk .. 32 blk + 31) in the own range: the ring's
+// tiles 0, 1, or with the fp8 cache the staging tiles the quantisation reads.
+template <bool F8>
+__device__ __forceinline__ lds_u8* own_tile(int blk) {
+  return AX_LDS(sRing) + (F8 ? kSStage8 : 0) + blk * kSTile;
+}
+
 // Norm + RoPE in place of query rows row0 .. row0 + 4 NP - 1 (NP passes of 4 rows, 16 lanes per
 // row: the arithmetic of the stand-alone norm/RoPE kernel, so the bits are the same) and, in the
 // own range, of the own k rows of the same tokens (same RoPE rows, gamma k). The 16 rows of a row
 // tile are split between the three waves of its SIMD (4 + 4 + 8), since a single wave issues
 // vector instructions at only half of a SIMD's rate. Within a pass every LDS read comes first,
 // then the arithmetic, then the stores, so that the rows' dependency chains interleave.
-template <int NP>
+template <int NP, bool F8>
 __device__ __forceinline__ void norm_rows(const SplitArgs& a, const SplitCtx& c, const int row0) {
   const int lane = c.lane, j16 = lane & 15, r4 = lane >> 4;
   lds_u8* ring = AX_LDS(sRing);
@@ -302,7 +317,7 @@ __device__ __forceinline__ void norm_rows(const SplitArgs& a, const SplitCtx& c,
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int tr = (row0 + 4 * i + r4) & (kBlk - 1);
-      const lds_u8* krow = ring + ((row0 + 4 * i) >> 5) * kSTile + tr * 256;
+      const lds_u8* krow = own_tile<F8>((row0 + 4 * i) >> 5) + tr * 256;
       klo[i] = lds_ld<uint2>(krow + pair_off_lo(j16, kswz16(tr)));
       khi[i] = lds_ld<uint2>(krow + pair_off_hi(j16, kswz16(tr)));
     }
@@ -317,7 +332,7 @@ __device__ __forceinline__ void norm_rows(const SplitArgs& a, const SplitCtx& c,
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       const int tr = (row0 + 4 * i + r4) & (kBlk - 1);
-      lds_u8* krow = ring + ((row0 + 4 * i) >> 5) * kSTile + tr * 256;
+      lds_u8* krow = own_tile<F8>((row0 + 4 * i) >> 5) + tr * 256;
       lds_st(krow + pair_off_lo(j16, kswz16(tr)), klo[i]);
       lds_st(krow + pair_off_hi(j16, kswz16(tr)), khi[i]);
     }
@@ -325,10 +340,11 @@ __device__ __forceinline__ void norm_rows(const SplitArgs& a, const SplitCtx& c,
 }
 
 // fp8 cache, own range: the own k rows (normed and roped, or given roped) and the own v rows of
-// tokens row0 .. row0 + 4 NP - 1 quantised per row in place (16 lanes per row: quant_row16, the
-// definition of the cache format), the tiles then holding the codes' e4m3 values in bf16 and the
-// block's scale record the row scales, as for a block the loaders convert; the codes and scales
-// go to the cache tail here (q head parity 0), while they are at hand.
+// tokens row0 .. row0 + 4 NP - 1, from the staging tiles, quantised per row (16 lanes per row:
+// quant_row16, the definition of the cache format): the K codes into raw tile blk, the V codes'
+// values in bf16 into V tile blk and the row scales into the block's scale record, as for a block
+// the loaders bring; the codes and scales go to the cache tail here (q head parity 0), while they
+// are at hand.
 template <int NP>
 __device__ __forceinline__ void quant_own_rows(const SplitArgs& a, const SplitCtx& c, const int row0) {
   const int j16 = c.lane & 15, r4 = c.lane >> 4;
@@ -336,15 +352,15 @@ __device__ __forceinline__ void quant_own_rows(const SplitArgs& a, const SplitCt
   for (int i = 0; i < NP; ++i) {
     const int tok = row0 + 4 * i + r4;
     const int tr = tok & (kBlk - 1), blk = tok >> 5;
-    lds_u8* krow = AX_LDS(sRing) + blk * kSTile + tr * 256 + 16 * (j16 ^ kswz16(tr));
-    lds_u8* vrow = AX_LDS(sRing) + blk * kSTile + kSV + tr * 256 + 16 * (j16 ^ vswz16(tr));
+    const lds_u8* st = own_tile<true>(blk);
     float x[8], y[8], sk, sv;
-    unpack8v(lds_ld<u32x4>(krow), x);
-    unpack8v(lds_ld<u32x4>(vrow), y);
+    unpack8v(lds_ld<u32x4>(st + tr * 256 + 16 * (j16 ^ kswz16(tr))), x);
+    unpack8v(lds_ld<u32x4>(st + kSV + tr * 256 + 16 * (j16 ^ vswz16(tr))), y);
     const uint2 ck = quant_row16(x, sk);
     const uint2 cv = quant_row16(y, sv);
-    lds_st(krow, e4m3x8_to_bf16(ck.x, ck.y));
-    lds_st(vrow, e4m3x8_to_bf16(cv.x, cv.y));
+    // lane j16's 8 codes are half j16 & 1 of code chunk j16 >> 1
+    lds_st(AX_LDS(sRing) + kSRawBase + blk * kSRawTile + tr * kD + 16 * ((j16 >> 1) ^ kswz8(tr)) + 8 * (j16 & 1), ck);
+    lds_st(AX_LDS(sRing) + blk * kSVTile8 + tr * 256 + 16 * (j16 ^ vswz16(tr)), e4m3x8_to_bf16(cv.x, cv.y));
     if (j16 == 0) {
       sScl8[blk][16 * (tr >> 3) + (tr & 7)] = sk;
       sScl8[blk][16 * (tr >> 3) + 8 + (tr & 7)] = sv;
@@ -395,7 +411,7 @@ __device__ __forceinline__ void split_loader(const SplitArgs& a, const SplitCtx&
   if (c.pre) {
     const uint16_t* kt = a.kt_base + c.g * a.tail_stride;
     const uint16_t* vt = a.vt_base + c.g * a.tail_stride;
-    lds_u8* ot = ring + (L >> 1) * kSTile;  // tokens 0..31 in tile 0, 32..63 in tile 1
+    lds_u8* ot = own_tile<F8>(L >> 1);  // tokens 0..31 in own tile 0, 32..63 in own tile 1
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tr0 = 16 * (L & 1) + 4 * i;
@@ -410,22 +426,24 @@ __device__ __forceinline__ void split_loader(const SplitArgs& a, const SplitCtx&
   if (c.pre) {
     vm_wait<0>();
     arrive(&sCnt[kCPro + L], lane);
-    if constexpr (NORM) norm_rows<2>(a, c, 16 * L + 8);
+    if constexpr (NORM) norm_rows<2, F8>(a, c, 16 * L + 8);
     if constexpr (F8) quant_own_rows<2>(a, c, 16 * L + 8);
     if constexpr (NORM || F8) arrive(&sCnt[kCNorm], lane);
     return;
   }
   // 2. blocks: kSDepth in flight. bf16: block b goes to tile b % kSRing once all four uses of the
   //    tile's previous block (one per row tile) are finished; 4 loads of this wave. fp8: block b
-  //    goes to raw tile b % 4 at once (this wave converted its previous block), 3 loads; once
-  //    landed, and once the bf16 tile b % 4 is free, this wave converts its rows into it.
+  //    goes to raw tile b % 8 once the four uses of block b - 8 are finished, 3 loads; once
+  //    landed, and once V tile b % 4 is free, this wave converts its V rows into it.
   constexpr int LPB = F8 ? 3 : 4;  // loads per block
   const int nb = c.nb;
   auto issue = [&](int b) {
     if constexpr (F8) {
+      // raw tile b % 8: all four uses of its previous block (K codes read by the matrix cores) done
+      if (b >= kSRaw8) await_cnt(kCDone + b % kSRaw8, kSRT * (b / kSRaw8), a.spin_limit, expired);
       dma_block_f8(a, c, L, b);
     } else {
-      if (b >= kSRing) await_cnt(kCDone + b % kSRing, (kSC / 2) * (b / kSRing), a.spin_limit, expired);
+      if (b >= kSRing) await_cnt(kCDone + b % kSRing, kSRT * (b / kSRing), a.spin_limit, expired);
       dma_block_share(kc, vc, c, L, b, ring + (b % kSRing) * kSTile);
     }
   };
@@ -443,7 +461,7 @@ __device__ __forceinline__ void split_loader(const SplitArgs& a, const SplitCtx&
   }
   arrive(&sCnt[kCPro + L], lane);
   if constexpr (NORM) {
-    norm_rows<2>(a, c, 16 * L + 8);
+    norm_rows<2, F8>(a, c, 16 * L + 8);
     arrive(&sCnt[kCNorm], lane);
   }
   for (int b = 2; b < d0; ++b) issue(b);
@@ -451,7 +469,9 @@ __device__ __forceinline__ void split_loader(const SplitArgs& a, const SplitCtx&
     const int later = (b + kSDepth - 1 < nb ? b + kSDepth - 1 : nb - 1) - b;  // blocks issued after b
     if (later >= 2) vm_wait<2 * LPB>(); else if (later == 1) vm_wait<LPB>(); else vm_wait<0>();
     if constexpr (F8) {
-      if (b >= kSRing8) await_cnt(kCDone + b % kSRing8, (kSC / 2) * (b / kSRing8), a.spin_limit, expired);
+      // V tile b % 4: all four uses of block b - 4 done (its uses count at kCDone + (b - 4) % 8)
+      if (b >= kSRing8)
+        await_cnt(kCDone + (b - kSRing8) % kSRaw8, kSRT * ((b - kSRing8) / kSRaw8 + 1), a.spin_limit, expired);
       convert_block_f8(c, L, b);
     }
     arrive(&sCnt[kCLand + b], lane);
@@ -488,7 +508,7 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
   //    the other four the partner wave's); in the own range also the own k rows of the same
   //    tokens, and with the fp8 cache the own k and v rows quantised. Roped q arrives ready.
   await_cnt(kCPro + T, 1, a.spin_limit, expired);
-  if constexpr (NORM) norm_rows<1>(a, c, 16 * T + 4 * P);
+  if constexpr (NORM) norm_rows<1, F8>(a, c, 16 * T + 4 * P);
   if constexpr (F8) {
     if (c.pre) quant_own_rows<1>(a, c, 16 * T + 4 * P);
   }
@@ -497,27 +517,64 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
   await_cnt(kCNorm, (NORM || (F8 && c.pre)) ? kSC + kSL : kSC, a.spin_limit, expired);
 
   // 2. The query rows of row tile T as MFMA B operands (k-step kk: columns 32 kk .. 32 kk + 31).
+  //    fp8 cache: the scores are products of the K codes with q on v_mfma_f32_16x16x128_f8f6f4
+  //    (e4m3 x e4m3; lane l holds row l & 15 of either operand, columns 32 (l >> 4) .. + 31, as
+  //    32 codes), q in two e4m3 parts: x = q 2^sg with 2^sg putting the row's largest |q| in
+  //    [128, 256), hi = e4m3(x), lo = e4m3(x - hi) (both to nearest even, no saturation), so that
+  //    hi + lo carries x to within the bf16 rounding q already had; the score scale takes 2^-sg.
   bf16x8 qf[4];
+  v8i32 qh, ql;
+  float sscale = kScoreScale;  // log2(e) / sqrt(128), and with the fp8 cache times 2^-sg
   {
     const int r = 16 * T + j16;
     const lds_u8* qrow = AX_LDS(sQ) + r * 256;
+    if constexpr (!F8) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qf[kk] = lds_ld<bf16x8>(qrow + 16 * ((4 * kk + g4) ^ qswz(r)));
+      for (int kk = 0; kk < 4; ++kk) qf[kk] = lds_ld<bf16x8>(qrow + 16 * ((4 * kk + g4) ^ qswz(r)));
+    } else {
+      float x[32];
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) unpack8v(lds_ld<u32x4>(qrow + 16 * ((4 * g4 + cc) ^ qswz(r))), x + 8 * cc);
+      float mx = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) mx = fmax_(mx, fabsf(x[e]));
+      mx = row_max4(mx);
+      const int sg = mx > 0.f ? 8 - __builtin_amdgcn_frexp_expf(mx) : 0;
+      sscale = kScoreScale * __builtin_ldexpf(1.0f, -sg);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = __builtin_ldexpf(x[4 * j + e], sg);
+        int wh = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        wh = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], wh, true);
+        const auto d01 = __builtin_amdgcn_cvt_pk_f32_fp8(wh, false);
+        const auto d23 = __builtin_amdgcn_cvt_pk_f32_fp8(wh, true);
+        int wl = __builtin_amdgcn_cvt_pk_fp8_f32(y[0] - d01[0], y[1] - d01[1], 0, false);
+        wl = __builtin_amdgcn_cvt_pk_fp8_f32(y[2] - d23[0], y[3] - d23[1], wl, true);
+        qh[j] = wh;
+        ql[j] = wl;
+      }
+    }
   }
   arrive(&sCnt[kCFrag], lane);  // (the exchange of step 5 reuses the RoPE rows once all eight have read)
 
   // 3. The blocks P, P + 2, ..., software-pipelined one block deep.
-  // K: key row 16 t + j16, chunk 4 kk + g4; the second half of the keys is 4 KB further on.
+  // K: key row 16 t + j16, chunk 4 kk + g4; the second half of the keys is 4 KB further on. fp8
+  // cache: the codes of key row 16 t + j16, chunks 2 g4 and 2 g4 + 1 (columns 32 g4 .. + 31); the
+  // second half 2 KB further on.
   int koff[4];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) koff[kk] = j16 * 256 + 16 * ((4 * kk + g4) ^ kswz16(j16));
+  for (int kk = 0; kk < 4; ++kk)
+    koff[kk] = F8 ? (kk < 2 ? j16 * kD + 16 * ((2 * g4 + kk) ^ kswz8(j16)) : 0)
+                  : j16 * 256 + 16 * ((4 * kk + g4) ^ kswz16(j16));
   // V: lane j16 of 16-lane group g4 supplies key row 4 g4 + (j16 >> 2) (+ 16 for the second read),
   // columns 16 dt + 4 (j16 & 3) .. + 3: half j16 & 1 of chunk 2 dt + ((j16 & 3) >> 1)
   const int vr = 4 * g4 + (j16 >> 2);
   int voff[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
-    voff[dt] = kSV + vr * 256 + 16 * ((2 * dt + ((j16 & 3) >> 1)) ^ vswz16(vr)) + 8 * (j16 & 1);
+    voff[dt] = vr * 256 + 16 * ((2 * dt + ((j16 & 3) >> 1)) ^ vswz16(vr)) + 8 * (j16 & 1);
   f32x4 o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -525,16 +582,30 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
   float l = 0.f;        // this lane's share of the row sum
   f32x4 s[2];           // raw scores q . k of the block being exponentiated
   bf16x8 kf[2][4];
+  v8i32 ka[2];  // fp8 cache: the K codes of the two halves
   v4i16 vt[8][2];
   bf16x8 pb;
   const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
-  constexpr int RS = F8 ? kSRing8 : kSRing;
-  auto tile_of = [&](int b) { return ring + (b % RS) * kSTile; };  // (b uniform: scalar ops)
+  constexpr int RS = F8 ? kSRaw8 : kSRing;  // tile-use counters in turn
+  // (b uniform: scalar ops) K rows of block b (fp8: its raw tile's codes) and its V rows
+  auto ktile_of = [&](int b) {
+    return F8 ? ring + kSRawBase + (b % kSRaw8) * kSRawTile : ring + (b % kSRing) * kSTile;
+  };
+  auto vtile_of = [&](int b) { return F8 ? ring + (b % kSRing8) * kSVTile8 : ring + (b % kSRing) * kSTile + kSV; };
   auto read_k = [&](const lds_u8* base) {
+    if constexpr (F8) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t) {
+        const u32x4 c0 = lds_ld<u32x4>(base + koff[0] + 2048 * t);
+        const u32x4 c1 = lds_ld<u32x4>(base + koff[1] + 2048 * t);
+        ka[t] = v8i32{(int)c0[0], (int)c0[1], (int)c0[2], (int)c0[3], (int)c1[0], (int)c1[1], (int)c1[2], (int)c1[3]};
+      }
+    } else {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) kf[t][kk] = lds_ld<bf16x8>(base + koff[kk] + 4096 * t);
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) kf[t][kk] = lds_ld<bf16x8>(base + koff[kk] + 4096 * t);
+    }
   };
   auto read_v = [&](const lds_u8* base) {
 #pragma unroll
@@ -547,8 +618,14 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       sd[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (F8) {
+        sd[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[t], qh, sd[t], 0, 0, 0, 0, 0, 0);
+        sd[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka[t], ql, sd[t], 0, 0, 0, 0, 0, 0);
+      } else {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) sd[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][kk], qf[kk], sd[t], 0, 0, 0);
+        for (int kk = 0; kk < 4; ++kk)
+          sd[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][kk], qf[kk], sd[t], 0, 0, 0);
+      }
     }
   };
   // p = 2^(s log2(e) / sqrt(128) - m) (v_exp_f32 directly: the arguments are at most kSRescale, or
@@ -571,8 +648,8 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][2 * i], kScoreScale, mo));
-        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][2 * i + 1], kScoreScale, mo));
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][2 * i], sscale, mo));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][2 * i + 1], sscale, mo));
         if constexpr (F8) {
           const bf16x2_t pr = {(__bf16)(e0 * vs[t][2 * i]), (__bf16)(e1 * vs[t][2 * i + 1])};
           pb[4 * t + 2 * i] = pr[0];
@@ -640,16 +717,16 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
   // partial sum, and with it the result, is the same from run to run.)
   if (NB > 0) {
     landed(P);
-    read_k(tile_of(P));
+    read_k(ktile_of(P));
     qk(s);
     kscale(s, P);
-    read_v(tile_of(P));
-    m = row_max4(lane_max8(s)) * kScoreScale;  // finite: the block holds a visible key
+    read_v(vtile_of(P));
+    m = row_max4(lane_max8(s)) * sscale;  // finite: the block holds a visible key
     if (c.partial && P == c.nb - 1) mask_tail(s, P);
     release(P);
     if (NB > 1) {
       landed(P + 2);
-      read_k(tile_of(P + 2));
+      read_k(ktile_of(P + 2));
     }
 #pragma clang loop unroll(disable)
     for (int k = 1; k < NB; ++k) {
@@ -666,8 +743,8 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
       kscale(sn, b);
       // (B) PV of block b - 2 beside the lane's share of the row max of block b
       pv();
-      const float bm = lane_max8(sn) * kScoreScale;
-      read_v(tile_of(b));
+      const float bm = lane_max8(sn) * sscale;
+      read_v(vtile_of(b));
       // the reference moves only when the row's block max exceeds it by more than kSRescale:
       // p stays below 2^kSRescale and the O rescale is rare; a lane's share of the row max
       // decides whether any row needs it, and only then are the row's four lanes combined
@@ -687,7 +764,7 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
       release(b);
       if (more) {
         if (__builtin_amdgcn_readfirstlane(early) < kSL) landed(b + 2);
-        read_k(tile_of(b + 2));
+        read_k(ktile_of(b + 2));
       }
     }
     softmax(P + 2 * (NB - 1));

@@ -13,6 +13,7 @@ constexpr float kRescale = 8.0f;              // lazy-rescale threshold (log2 un
 constexpr int kNonTemporal = 2;               // cache-policy operand of a load: nt
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef int v8i32 __attribute__((ext_vector_type(8)));  // 32 fp8 codes: an f8f6f4 MFMA operand
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) void lds_void;
 
