@@ -33,6 +33,10 @@
 //   software-pipelined: the scores of block b run on the matrix cores while the exponentials of
 //   the previous block run on the vector ALU, and the PV of the previous block beside the row
 //   max of block b.
+// - fp8 cache: K stays in e4m3 codes and S^T comes from v_mfma_f32_16x16x128_f8f6f4, with each
+//   query row scaled by a power of two and split into two e4m3 parts whose sum is the scaled bf16
+//   row exactly for every element down to 2^-10 of the row's largest (below, within 2^-17 of
+//   it); the loaders convert only V to bf16. Key scales multiply S, value scales P.
 // - The three waves of a SIMD norm and rope their row tile's 16 query rows in LDS first.
 // - The two parity waves of a row tile merge (m, l, O) through LDS, each finalising half of the
 //   columns, and store the range's partial: O in float16 with a power-of-two exponent per (row,

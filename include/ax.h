@@ -253,11 +253,14 @@ int ax_cache_tail_write_fp8(const uint16_t* k_roped, const uint16_t* v, uint8_t*
  * ax_expert_attn over an fp8 cache: if k_own/v_own (roped k, v; bf16) are
  * both non-NULL their quantised rows are written to the tail first, if both
  * are NULL the tail is taken as already written. Scores and the value sum use
- * the dequantised rows: each e4m3 code is converted exactly to bf16 for the
- * matrix cores, the key scales multiply the float32 scores and the value
- * scales (times a fixed 2^64, taken back out in the combine) the float32
- * softmax weights before they are rounded to bf16; value scales from the
- * float32 denormals up to 2^25 keep those products in bf16's normal range.
+ * the dequantised rows: the key codes meet q on the fp8 matrix cores, q as
+ * two e4m3 parts whose sum is its bf16 row scaled by a power of two (exact
+ * down to 2^-10 of the row's largest element, within 2^-17 of it below); each
+ * value code is converted exactly to bf16 for the bf16 matrix cores. The key
+ * scales multiply the float32 scores and the value scales (times a fixed
+ * 2^64, taken back out in the combine) the float32 softmax weights before
+ * they are rounded to bf16; value scales from the float32 denormals up to
+ * 2^25 keep those products in bf16's normal range.
  * ws: at least ax_expert_attn_fp8_workspace_bytes(S, Smax) bytes, 256-byte
  * aligned (the status word, then partials in the bf16 cache's layout, with
  * longer key ranges).

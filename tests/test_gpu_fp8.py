@@ -227,3 +227,47 @@ def test_fp8_benchmark_inputs_match_oracle(ax, step, layer):
     torch.cuda.synchronize()
     check_out(bits(out), ref, f"fp8 sequence s={step} l={layer}")
     assert np.array_equal(down8(Vc)[:, Smax - 64:], ref["v_tail_codes"])
+
+
+def test_fp8_scores_over_wide_range_query_rows(ax):
+    # The scores take the K codes on the fp8 matrix cores against q in two e4m3 parts of the row
+    # scaled by a power of two. Given bf16 q rows of very different sizes (zero, 1e-30, 2^-6 .. 64)
+    # whose elements spread over 16 binades (and rows with one nonzero element), the output stays
+    # within 2^-6 of each row's largest output element of the fp64 oracle on the same bf16 q: the
+    # bf16 rounding of P and of the output (2^-9 each, relative) weigh more where a row's output is
+    # smaller than the values it averages (5.4e-3 measured at worst). The large rows make the
+    # softmax peaked, where an error of a few percent in q moves the output by far more: with q's
+    # first e4m3 part alone, 410 rows of this input miss 2^-7 and the worst is 0.89.
+    S, Smax = 4700, 8192
+    inp = synth.layer_inputs_fp8(Smax, S, seed=77)
+    rng = np.random.Generator(np.random.PCG64(78))
+    mags = np.array([0.0, 1e-30, 2.0 ** -6, 1.0, 4.0, 16.0, 64.0])
+    rows = 16 * 64
+    mag = mags[np.arange(rows) % len(mags)].reshape(16, 64, 1)
+    x = rng.standard_normal((16, 64, 128)) * np.exp2(-rng.uniform(0, 16, (16, 64, 128))) * mag
+    x[3, 5] = 0.0
+    x[3, 5, 17] = 9.5                                        # one nonzero element
+    x[7, 9] = 0.0
+    x[7, 9, 100] = -3.0e-20
+    q_bits = oracle.f64_to_bf16_bits(x)
+    q = bf16_to_f64(q_bits)
+    say(f"expert_attn_fp8 wide-range q rows, S={S} Smax={Smax}")
+    Kc, Vc, Ks, Vs = up8(inp["Kc8"]), up8(inp["Vc8"]), up8(inp["Ks"]), up8(inp["Vs"])
+    out_g = Guarded(16 * 64 * 128 * 2)
+    out = out_g.t.view(torch.int16).view(16, 64, 128)
+    ws_g = Guarded(ax.expert_attn_fp8_workspace_bytes(S, Smax))
+    ax.expert_attn_fp8(up(q_bits), None, None, Kc, Ks, Vc, Vs, S, Smax, out, ws_g.t)
+    torch.cuda.synchronize()
+    out_g.check("out")
+    ws_g.check("workspace")
+    assert_status_clear(ax, ws_g.t)
+    got = bf16_to_f64(down(out))
+    K = oracle.dequantize_rows_e4m3(inp["Kc8"], inp["Ks"])
+    V = oracle.dequantize_rows_e4m3(inp["Vc8"], inp["Vs"])
+    ref = oracle.attention(q, K, V, oracle.build_mask(S, Smax, 128, 64), 128 ** -0.5)
+    err = np.abs(got - ref).max(axis=-1)
+    big = np.abs(ref).max(axis=-1)
+    worst = float((err / big).max())
+    print(f"wide-range q: worst row error / row max = {worst:.3e} (bound 2^-6 = {2.0 ** -6:.3e})", flush=True)
+    assert np.all(np.isfinite(got))
+    assert np.all(err <= 2.0 ** -6 * big)
