@@ -282,7 +282,6 @@ __device__ __forceinline__ lds_u8* own_tile(int blk) {
 template <int NP, bool F8>
 __device__ __forceinline__ void norm_rows(const SplitArgs& a, const SplitCtx& c, const int row0) {
   const int lane = c.lane, j16 = lane & 15, r4 = lane >> 4;
-  lds_u8* ring = AX_LDS(sRing);
   float g8[8];
   unpack_pair(lds_ld<uint2>(AX_LDS(sGam) + 8 * j16), lds_ld<uint2>(AX_LDS(sGam) + 128 + 8 * j16), g8);
   uint2 lo[NP], hi[NP];
@@ -371,8 +370,8 @@ __device__ __forceinline__ void quant_own_rows(const SplitArgs& a, const SplitCt
     }
     if (c.hp == 0) {
       const long long crow = (long long)c.g * a.Smax + a.Smax - kT + tok;
-      *reinterpret_cast<uint2*>(a.Kc8 + crow * kD + 8 * j16) = ck;
-      *reinterpret_cast<uint2*>(a.Vc8 + crow * kD + 8 * j16) = cv;
+      __builtin_nontemporal_store(u32x2{ck.x, ck.y}, reinterpret_cast<u32x2*>(a.Kc8 + crow * kD + 8 * j16));
+      __builtin_nontemporal_store(u32x2{cv.x, cv.y}, reinterpret_cast<u32x2*>(a.Vc8 + crow * kD + 8 * j16));
       if (j16 == 0) {
         a.Ks[crow] = sk;
         a.Vs[crow] = sv;
@@ -786,8 +785,10 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
         const int tr = tok & (kBlk - 1);
         const lds_u8* ot = ring + (tok >> 5) * kSTile;
         const long long dst = head_off + (long long)(a.Smax - kT + tok) * kD + 8 * j16;
-        *reinterpret_cast<u32x4*>(a.Kc + dst) = lds_ld<u32x4>(ot + tr * 256 + 16 * (j16 ^ kswz16(tr)));
-        *reinterpret_cast<u32x4*>(a.Vc + dst) = lds_ld<u32x4>(ot + kSV + tr * 256 + 16 * (j16 ^ vswz16(tr)));
+        const u32x4 kr = lds_ld<u32x4>(ot + tr * 256 + 16 * (j16 ^ kswz16(tr)));
+        const u32x4 vr = lds_ld<u32x4>(ot + kSV + tr * 256 + 16 * (j16 ^ vswz16(tr)));
+        __builtin_nontemporal_store(kr, reinterpret_cast<u32x4*>(a.Kc + dst));
+        __builtin_nontemporal_store(vr, reinterpret_cast<u32x4*>(a.Vc + dst));
       }
     }
   }
@@ -833,6 +834,10 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
   // maps into [0.5, 1) and ldexp scales each element exactly, with no intermediate overflow.
   // Group (part, hp, T, qd) holds the quarter's 16 rows row-major (64 bytes a row), so that the
   // combine reads a row's quarter as one contiguous run; the two stores of a quarter fill its 1 KB.
+  // Whole-line results that a later launch reads (these partials, the cache tail, the combine's
+  // output) are stored nontemporally: they drain to memory during the launch rather than in the
+  // L2 write-back at its end. (The 4- and 8-byte record words stay ordinary stores: as
+  // nontemporal partial-line writes they slowed the launch.)
   auto store = [&](auto pc) {
     constexpr int PP = decltype(pc)::value;
     int exq[2];
@@ -860,8 +865,8 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
         v[jj] = pack_f16x4(__builtin_ldexpf(acc[jj][0], -ex), __builtin_ldexpf(acc[jj][1], -ex),
                            __builtin_ldexpf(acc[jj][2], -ex), __builtin_ldexpf(acc[jj][3], -ex));
       u32x2* po = reinterpret_cast<u32x2*>(a.part.po) + (((part * 2 + c.hp) * 4 + T) * 4 + 2 * PP + qq) * 128 + 8 * j16 + g4;
-      po[0] = v[0];  // columns 4 g4 .. 4 g4 + 3 of the quarter
-      po[4] = v[1];  // columns 16 + 4 g4 .. 16 + 4 g4 + 3
+      __builtin_nontemporal_store(v[0], po);  // columns 4 g4 .. 4 g4 + 3 of the quarter
+      __builtin_nontemporal_store(v[1], po + 4);  // columns 16 + 4 g4 .. 16 + 4 g4 + 3
     }
     // the two quarters' exponents as one word of the row's record (e[2 PP], e[2 PP + 1])
     if (g4 == 0)
@@ -962,7 +967,8 @@ __global__ __launch_bounds__(256) void k_attn_combine(WsLayout p, uint16_t* out,
     });
   }
   const float inv = 1.0f / L;
-  *reinterpret_cast<uint32_t*>(out + ((long long)g * kQRows + r) * kD + 2 * lane) = pack_bf16x2(acc0 * inv, acc1 * inv);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(out + ((long long)g * kQRows + r) * kD + 2 * lane);
+  __builtin_nontemporal_store(pack_bf16x2(acc0 * inv, acc1 * inv), dst);  // (a whole 256-byte row per wave)
 }
 
 AttnPlan attn_plan(int S, int /*Smax*/) {
