@@ -204,3 +204,21 @@ def test_fp8_tail_placement_equals_concatenation():
     Vcat = np.concatenate([V[:, :100], V[:, 192:]], 1)
     ref = oracle.attention(r["q_roped"], Kcat, Vcat, None, 128 ** -0.5)
     assert np.abs(ref - r["out"]).max() < 1e-12
+
+
+def test_two_e4m3_parts_carry_a_scaled_bf16_value():
+    # The fp8 scores take q in two e4m3 parts: a query row scaled by a power of two so that its
+    # largest |element| lies in [128, 256), hi = e4m3(x) and lo = e4m3(x - hi), both to nearest
+    # even. Over every bf16 value below 256 in magnitude: hi + lo is x exactly for |x| >= 1/4
+    # (x's last bit is then no finer than e4m3's smallest subnormal 2^-9, and x - hi is a
+    # multiple of it no larger than 8 of them), and within 2^-10 of x below.
+    bits = np.arange(0x0000, 0x4380, dtype=np.uint32)       # +0 .. the largest bf16 below 256
+    bits = np.concatenate([bits, bits | 0x8000]).astype(np.uint16)
+    x = bf16_bits_to_f64(bits)
+    assert np.all(np.abs(x) < 256)
+    hi = e4m3_bits_to_f64(f64_to_e4m3_bits(x))
+    lo = e4m3_bits_to_f64(f64_to_e4m3_bits(x - hi))
+    big = np.abs(x) >= 0.25
+    assert np.array_equal(hi[big] + lo[big], x[big])
+    assert np.all(np.abs(hi + lo - x) <= 2.0 ** -10)
+    assert not np.array_equal(hi[big], x[big])               # one part alone does not suffice
