@@ -523,8 +523,10 @@ __device__ __forceinline__ void split_compute(const SplitArgs& a, const SplitCtx
   //    fp8 cache: the scores are products of the K codes with q on v_mfma_f32_16x16x128_f8f6f4
   //    (e4m3 x e4m3; lane l holds row l & 15 of either operand, columns 32 (l >> 4) .. + 31, as
   //    32 codes), q in two e4m3 parts: x = q 2^sg with 2^sg putting the row's largest |q| in
-  //    [128, 256), hi = e4m3(x), lo = e4m3(x - hi) (both to nearest even, no saturation), so that
-  //    hi + lo carries x to within the bf16 rounding q already had; the score scale takes 2^-sg.
+  //    [128, 256), hi = e4m3(x), lo = e4m3(x - hi) (both to nearest even; |x| < 256 needs no
+  //    saturation): hi + lo = x exactly for |x| >= 1/4 (x keeps bf16's 8 significant bits, and
+  //    x - hi is a multiple of x's last bit no larger than 8 of them), and within 2^-10 below,
+  //    2^-17 of the row's largest; the score scale takes 2^-sg.
   bf16x8 qf[4];
   v8i32 qh, ql;
   float sscale = kScoreScale;  // log2(e) / sqrt(128), and with the fp8 cache times 2^-sg
