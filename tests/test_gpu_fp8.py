@@ -197,6 +197,36 @@ def test_fp8_attn_entry_points_equal_layer(ax):
     assert np.array_equal(down8(Kc2), down8(L.Kc)) and np.array_equal(down8(Ks2), down8(L.Ks))
 
 
+def test_fp8_graph_replay_equals_eager(ax):
+    # the fp8 step captured in a hipGraph (as the benchmark runs it): every replay, with eager
+    # work between them, equals the eager call bit for bit, caches included
+    inp = synth.layer_inputs_fp8(4096, 3000, seed=36)
+    say("fp8 graph capture / replay x3")
+    L = Layer8(inp, ax)
+    eager = L.run(ax)
+    caches = [down8(t) for t in (L.Kc, L.Ks, L.Vc, L.Vs)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        L.out.zero_()
+        with torch.cuda.graph(g, stream=s):
+            ax.expert_layer_attn_fp8(L.q, L.k, L.v, L.gq, L.gk, L.cos, L.sin, 1e-6, L.Kc, L.Ks, L.Vc, L.Vs, L.S,
+                                     L.Smax, L.out, L.ws, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        L.out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(down(L.out), eager), f"replay {rep}"
+        for a, b in zip(caches, (L.Kc, L.Ks, L.Vc, L.Vs)):
+            assert np.array_equal(a, down8(b)), f"replay {rep}: cache"
+        assert_status_clear(ax, L.ws)
+        torch.randn(1 << 20, device=DEV).sum().item()   # eager work between replays
+
+
 def test_fp8_repeat_is_bitwise_deterministic(ax):
     inp = synth.layer_inputs_fp8(8192, 8128, seed=5)
     say("fp8 determinism x3, S=8128")
